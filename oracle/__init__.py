@@ -1,0 +1,188 @@
+"""fp64 CPU oracle for the routed LoRA delta.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package; the product library never does.  It shares no code with the HIP
+path: admission and per-token routing are plain Python loops written from the
+pages, the delta is the plain C loop in lora_oracle.c.
+
+What it follows:
+  * admission under max_loras -- tokenspeed PR #976, first commit message
+    ("max_loras batch cap"): walk the candidate requests in order; a base-model
+    request is never charged; a request whose adapter is already in the batch
+    costs nothing; a request that would bring a new adapter past the cap is
+    deferred and the walk goes on; max_loras == 0 means no cap at all.
+  * per-token adapter ids -- xLLM PR #2014, "Wire-up": one adapter id per
+    sequence, aligned with the sequences' query lengths, expanded to one id
+    per token with repeat_interleave; id 0 is the base model (tokenspeed PR
+    #976, third commit message).
+  * the delta -- TensorFold PR #47, third commit message: scale * B @ (A @ x)
+    added to the fp32 partial sum of the projection; a row of slot 0 is not
+    read or written.
+
+Rows of deferred sequences are outside this batch: the oracle leaves them
+exactly as they were, like base-model rows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lora_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+X_KIND = {"bf16": 1, "fp16": 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile lora_oracle.c with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_fp16_value.restype = ctypes.c_double
+        lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.oracle_slice_delta.restype = ctypes.c_int
+        lib.oracle_slice_delta.argtypes = [
+            I, P, I, P, I, ctypes.c_int32, I, P, I, I, I, P, I,
+            ctypes.c_double, P, I, I]
+        _lib = lib
+    return _lib
+
+
+def bf16_value(bits: int) -> float:
+    return _load().oracle_bf16_value(int(bits))
+
+
+def fp16_value(bits: int) -> float:
+    return _load().oracle_fp16_value(int(bits))
+
+
+# --------------------------------------------------------------------------
+# Admission and routing (tokenspeed PR #976; xLLM PR #2014 "Wire-up")
+# --------------------------------------------------------------------------
+
+def admit(seq_adapter_ids, max_loras: int):
+    """Admission of candidate sequences under the distinct-adapter cap.
+
+    Returns (admitted: list[bool], distinct: list[int] in order of admission).
+    """
+    admitted = []
+    in_batch = []
+    for aid in seq_adapter_ids:
+        aid = int(aid)
+        if aid == 0:
+            admitted.append(True)             # base model: never charged
+        elif aid in in_batch:
+            admitted.append(True)             # reuse: no extra slot
+        elif max_loras == 0 or len(in_batch) < max_loras:
+            in_batch.append(aid)              # new adapter within the cap
+            admitted.append(True)
+        else:
+            admitted.append(False)            # defer, keep scanning
+    return admitted, in_batch
+
+
+def token_adapters(seq_adapter_ids, seq_lens, admitted):
+    """Per-token adapter id: repeat each sequence's id over its query length.
+
+    Rows of a deferred sequence get id 0: they are not part of this batch and
+    nothing reads or writes them.
+    """
+    out = []
+    for aid, n, ok in zip(seq_adapter_ids, seq_lens, admitted):
+        out.extend([int(aid) if ok else 0] * int(n))
+    return np.array(out, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# The delta
+# --------------------------------------------------------------------------
+
+def slice_delta(rows, x_bits, x_dtype, A_bits, a_col0, h_in, B_bits, rank, scale):
+    """fp64 delta of one adapter on one slice for the given rows of x.
+
+    Returns float64 [len(rows), h_out_j].
+    """
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    A_bits = np.ascontiguousarray(A_bits, dtype=np.uint16)
+    B_bits = np.ascontiguousarray(B_bits, dtype=np.uint16)
+    h_out = B_bits.shape[0]
+    out = np.zeros((len(rows), h_out), dtype=np.float64)
+    if len(rows) == 0 or h_out == 0:
+        return out
+    assert A_bits.shape[0] >= rank and B_bits.shape[1] >= rank
+    assert a_col0 + h_in <= A_bits.shape[1] and x_bits.shape[1] >= h_in
+    rc = lib.oracle_slice_delta(
+        len(rows), rows.ctypes.data, h_in, x_bits.ctypes.data, x_bits.shape[1],
+        X_KIND[x_dtype], rank, A_bits.ctypes.data, A_bits.shape[1], a_col0,
+        h_out, B_bits.ctypes.data, B_bits.shape[1], float(scale),
+        out.ctypes.data, h_out, 0)
+    if rc != 0:
+        raise MemoryError("oracle_slice_delta")
+    return out
+
+
+def lane_delta(x_bits, x_dtype, tok_adapter, factors, h_out, a_col0, h_in,
+               rows=None):
+    """fp64 delta of a lane for the rows `rows` (default: all rows of x).
+
+    tok_adapter  per-token adapter id (0 = base, or deferred)
+    factors      adapter id -> list over slices of (A_bits, B_bits, rank, scale)
+    h_out        per-slice output widths; slice j sits at column sum(h_out[:j])
+
+    Returns float64 [len(rows), sum(h_out)]; rows with adapter 0 are all zero.
+    """
+    tok_adapter = np.asarray(tok_adapter, dtype=np.int64)
+    if rows is None:
+        rows = np.arange(len(tok_adapter), dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    H = int(sum(h_out))
+    delta = np.zeros((len(rows), H), dtype=np.float64)
+    ids = tok_adapter[rows]
+    for aid in sorted(set(ids.tolist()) - {0}):
+        sel = np.nonzero(ids == aid)[0]
+        col = 0
+        for j, hj in enumerate(h_out):
+            A, B, r, s = factors[aid][j]
+            delta[sel, col:col + hj] = slice_delta(
+                rows[sel], x_bits, x_dtype, A, a_col0, h_in, B, r, s)
+            col += hj
+    return delta
+
+
+def workload_lane_delta(workload, lane_name, max_loras=None, rows=None):
+    """Routing + delta for one lane of a generated workload.
+
+    Returns (delta float64 [n_rows, H_out], tok_adapter int64 [T], admitted).
+    """
+    spec = workload.spec
+    cap = spec.max_loras if max_loras is None else max_loras
+    admitted, _ = admit(workload.seq_adapter, cap)
+    tok = token_adapters(workload.seq_adapter, workload.seq_len, admitted)
+    lane = workload.lanes[lane_name]
+    factors = {aid: [(sf.A, sf.B, sf.rank, sf.scale) for sf in ad.lanes[lane_name]]
+               for aid, ad in workload.adapters.items()}
+    d = lane_delta(lane.x, lane.spec.x_dtype, tok, factors, lane.spec.h_out,
+                   lane.spec.a_col0, lane.spec.h_in, rows)
+    return d, tok, admitted

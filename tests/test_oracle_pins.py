@@ -1,0 +1,236 @@
+"""Pins of the fp64 oracle against facts other than itself.
+
+Each test checks the oracle against something the pages or the mathematics
+fix: hand-derived worked examples (tests/golden), library decoders, the dense
+product B @ A computed by numpy, exact integer brute force, and invariants
+(slot 0, permutation, scale 0, linearity, slices, column shares).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (CONFIGS, WorkloadSpec, LaneSpec, generate, config_by_name,
+                       f32_to_bf16_bits, bf16_bits_to_f32)
+from workloads.gen import f32_to_fp16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(vals, dtype="bf16"):
+    a = np.asarray(vals, dtype=np.float32)
+    return f32_to_fp16_bits(a) if dtype == "fp16" else f32_to_bf16_bits(a)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decode_matches_torch_for_every_pattern():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_value(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp16_decode_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16_value(b) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ---------------------------------------------------------- worked examples
+
+def test_worked_examples():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        dt = c["x_dtype"]
+        if "x_bits" in c:
+            x = np.array([c["x_bits"]], dtype=np.uint16)
+        else:
+            x = _bits([c["x"]], dt)
+        h_in = x.shape[1]
+        factors = {5: []}
+        h_out = []
+        for s in c["slices"]:
+            A = _bits(s["A"])
+            B = _bits(s["B"])
+            factors[5].append((A, B, A.shape[0], s["scale"]))
+            h_out.append(B.shape[0])
+        d = oracle.lane_delta(x, dt, [5], factors, h_out, c["a_col0"], h_in)
+        assert d.tolist() == [c["delta"]], c["name"]
+
+
+# ----------------------------------------------------------------- admission
+
+def test_admission_cases():
+    with open(os.path.join(GOLDEN, "admission_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        adm, distinct = oracle.admit(c["ids"], c["max_loras"])
+        assert adm == c["admitted"], c["name"]
+        assert distinct == c["distinct"], c["name"]
+
+
+def test_token_adapters_is_repeat_interleave():
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, 4, size=50) * 11
+    lens = rng.integers(1, 9, size=50)
+    adm = rng.random(50) < 0.8
+    got = oracle.token_adapters(ids, lens, adm)
+    ref = np.repeat(np.where(adm, ids, 0), lens)
+    assert np.array_equal(got, ref)
+
+
+# -------------------------------------------------- dense identity, brute force
+
+def _single_adapter_lane(seed, h_in, h_out, rank, T, x_dtype="bf16", mode="real",
+                         tp_size=1, tp_rank=0):
+    spec = WorkloadSpec(
+        name="pin", seed=seed,
+        lanes=(LaneSpec("l", h_in, tuple(h_out), x_dtype, tp_size, tp_rank),),
+        n_adapters=1, ranks=(rank,), rank_mode="list", scale_mode="fixed",
+        scale=1.75, max_rank=rank, decode_rows=T, base_prob=0.0)
+    return generate(spec, mode=mode)
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "fp16"])
+def test_dense_identity(x_dtype):
+    """Single adapter: the factored delta equals scale * (B A) x with the dense
+    [h_out, h_in] matrix formed by numpy's fp64 matmul."""
+    w = _single_adapter_lane(11, 96, [40, 24], 7, 13, x_dtype)
+    lane = w.lanes["l"]
+    d, tok, _ = oracle.workload_lane_delta(w, "l")
+    xf = (lane.x.view(np.float16).astype(np.float64) if x_dtype == "fp16"
+          else bf16_bits_to_f32(lane.x).astype(np.float64))
+    (aid, ad), = w.adapters.items()
+    col = 0
+    for sf in ad.lanes["l"]:
+        A = bf16_bits_to_f32(sf.A).astype(np.float64)
+        B = bf16_bits_to_f32(sf.B).astype(np.float64)
+        M = np.matmul(B, A)                               # [h_out_j, h_in]
+        ref = np.float64(sf.scale) * np.matmul(xf, M.T)   # [T, h_out_j]
+        got = d[:, col:col + sf.B.shape[0]]
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        assert err <= 1e-12, err
+        col += sf.B.shape[0]
+
+
+def test_integer_brute_force_exact():
+    """Integer mode: exact rational brute force through B @ A first."""
+    w = _single_adapter_lane(12, 40, [9, 5], 3, 6, mode="int")
+    lane = w.lanes["l"]
+    d, _, _ = oracle.workload_lane_delta(w, "l")
+    x = bf16_bits_to_f32(lane.x).astype(np.int64)
+    (aid, ad), = w.adapters.items()
+    col = 0
+    for sf in ad.lanes["l"]:
+        A = bf16_bits_to_f32(sf.A).astype(np.int64).tolist()
+        B = bf16_bits_to_f32(sf.B).astype(np.int64).tolist()
+        M = [[sum(B[o][k] * A[k][i] for k in range(sf.rank)) for i in range(40)]
+             for o in range(len(B))]
+        for t in range(x.shape[0]):
+            for o in range(len(B)):
+                exact = sum(M[o][i] * int(x[t, i]) for i in range(40)) * sf.scale
+                assert d[t, col + o] == exact
+        col += len(B)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_base_rows_get_zero_delta_and_scale_zero():
+    w = generate(config_by_name("tiny"))
+    d, tok, _ = oracle.workload_lane_delta(w, "proj")
+    assert (tok == 0).any() and (tok != 0).any()
+    assert np.all(d[tok == 0] == 0.0)
+    assert np.all(np.abs(d[tok != 0]).max(axis=1) > 0)
+    lane = w.lanes["proj"]
+    factors = {aid: [(sf.A, sf.B, sf.rank, 0.0) for sf in ad.lanes["proj"]]
+               for aid, ad in w.adapters.items()}
+    d0 = oracle.lane_delta(lane.x, "bf16", tok, factors, lane.spec.h_out, 0, 64)
+    assert np.all(d0 == 0.0)
+
+
+def test_permutation_invariance():
+    w = generate(config_by_name("decode_mix"))
+    d, tok, _ = oracle.workload_lane_delta(w, "qkv")
+    perm = np.random.default_rng(3).permutation(len(tok))
+    lane = w.lanes["qkv"]
+    factors = {aid: [(sf.A, sf.B, sf.rank, sf.scale) for sf in ad.lanes["qkv"]]
+               for aid, ad in w.adapters.items()}
+    dp = oracle.lane_delta(lane.x[perm], "bf16", tok[perm], factors,
+                           lane.spec.h_out, 0, 4096)
+    assert np.array_equal(dp, d[perm])
+
+
+def test_linearity_exact_in_integer_mode():
+    w = _single_adapter_lane(13, 64, [16], 4, 8, mode="int")
+    lane = w.lanes["l"]
+    x = bf16_bits_to_f32(lane.x)
+    x1 = np.where(np.arange(64) < 32, x, 0).astype(np.float32)
+    x2 = (x - x1).astype(np.float32)
+    (aid, ad), = w.adapters.items()
+    f = {aid: [(sf.A, sf.B, sf.rank, sf.scale) for sf in ad.lanes["l"]]}
+    tok = np.full(8, aid)
+    d = oracle.lane_delta(lane.x, "bf16", tok, f, [16], 0, 64)
+    d1 = oracle.lane_delta(f32_to_bf16_bits(x1), "bf16", tok, f, [16], 0, 64)
+    d2 = oracle.lane_delta(f32_to_bf16_bits(x2), "bf16", tok, f, [16], 0, 64)
+    assert np.array_equal(d, d1 + d2)
+    assert np.abs(d).max() > 0
+
+
+def test_fused_slices_equal_separate_lanes():
+    w = generate(config_by_name("decode_mix"))
+    d, tok, _ = oracle.workload_lane_delta(w, "qkv")
+    lane = w.lanes["qkv"]
+    col = 0
+    for j, hj in enumerate(lane.spec.h_out):
+        f = {aid: [tuple((sf.A, sf.B, sf.rank, sf.scale))
+                   for sf in ad.lanes["qkv"][j:j + 1]]
+             for aid, ad in w.adapters.items()}
+        dj = oracle.lane_delta(lane.x, "bf16", tok, f, [hj], 0, 4096)
+        assert np.array_equal(dj, d[:, col:col + hj])
+        col += hj
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+def test_column_shares_sum_to_unsharded(mode):
+    """A cut by input columns: the shares' deltas sum to the full delta."""
+    tp = 8
+    w = _single_adapter_lane(14, 8 * 24, [33], 5, 7, mode=mode)
+    lane = w.lanes["l"]
+    (aid, ad), = w.adapters.items()
+    f = {aid: [(sf.A, sf.B, sf.rank, sf.scale) for sf in ad.lanes["l"]]}
+    tok = np.full(7, aid)
+    full = oracle.lane_delta(lane.x, "bf16", tok, f, [33], 0, 8 * 24)
+    parts = np.zeros_like(full)
+    for r in range(tp):
+        xs = np.ascontiguousarray(lane.x[:, r * 24:(r + 1) * 24])
+        parts += oracle.lane_delta(xs, "bf16", tok, f, [33], r * 24, 24)
+    if mode == "int":
+        assert np.array_equal(parts, full)
+    else:
+        assert np.abs(parts - full).max() <= 1e-12 * np.abs(full).max()
+
+
+def test_deferred_rows_untouched():
+    spec = config_by_name("many_tenants")
+    w = generate(spec, lanes=("o_proj",))
+    d, tok, adm = oracle.workload_lane_delta(w, "o_proj", max_loras=8)
+    assert not all(adm)
+    lens = w.seq_len
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    for s, ok in enumerate(adm):
+        if not ok:
+            assert np.all(d[starts[s]:starts[s] + lens[s]] == 0.0)
+    assert len(set(tok.tolist()) - {0}) == 8
