@@ -1,0 +1,763 @@
+// Host side of the C ABI declared in include/lora.h: validation, the adapter
+// pool, admission and routing, and kernel launches.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+
+#include "lora_internal.h"
+
+using namespace lora;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int32_t hip_fail(hipError_t e, const char *what)
+{
+    return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_desc(const lora_lane_desc *d)
+{
+    if (!d) return fail(LORA_ERR_ARG, "lane descriptor is null");
+    if (d->n_slices < 1 || d->n_slices > LORA_MAX_SLICES)
+        return fail(LORA_ERR_SHAPE, "n_slices=%d outside 1..%d", d->n_slices, LORA_MAX_SLICES);
+    if (d->h_in <= 0 || d->h_in % 8 || d->h_in > (1 << 22))
+        return fail(LORA_ERR_SHAPE, "h_in=%d must be a positive multiple of 8 (<= 2^22)", d->h_in);
+    int64_t H = 0;
+    for (int j = 0; j < d->n_slices; ++j) {
+        if (d->h_out[j] <= 0 || d->h_out[j] % 8 || d->h_out[j] > (1 << 22))
+            return fail(LORA_ERR_SHAPE, "h_out[%d]=%d must be a positive multiple of 8", j,
+                        d->h_out[j]);
+        H += d->h_out[j];
+    }
+    if (H > (1 << 24)) return fail(LORA_ERR_SHAPE, "sum of h_out %lld too large", (long long)H);
+    if (d->max_slots < 1 || d->max_slots > 65535)
+        return fail(LORA_ERR_SHAPE, "max_slots=%d outside 1..65535", d->max_slots);
+    if (d->max_rank < 1 || d->max_rank > LORA_MAX_RANK)
+        return fail(LORA_ERR_RANK, "max_rank=%d outside 1..%d", d->max_rank, LORA_MAX_RANK);
+    if (d->x_dtype != LORA_DTYPE_BF16 && d->x_dtype != LORA_DTYPE_FP16)
+        return fail(LORA_ERR_DTYPE, "x_dtype=%d: only bf16 (1) and fp16 (2) inputs", d->x_dtype);
+    return LORA_OK;
+}
+
+void make_geom(const lora_lane_desc &d, LaneGeom &g)
+{
+    std::memset(&g, 0, sizeof g);
+    g.h_in = d.h_in;
+    g.n_slices = d.n_slices;
+    g.rank_pad = (int32_t)round_up(d.max_rank, kRankAlign);
+    g.x_fp16 = d.x_dtype == LORA_DTYPE_FP16;
+    int32_t col = 0;
+    for (int j = 0; j < d.n_slices; ++j) {
+        g.h_out[j] = d.h_out[j];
+        g.col_off[j] = col;
+        g.bt_slice_off[j] = (int64_t)g.rank_pad * col;
+        col += d.h_out[j];
+    }
+    g.H_out = col;
+    g.v_stride = d.n_slices * g.rank_pad;
+    g.a_slot_stride = (int64_t)d.n_slices * g.rank_pad * d.h_in;
+    g.bt_slot_stride = (int64_t)g.rank_pad * col;
+}
+
+struct PoolLayout {
+    int64_t a_off, bt_off, bn_off, rank_off, scale_off, total;
+};
+
+PoolLayout pool_layout(const lora_lane_desc &d, const LaneGeom &g)
+{
+    PoolLayout L;
+    int64_t o = 0;
+    L.a_off = o;
+    o = round_up(o + (int64_t)d.max_slots * g.a_slot_stride * 2, 256);
+    L.bt_off = o;
+    o = round_up(o + (int64_t)d.max_slots * g.bt_slot_stride * 2, 256);
+    L.bn_off = o;
+    o = round_up(o + (int64_t)d.max_slots * g.bt_slot_stride * 2, 256);
+    L.rank_off = o;
+    o = round_up(o + (int64_t)(d.max_slots + 1) * kMetaStride * 4, 256);
+    L.scale_off = o;
+    o = round_up(o + (int64_t)(d.max_slots + 1) * kMetaStride * 4, 256);
+    L.total = o;
+    return L;
+}
+
+uint16_t *slot_a(const lora_pool *p, int slot, int j)
+{
+    return p->A + (int64_t)(slot - 1) * p->geom.a_slot_stride +
+           (int64_t)j * p->geom.rank_pad * p->geom.h_in;
+}
+
+uint16_t *slot_bt(const lora_pool *p, int slot, int j)
+{
+    return p->Bt + (int64_t)(slot - 1) * p->geom.bt_slot_stride + p->geom.bt_slice_off[j];
+}
+
+uint16_t *slot_bn(const lora_pool *p, int slot, int j)
+{
+    return p->Bn + (int64_t)(slot - 1) * p->geom.bt_slot_stride + p->geom.bt_slice_off[j];
+}
+
+PoolDev pool_dev(const lora_pool *p)
+{
+    return PoolDev{p->A, p->Bt, p->Bn, p->rank_tab, p->scale_tab};
+}
+
+RoutingDev routing_dev(const lora_routing *r)
+{
+    return RoutingDev{reinterpret_cast<const int4 *>(r->dev + r->off_seg), r->dev + r->off_row,
+                      r->dev + r->off_tok};
+}
+
+// Largest rank over the routing's distinct slots and the lane's slices.
+int batch_max_rank(const lora_pool *p, const lora_routing *r)
+{
+    int m = 0;
+    for (int32_t s : r->distinct_slots)
+        for (int j = 0; j < p->desc.n_slices; ++j)
+            m = std::max(m, p->h_rank[(size_t)s * kMetaStride + j]);
+    return m;
+}
+
+int32_t check_pair(const lora_pool *p, const lora_routing *r)
+{
+    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
+    if (r->pool_max_slots > p->desc.max_slots)
+        return fail(LORA_ERR_MISMATCH, "routing resolved slots up to %d, pool has %d",
+                    r->pool_max_slots, p->desc.max_slots);
+    for (int32_t s : r->distinct_slots)
+        if (s < 1 || s > p->desc.max_slots || p->slot_to_id[s] == 0)
+            return fail(LORA_ERR_MISMATCH, "routing uses slot %d, which this pool does not hold",
+                        s);
+    return LORA_OK;
+}
+
+int32_t check_x(const lora_pool *p, const void *x, int64_t ldx)
+{
+    if (!x) return fail(LORA_ERR_ARG, "x is null");
+    if (!aligned16(x)) return fail(LORA_ERR_SHAPE, "x must be 16-byte aligned");
+    if (ldx < p->desc.h_in || ldx % 8)
+        return fail(LORA_ERR_SHAPE, "ldx=%lld must be >= h_in=%d and a multiple of 8",
+                    (long long)ldx, p->desc.h_in);
+    return LORA_OK;
+}
+
+int32_t check_y(const lora_pool *p, const float *y, int64_t ldy)
+{
+    if (!y) return fail(LORA_ERR_ARG, "y is null");
+    if (!aligned16(y)) return fail(LORA_ERR_SHAPE, "y must be 16-byte aligned");
+    if (ldy < p->geom.H_out || ldy % 4)
+        return fail(LORA_ERR_SHAPE, "ldy=%lld must be >= sum(h_out)=%d and a multiple of 4",
+                    (long long)ldy, p->geom.H_out);
+    return LORA_OK;
+}
+
+int32_t check_v(const float *v)
+{
+    if (!v) return fail(LORA_ERR_ARG, "v is null");
+    if (!aligned16(v)) return fail(LORA_ERR_SHAPE, "v must be 16-byte aligned");
+    return LORA_OK;
+}
+
+int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
+                       float *v, hipStream_t s)
+{
+    const lora_routing_info &I = r->info;
+    const int kmax = batch_max_rank(p, r);
+    RoutingDev rd = routing_dev(r);
+    PoolDev pd = pool_dev(p);
+    if (I.n_decode_segments > 0) {
+        int kb = (kmax + kKBlock - 1) / kKBlock;
+        hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, s);
+        if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
+    }
+    if (I.n_prefill_segments > 0) {
+        int nt = (kmax + 15) / 16;
+        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, I.n_decode_segments,
+                                          I.n_prefill_segments, nt, x, ldx, v, s);
+        if (e != hipSuccess) return hip_fail(e, "shrink (prefill) launch");
+    }
+    return LORA_OK;
+}
+
+int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v, float *y,
+                       int64_t ldy, hipStream_t s)
+{
+    const lora_routing_info &I = r->info;
+    RoutingDev rd = routing_dev(r);
+    PoolDev pd = pool_dev(p);
+    int hmax = 0;
+    for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
+    if (I.n_decode_segments > 0) {
+        int tiles = (hmax + kExpandTile - 1) / kExpandTile;
+        hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, v, y, ldy, s);
+        if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
+    }
+    if (I.n_prefill_segments > 0) {
+        int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
+        hipError_t e = launch_expand_mfma(p->geom, pd, rd, I.n_decode_segments,
+                                          I.n_prefill_segments, tiles, v, y, ldy, s);
+        if (e != hipSuccess) return hip_fail(e, "expand (prefill) launch");
+    }
+    return LORA_OK;
+}
+
+// Admission, per-token slots and segments of one candidate batch, on the host.
+// `resolve(id)` gives the slot of a resident id, or 0.
+template <class Resolve>
+int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
+                     int32_t max_loras, int32_t prefill_min_len, int32_t max_tokens,
+                     int32_t max_slots, Resolve resolve, Plan &pl)
+{
+    if (n_seq < 0) return fail(LORA_ERR_SHAPE, "n_seq < 0");
+    if (n_seq > 0 && (!seq_adapter_id || !seq_len))
+        return fail(LORA_ERR_ARG, "null per-sequence array");
+    if (max_loras < 0) return fail(LORA_ERR_ARG, "max_loras < 0");
+    if (prefill_min_len < 1) return fail(LORA_ERR_ARG, "prefill_min_len < 1");
+    int64_t T = 0;
+    for (int i = 0; i < n_seq; ++i) {
+        if (seq_len[i] < 0) return fail(LORA_ERR_SHAPE, "seq_len[%d] < 0", i);
+        if (seq_adapter_id[i] < 0) return fail(LORA_ERR_ARG, "seq_adapter_id[%d] < 0", i);
+        T += seq_len[i];
+    }
+    if (T > max_tokens)
+        return fail(LORA_ERR_CAPACITY, "batch has %lld rows > max_tokens=%d", (long long)T,
+                    max_tokens);
+
+    // Admission (tokenspeed PR #976, max_loras batch cap): walk in order; base
+    // is free, an adapter already admitted is free, a new adapter past the cap
+    // is deferred and the walk goes on; max_loras == 0 means no cap.
+    std::vector<uint8_t> &adm = pl.adm;
+    adm.assign((size_t)n_seq, 0);
+    std::vector<int32_t> seq_slot((size_t)n_seq, 0);
+    std::vector<int32_t> distinct_ids;
+    std::unordered_map<int32_t, int32_t> id_slot;
+    for (int i = 0; i < n_seq; ++i) {
+        const int32_t id = seq_adapter_id[i];
+        if (id == 0) {
+            adm[i] = 1;
+            continue;
+        }
+        auto it = id_slot.find(id);
+        if (it != id_slot.end()) {
+            adm[i] = 1;
+            seq_slot[i] = it->second;
+        } else if (max_loras == 0 || (int32_t)distinct_ids.size() < max_loras) {
+            const int32_t s = resolve(id);
+            if (s < 1 || s > max_slots)
+                return fail(LORA_ERR_UNKNOWN_ADAPTER,
+                            "sequence %d names adapter %d, which is not resident", i, id);
+            id_slot.emplace(id, s);
+            distinct_ids.push_back(id);
+            adm[i] = 1;
+            seq_slot[i] = s;
+        }
+    }
+
+    // Per-token slots; decode rows counted per slot in order of first appearance.
+    pl.tok.assign((size_t)T, 0);
+    std::vector<int32_t> count((size_t)max_slots + 1, 0);
+    std::vector<int32_t> slot_order;
+    int64_t row0 = 0, n_dec = 0, n_pre = 0;
+    for (int i = 0; i < n_seq; ++i) {
+        const int32_t L = seq_len[i], s = seq_slot[i];
+        if (s != 0 && L > 0) {
+            std::fill(pl.tok.begin() + row0, pl.tok.begin() + row0 + L, s);
+            if (L >= prefill_min_len) {
+                n_pre += L;
+            } else {
+                if (count[s] == 0) slot_order.push_back(s);
+                count[s] += L;
+                n_dec += L;
+            }
+        }
+        row0 += L;
+    }
+    std::vector<int32_t> start((size_t)max_slots + 1, 0);
+    {
+        int32_t acc = 0;
+        for (int32_t s : slot_order) {
+            start[s] = acc;
+            acc += count[s];
+        }
+    }
+    pl.rows.assign((size_t)(n_dec + n_pre), 0);
+    pl.seg.clear();
+    // decode rows: grouped by slot, token order within a slot, chunks of kDecodeSegRows
+    {
+        std::vector<int32_t> fill = start;
+        row0 = 0;
+        for (int i = 0; i < n_seq; ++i) {
+            const int32_t L = seq_len[i], s = seq_slot[i];
+            if (s != 0 && L > 0 && L < prefill_min_len)
+                for (int32_t t = 0; t < L; ++t) pl.rows[(size_t)fill[s]++] = (int32_t)(row0 + t);
+            row0 += L;
+        }
+        for (int32_t s : slot_order)
+            for (int32_t b = 0; b < count[s]; b += kDecodeSegRows) {
+                pl.seg.push_back(s);
+                pl.seg.push_back(start[s] + b);
+                pl.seg.push_back(std::min(kDecodeSegRows, count[s] - b));
+                pl.seg.push_back(kSegDecode);
+            }
+    }
+    const int32_t n_dec_seg = (int32_t)(pl.seg.size() / 4);
+    // prefill sequences: contiguous chunks of kPrefillSegRows rows, one slot each
+    {
+        int64_t pos = n_dec;
+        row0 = 0;
+        for (int i = 0; i < n_seq; ++i) {
+            const int32_t L = seq_len[i], s = seq_slot[i];
+            if (s != 0 && L >= prefill_min_len)
+                for (int32_t b = 0; b < L; b += kPrefillSegRows) {
+                    const int32_t n = std::min(kPrefillSegRows, L - b);
+                    pl.seg.push_back(s);
+                    pl.seg.push_back((int32_t)pos);
+                    pl.seg.push_back(n);
+                    pl.seg.push_back(kSegPrefill);
+                    for (int32_t t = 0; t < n; ++t) pl.rows[(size_t)pos++] = (int32_t)(row0 + b + t);
+                }
+            row0 += L;
+        }
+    }
+    const int32_t n_seg = (int32_t)(pl.seg.size() / 4);
+    pl.info.n_tokens = (int32_t)T;
+    pl.info.n_active = (int32_t)(n_dec + n_pre);
+    pl.info.n_segments = n_seg;
+    pl.info.n_decode_segments = n_dec_seg;
+    pl.info.n_prefill_segments = n_seg - n_dec_seg;
+    pl.info.n_distinct = (int32_t)distinct_ids.size();
+    pl.info.n_seqs = n_seq;
+    int32_t na = 0;
+    for (int i = 0; i < n_seq; ++i) na += adm[i];
+    pl.info.n_admitted_seqs = na;
+    pl.distinct_slots.clear();
+    for (int32_t id : distinct_ids) pl.distinct_slots.push_back(id_slot[id]);
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_last_error(void) { return g_err.c_str(); }
+
+const char *lora_version(void) { return "adapter_deltas_amd 0.1 (gfx950)"; }
+
+// ------------------------------------------------------------------ pool --
+
+int32_t lora_pool_bytes(const lora_lane_desc *desc, int64_t *bytes_out)
+{
+    if (int32_t rc = check_desc(desc)) return rc;
+    if (!bytes_out) return fail(LORA_ERR_ARG, "bytes_out is null");
+    LaneGeom g;
+    make_geom(*desc, g);
+    *bytes_out = pool_layout(*desc, g).total;
+    return LORA_OK;
+}
+
+int32_t lora_pool_create(const lora_lane_desc *desc, void *dev_mem, int64_t dev_bytes,
+                         void *stream, lora_pool **pool_out)
+{
+    if (int32_t rc = check_desc(desc)) return rc;
+    if (!dev_mem || !pool_out) return fail(LORA_ERR_ARG, "dev_mem or pool_out is null");
+    if (reinterpret_cast<uintptr_t>(dev_mem) % 256)
+        return fail(LORA_ERR_SHAPE, "pool memory must be 256-byte aligned");
+    LaneGeom g;
+    make_geom(*desc, g);
+    PoolLayout L = pool_layout(*desc, g);
+    if (dev_bytes < L.total)
+        return fail(LORA_ERR_CAPACITY, "pool memory %lld bytes < %lld needed",
+                    (long long)dev_bytes, (long long)L.total);
+    lora_pool *p = new (std::nothrow) lora_pool();
+    if (!p) return fail(LORA_ERR_CAPACITY, "out of host memory");
+    p->desc = *desc;
+    p->geom = g;
+    char *base = static_cast<char *>(dev_mem);
+    p->A = reinterpret_cast<uint16_t *>(base + L.a_off);
+    p->Bt = reinterpret_cast<uint16_t *>(base + L.bt_off);
+    p->Bn = reinterpret_cast<uint16_t *>(base + L.bn_off);
+    p->rank_tab = reinterpret_cast<int32_t *>(base + L.rank_off);
+    p->scale_tab = reinterpret_cast<float *>(base + L.scale_off);
+    p->h_rank.assign((size_t)(desc->max_slots + 1) * kMetaStride, 0);
+    p->h_scale.assign((size_t)(desc->max_slots + 1) * kMetaStride, 0.f);
+    p->slot_to_id.assign((size_t)desc->max_slots + 1, 0);
+    hipError_t e = launch_clear_meta(p->rank_tab, p->scale_tab, desc->max_slots + 1,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "clearing pool metadata");
+    }
+    *pool_out = p;
+    return LORA_OK;
+}
+
+int32_t lora_pool_destroy(lora_pool *pool)
+{
+    delete pool;
+    return LORA_OK;
+}
+
+int32_t lora_pool_load(lora_pool *p, int32_t adapter_id, int32_t slot, const void *const *A,
+                       const int64_t *lda, int64_t a_col0, const void *const *B,
+                       const int64_t *ldb, const int32_t *rank, const float *scale,
+                       int32_t src_on_device, void *stream, int32_t *slot_out)
+{
+    if (!p || !A || !lda || !B || !ldb || !rank || !scale)
+        return fail(LORA_ERR_ARG, "null argument to lora_pool_load");
+    if (adapter_id <= 0)
+        return fail(LORA_ERR_ARG, "adapter id %d: ids are > 0 (0 is the base model)", adapter_id);
+    if (src_on_device != 0 && src_on_device != 1)
+        return fail(LORA_ERR_ARG, "src_on_device must be 0 or 1");
+    const lora_lane_desc &d = p->desc;
+    if (slot == 0 || slot < -1 || slot > d.max_slots)
+        return fail(LORA_ERR_SLOT, "slot %d: slots are 1..%d (or -1 for any)", slot, d.max_slots);
+    if (a_col0 < 0) return fail(LORA_ERR_SHAPE, "a_col0 < 0");
+    for (int j = 0; j < d.n_slices; ++j) {
+        if (!A[j] || !B[j]) return fail(LORA_ERR_ARG, "slice %d: null factor", j);
+        if (rank[j] < 1 || rank[j] > d.max_rank)
+            return fail(LORA_ERR_RANK, "slice %d: rank %d outside 1..%d", j, rank[j], d.max_rank);
+        if (!std::isfinite(scale[j]))
+            return fail(LORA_ERR_ARG, "slice %d: scale is not finite", j);
+        if (lda[j] < a_col0 + d.h_in)
+            return fail(LORA_ERR_SHAPE, "slice %d: lda %lld < a_col0 + h_in = %lld", j,
+                        (long long)lda[j], (long long)(a_col0 + d.h_in));
+        if (ldb[j] < rank[j])
+            return fail(LORA_ERR_SHAPE, "slice %d: ldb %lld < rank %d", j, (long long)ldb[j],
+                        rank[j]);
+    }
+    auto it = p->id_to_slot.find(adapter_id);
+    int target = slot;
+    if (target == -1) {
+        if (it != p->id_to_slot.end()) {
+            target = it->second;
+        } else {
+            for (int s = 1; s <= d.max_slots; ++s)
+                if (p->slot_to_id[s] == 0) {
+                    target = s;
+                    break;
+                }
+            if (target == -1)
+                return fail(LORA_ERR_CAPACITY, "all %d slots are taken", d.max_slots);
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const LaneGeom &g = p->geom;
+    hipError_t e = hipSuccess;
+    if (src_on_device) {
+        for (int j = 0; j < d.n_slices && e == hipSuccess; ++j) {
+            e = launch_pack_a(slot_a(p, target, j), static_cast<const uint16_t *>(A[j]), lda[j],
+                              a_col0, rank[j], g.rank_pad, d.h_in, st);
+            if (e == hipSuccess)
+                e = launch_pack_bt(slot_bt(p, target, j), static_cast<const uint16_t *>(B[j]),
+                                   ldb[j], rank[j], g.rank_pad, d.h_out[j], st);
+            if (e == hipSuccess)
+                e = launch_pack_bn(slot_bn(p, target, j), static_cast<const uint16_t *>(B[j]),
+                                   ldb[j], rank[j], g.rank_pad, d.h_out[j], st);
+        }
+        if (e == hipSuccess) e = launch_set_meta(p->rank_tab, p->scale_tab, target, d.n_slices,
+                                                  rank, scale, st);
+        if (e != hipSuccess) return hip_fail(e, "packing adapter factors");
+    } else {
+        std::vector<uint16_t> pa((size_t)g.a_slot_stride, 0), pb((size_t)g.bt_slot_stride, 0);
+        std::vector<uint16_t> pn((size_t)g.bt_slot_stride, 0);
+        for (int j = 0; j < d.n_slices; ++j) {
+            const uint16_t *a = static_cast<const uint16_t *>(A[j]);
+            const uint16_t *b = static_cast<const uint16_t *>(B[j]);
+            uint16_t *da = pa.data() + (size_t)j * g.rank_pad * d.h_in;
+            for (int k = 0; k < rank[j]; ++k)
+                std::memcpy(da + (size_t)k * d.h_in, a + k * lda[j] + a_col0,
+                            (size_t)d.h_in * 2);
+            uint16_t *db = pb.data() + g.bt_slice_off[j];
+            const int hj = d.h_out[j];
+            uint16_t *dn = pn.data() + g.bt_slice_off[j];
+            for (int o = 0; o < hj; ++o)
+                for (int k = 0; k < rank[j]; ++k) {
+                    db[(size_t)k * hj + o] = b[o * ldb[j] + k];
+                    dn[(size_t)o * g.rank_pad + k] = b[o * ldb[j] + k];
+                }
+        }
+        e = hipMemcpyAsync(slot_a(p, target, 0), pa.data(), pa.size() * 2,
+                           hipMemcpyHostToDevice, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_bt(p, target, 0), pb.data(), pb.size() * 2,
+                               hipMemcpyHostToDevice, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(slot_bn(p, target, 0), pn.data(), pn.size() * 2,
+                               hipMemcpyHostToDevice, st);
+        if (e == hipSuccess)
+            e = launch_set_meta(p->rank_tab, p->scale_tab, target, d.n_slices, rank, scale, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "copying adapter factors");
+    }
+    // bookkeeping: evict this id from an old slot, and the old occupant of target
+    if (it != p->id_to_slot.end() && it->second != target) p->slot_to_id[it->second] = 0;
+    if (int32_t old = p->slot_to_id[target]; old != 0 && old != adapter_id)
+        p->id_to_slot.erase(old);
+    p->id_to_slot[adapter_id] = target;
+    p->slot_to_id[target] = adapter_id;
+    for (int j = 0; j < kMetaStride; ++j) {
+        p->h_rank[(size_t)target * kMetaStride + j] = j < d.n_slices ? rank[j] : 0;
+        p->h_scale[(size_t)target * kMetaStride + j] = j < d.n_slices ? scale[j] : 0.f;
+    }
+    if (slot_out) *slot_out = target;
+    return LORA_OK;
+}
+
+int32_t lora_pool_unload(lora_pool *p, int32_t adapter_id)
+{
+    if (!p) return fail(LORA_ERR_ARG, "pool is null");
+    auto it = p->id_to_slot.find(adapter_id);
+    if (it == p->id_to_slot.end())
+        return fail(LORA_ERR_UNKNOWN_ADAPTER, "adapter %d is not resident", adapter_id);
+    p->slot_to_id[it->second] = 0;
+    p->id_to_slot.erase(it);
+    return LORA_OK;
+}
+
+int32_t lora_pool_slot_of(const lora_pool *p, int32_t adapter_id, int32_t *slot_out)
+{
+    if (!p || !slot_out) return fail(LORA_ERR_ARG, "null argument");
+    auto it = p->id_to_slot.find(adapter_id);
+    if (it == p->id_to_slot.end())
+        return fail(LORA_ERR_UNKNOWN_ADAPTER, "adapter %d is not resident", adapter_id);
+    *slot_out = it->second;
+    return LORA_OK;
+}
+
+// --------------------------------------------------------------- routing --
+
+int32_t lora_routing_bytes(int32_t max_tokens, int64_t *bytes_out)
+{
+    if (max_tokens < 1 || max_tokens > (1 << 26))
+        return fail(LORA_ERR_SHAPE, "max_tokens=%d outside 1..2^26", max_tokens);
+    if (!bytes_out) return fail(LORA_ERR_ARG, "bytes_out is null");
+    // segments (4 words each, at most one per active row) + row list + token slots
+    *bytes_out = round_up((int64_t)max_tokens * 6 * 4 + 64, 256);
+    return LORA_OK;
+}
+
+int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
+                            int64_t dev_bytes, lora_routing **routing_out)
+{
+    int64_t need = 0;
+    if (int32_t rc = lora_routing_bytes(max_tokens, &need)) return rc;
+    if (max_seqs < 1 || max_seqs > (1 << 26))
+        return fail(LORA_ERR_SHAPE, "max_seqs=%d outside 1..2^26", max_seqs);
+    if (!dev_mem || !routing_out) return fail(LORA_ERR_ARG, "dev_mem or routing_out is null");
+    if (reinterpret_cast<uintptr_t>(dev_mem) % 16)
+        return fail(LORA_ERR_SHAPE, "routing memory must be 16-byte aligned");
+    if (dev_bytes < need)
+        return fail(LORA_ERR_CAPACITY, "routing memory %lld bytes < %lld needed",
+                    (long long)dev_bytes, (long long)need);
+    lora_routing *r = new (std::nothrow) lora_routing();
+    if (!r) return fail(LORA_ERR_CAPACITY, "out of host memory");
+    r->max_tokens = max_tokens;
+    r->max_seqs = max_seqs;
+    r->dev = static_cast<int32_t *>(dev_mem);
+    r->dev_words = need / 4;
+    r->stage[0] = r->stage[1] = nullptr;
+    r->stage_done[0] = r->stage_done[1] = nullptr;
+    for (int i = 0; i < 2; ++i) {
+        hipError_t e = hipHostMalloc(reinterpret_cast<void **>(&r->stage[i]), need,
+                                     hipHostMallocDefault);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->stage_done[i], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            lora_routing_destroy(r);
+            return hip_fail(e, "allocating routing staging");
+        }
+    }
+    r->stage_next = 0;
+    std::memset(&r->info, 0, sizeof r->info);
+    r->off_seg = r->off_row = r->off_tok = 0;
+    r->pool_max_slots = 0;
+    *routing_out = r;
+    return LORA_OK;
+}
+
+int32_t lora_routing_destroy(lora_routing *r)
+{
+    if (!r) return LORA_OK;
+    for (int i = 0; i < 2; ++i) {
+        if (r->stage_done[i]) {
+            (void)hipEventSynchronize(r->stage_done[i]);
+            (void)hipEventDestroy(r->stage_done[i]);
+        }
+        if (r->stage[i]) (void)hipHostFree(r->stage[i]);
+    }
+    delete r;
+    return LORA_OK;
+}
+
+int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq_adapter_id,
+                           const int32_t *seq_len, int32_t max_loras, int32_t prefill_min_len,
+                           lora_routing *r, uint8_t *admitted_out, int32_t *n_distinct_out,
+                           void *stream)
+{
+    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
+    if (n_seq > r->max_seqs)
+        return fail(LORA_ERR_CAPACITY, "n_seq=%d > max_seqs=%d", n_seq, r->max_seqs);
+    Plan &pl = r->plan;
+    auto resolve = [p](int32_t id) -> int32_t {
+        auto it = p->id_to_slot.find(id);
+        return it == p->id_to_slot.end() ? 0 : it->second;
+    };
+    if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
+                                  r->max_tokens, p->desc.max_slots, resolve, pl))
+        return rc;
+
+    const int64_t words = pl.words();
+    if (words > r->dev_words)
+        return fail(LORA_ERR_CAPACITY, "routing needs %lld words > %lld", (long long)words,
+                    (long long)r->dev_words);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int b = r->stage_next;
+    hipError_t e = hipEventSynchronize(r->stage_done[b]);
+    if (e != hipSuccess) return hip_fail(e, "waiting for routing staging");
+    pl.pack(r->stage[b]);
+    if (words > 0) {
+        e = hipMemcpyAsync(r->dev, r->stage[b], (size_t)words * 4, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipEventRecord(r->stage_done[b], st);
+        if (e != hipSuccess) return hip_fail(e, "copying routing to the device");
+        r->stage_next = b ^ 1;
+    }
+    r->off_seg = 0;
+    r->off_row = (int32_t)pl.off_row();
+    r->off_tok = (int32_t)pl.off_tok();
+    r->info = pl.info;
+    r->pool_max_slots = p->desc.max_slots;
+    r->distinct_slots = pl.distinct_slots;
+    if (admitted_out)
+        for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
+    if (n_distinct_out) *n_distinct_out = pl.info.n_distinct;
+    return LORA_OK;
+}
+
+int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
+                          int32_t max_loras, int32_t prefill_min_len, int32_t n_resident,
+                          const int32_t *resident_id, const int32_t *resident_slot,
+                          int32_t max_slots, int32_t max_tokens, int32_t *words_out,
+                          int64_t words_capacity, int32_t *offsets_out,
+                          lora_routing_info *info_out, uint8_t *admitted_out)
+{
+    if (n_resident < 0 || (n_resident > 0 && (!resident_id || !resident_slot)))
+        return fail(LORA_ERR_ARG, "bad resident table");
+    if (max_slots < 1 || max_slots > 65535)
+        return fail(LORA_ERR_SHAPE, "max_slots=%d outside 1..65535", max_slots);
+    if (max_tokens < 1) return fail(LORA_ERR_SHAPE, "max_tokens < 1");
+    std::unordered_map<int32_t, int32_t> table;
+    for (int i = 0; i < n_resident; ++i) {
+        if (resident_id[i] <= 0 || resident_slot[i] < 1 || resident_slot[i] > max_slots)
+            return fail(LORA_ERR_SLOT, "resident entry %d: id %d slot %d", i, resident_id[i],
+                        resident_slot[i]);
+        table[resident_id[i]] = resident_slot[i];
+    }
+    auto resolve = [&table](int32_t id) -> int32_t {
+        auto it = table.find(id);
+        return it == table.end() ? 0 : it->second;
+    };
+    Plan pl;
+    if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
+                                  max_tokens, max_slots, resolve, pl))
+        return rc;
+    if (!words_out || !offsets_out || !info_out)
+        return fail(LORA_ERR_ARG, "null output");
+    if (pl.words() > words_capacity)
+        return fail(LORA_ERR_CAPACITY, "plan needs %lld words > %lld", (long long)pl.words(),
+                    (long long)words_capacity);
+    pl.pack(words_out);
+    offsets_out[0] = 0;
+    offsets_out[1] = (int32_t)pl.off_row();
+    offsets_out[2] = (int32_t)pl.off_tok();
+    *info_out = pl.info;
+    if (admitted_out)
+        for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
+    return LORA_OK;
+}
+
+int32_t lora_routing_get_info(const lora_routing *r, lora_routing_info *info_out)
+{
+    if (!r || !info_out) return fail(LORA_ERR_ARG, "null argument");
+    *info_out = r->info;
+    return LORA_OK;
+}
+
+int32_t lora_routing_token_slots(const lora_routing *r, const int32_t **dev_ptr_out)
+{
+    if (!r || !dev_ptr_out) return fail(LORA_ERR_ARG, "null argument");
+    *dev_ptr_out = r->dev + r->off_tok;
+    return LORA_OK;
+}
+
+// --------------------------------------------------------------- compute --
+
+int32_t lora_shrink(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
+                    float *v, void *stream)
+{
+    if (int32_t rc = check_pair(p, r)) return rc;
+    if (r->info.n_active == 0) return LORA_OK;
+    if (int32_t rc = check_x(p, x, ldx)) return rc;
+    if (int32_t rc = check_v(v)) return rc;
+    return enqueue_shrink(p, r, x, ldx, v, static_cast<hipStream_t>(stream));
+}
+
+int32_t lora_expand(const lora_pool *p, const lora_routing *r, const float *v, float *y,
+                    int64_t ldy, void *stream)
+{
+    if (int32_t rc = check_pair(p, r)) return rc;
+    if (r->info.n_active == 0) return LORA_OK;
+    if (int32_t rc = check_v(v)) return rc;
+    if (int32_t rc = check_y(p, y, ldy)) return rc;
+    return enqueue_expand(p, r, v, y, ldy, static_cast<hipStream_t>(stream));
+}
+
+int32_t lora_workspace_bytes(const lora_pool *p, const lora_routing *r, int64_t *bytes_out)
+{
+    if (int32_t rc = check_pair(p, r)) return rc;
+    if (!bytes_out) return fail(LORA_ERR_ARG, "bytes_out is null");
+    *bytes_out = round_up((int64_t)r->info.n_active * p->geom.v_stride * 4, 256);
+    return LORA_OK;
+}
+
+int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
+                         float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                         void *stream)
+{
+    if (int32_t rc = check_pair(p, r)) return rc;
+    if (r->info.n_active == 0) return LORA_OK;
+    if (int32_t rc = check_x(p, x, ldx)) return rc;
+    if (int32_t rc = check_y(p, y, ldy)) return rc;
+    int64_t need = 0;
+    lora_workspace_bytes(p, r, &need);
+    if (!workspace) return fail(LORA_ERR_ARG, "workspace is null");
+    if (!aligned16(workspace)) return fail(LORA_ERR_SHAPE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(LORA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                    (long long)workspace_bytes, (long long)need);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *v = static_cast<float *>(workspace);
+    if (int32_t rc = enqueue_shrink(p, r, x, ldx, v, st)) return rc;
+    return enqueue_expand(p, r, v, y, ldy, st);
+}
+
+}  // extern "C"

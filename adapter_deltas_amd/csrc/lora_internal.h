@@ -1,0 +1,137 @@
+// Internal types shared by the host-side ABI code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "lora.h"
+
+namespace lora {
+
+constexpr int kDecodeSegRows = LORA_DECODE_SEG_ROWS;    // rows per decode segment
+constexpr int kPrefillSegRows = LORA_PREFILL_SEG_ROWS;  // rows per prefill segment
+constexpr int kRankAlign = 16;                          // rank padding of the pool
+constexpr int kKBlock = 8;                              // ranks per decode shrink task
+constexpr int kSubChunk = 512;                          // h_in elements per wave pass
+constexpr int kParts = 4;                               // interleaved h_in parts
+constexpr int kExpandTile = 512;                        // columns per decode expand task
+constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
+constexpr int kMetaStride = 4;                          // slices per slot in metadata
+
+enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1 };
+
+// Geometry of a lane's pool, passed by value to kernels.
+struct LaneGeom {
+    int32_t h_in;
+    int32_t n_slices;
+    int32_t rank_pad;
+    int32_t x_fp16;
+    int32_t h_out[LORA_MAX_SLICES];
+    int32_t col_off[LORA_MAX_SLICES];   // column of slice j in y
+    int32_t H_out;
+    int32_t v_stride;                   // floats per v row = n_slices * rank_pad
+    int64_t a_slot_stride;              // bf16 elements of A per slot
+    int64_t bt_slot_stride;             // bf16 elements of B^T per slot
+    int64_t bt_slice_off[LORA_MAX_SLICES];
+};
+
+// Device views of a pool.  Slot s >= 1 is stored at index s - 1; the
+// metadata tables have a row for slot 0 that stays zero.
+struct PoolDev {
+    const uint16_t *A;     // [max_slots][n_slices][rank_pad][h_in]
+    const uint16_t *Bt;    // [max_slots][sum_j rank_pad * h_j]   B^T, rank-major
+    const uint16_t *Bn;    // [max_slots][sum_j h_j * rank_pad]   B, output-major
+    const int32_t *rank;   // [max_slots + 1][kMetaStride]
+    const float *scale;    // [max_slots + 1][kMetaStride]
+};
+
+// Device views of a routing.  seg[i] = {slot, row_begin, n_rows, kind}.
+struct RoutingDev {
+    const int4 *seg;
+    const int32_t *row_idx;   // token row of each active row, segment order
+    const int32_t *tok_slot;  // slot per token row
+};
+
+// ---- launchers (kernels_*.hip) ----
+hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                              int n_seg, int kb_per_slice, const void *x, int64_t ldx,
+                              float *v, hipStream_t s);
+hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                              int n_seg, int tiles_per_slice, const float *v, float *y,
+                              int64_t ldy, hipStream_t s);
+hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                              int seg_begin, int n_seg, int nt_per_slice, const void *x,
+                              int64_t ldx, float *v, hipStream_t s);
+hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                              int seg_begin, int n_seg, int tiles_per_slice, const float *v,
+                              float *y, int64_t ldy, hipStream_t s);
+hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
+                         int rank, int rank_pad, int h_in, hipStream_t s);
+hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,
+                          int rank_pad, int h_out, hipStream_t s);
+hipError_t launch_pack_bn(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,
+                          int rank_pad, int h_out, hipStream_t s);
+hipError_t launch_set_meta(int32_t *rank_tab, float *scale_tab, int slot, int n_slices,
+                           const int32_t *ranks, const float *scales, hipStream_t s);
+hipError_t launch_clear_meta(int32_t *rank_tab, float *scale_tab, int n_rows,
+                             hipStream_t s);
+
+}  // namespace lora
+
+// ---- opaque handles ----
+struct lora_pool {
+    lora_lane_desc desc;
+    lora::LaneGeom geom;
+    uint16_t *A;
+    uint16_t *Bt;
+    uint16_t *Bn;
+    int32_t *rank_tab;
+    float *scale_tab;
+    std::vector<int32_t> h_rank;     // [(max_slots + 1) * kMetaStride]
+    std::vector<float> h_scale;
+    std::unordered_map<int32_t, int32_t> id_to_slot;
+    std::vector<int32_t> slot_to_id;  // [max_slots + 1], 0 = free
+};
+
+namespace lora {
+// Host tables of one batch's routing.  Packed layout (int32 words):
+// [segments: 4 per segment][active rows][pad to 4][token slots][pad to 4].
+struct Plan {
+    std::vector<int32_t> seg, rows, tok;
+    std::vector<uint8_t> adm;
+    std::vector<int32_t> distinct_slots;
+    lora_routing_info info{};
+    int64_t off_row() const { return (int64_t)seg.size(); }
+    int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
+    int64_t words() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
+    void pack(int32_t *w) const
+    {
+        int64_t o = 0;
+        for (int32_t a : seg) w[o++] = a;
+        for (int32_t a : rows) w[o++] = a;
+        while (o < off_tok()) w[o++] = 0;
+        for (int32_t a : tok) w[o++] = a;
+        while (o < words()) w[o++] = 0;
+    }
+};
+}  // namespace lora
+
+struct lora_routing {
+    int32_t max_tokens;
+    int32_t max_seqs;
+    int32_t *dev;                     // caller memory
+    int64_t dev_words;
+    int32_t *stage[2];                // pinned host staging
+    hipEvent_t stage_done[2];
+    int32_t stage_next;
+    // device views of the current batch (offsets into dev)
+    int32_t off_seg, off_row, off_tok;
+    lora_routing_info info;
+    int32_t pool_max_slots;           // slots of the pool the ids were resolved in
+    std::vector<int32_t> distinct_slots;
+    lora::Plan plan;                  // host tables, reused between builds
+};

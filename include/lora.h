@@ -1,0 +1,295 @@
+/*
+ * lora.h -- C ABI of the routed LoRA delta library for MI355X (gfx950).
+ *
+ * The library adds, for every token row t of a mixed batch whose sequence
+ * carries adapter slot s != 0,
+ *
+ *     y[t, off_j : off_j + h_j] += scale[s][j] * B[s][j] @ (A[s][j] @ x[t])
+ *
+ * to a projection's fp32 partial sum y, for each output slice j of the lane
+ * (TensorFold PR #47, third commit message: the delta is added to the fp32
+ * partial sum before the cross-rank reduction; xLLM PR #2014, "New
+ * subsystems": fused QKV with GQA k/v slices, fused gate/up, and the
+ * row-parallel o_proj / down_proj lanes).  Slot 0 is the base model: its rows
+ * are neither read nor written (tokenspeed PR #976, third commit message: id 0
+ * is the base model; TensorFold PR #47, third commit message: a slot-0 row is
+ * not read or written, and a layer no adapter edits launches nothing).
+ *
+ * Conventions for every call
+ *   - Return value: LORA_OK (0) or a negative lora_status.  No exception or
+ *     abort crosses this boundary.  lora_last_error() gives a thread-local
+ *     message for the last failing call on the calling thread.
+ *   - Arguments are validated on the host before anything is enqueued, so a
+ *     call that fails has launched nothing and written no device memory.
+ *   - Device buffers (x, y, pool memory, routing memory, workspace) belong to
+ *     the caller; the library never allocates or frees device memory.  The
+ *     library owns only its opaque host handles and, inside a routing handle,
+ *     two small pinned host staging buffers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it asynchronously; nothing synchronises
+ *     except where a call says so.
+ *   - A handle must not be used by two threads at once.  Buffers written by
+ *     a call must not be read or written on another stream until that
+ *     stream's work is ordered after the call.
+ *   - Device pointers to x, y and the workspace must be 16-byte aligned;
+ *     widths h_in and h_out[j] must be multiples of 8, ldx a multiple of 8
+ *     and ldy a multiple of 4 (elements).
+ */
+#ifndef ADAPTER_DELTAS_LORA_H
+#define ADAPTER_DELTAS_LORA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_ARG = -1,              /* null pointer, bad enum or flag          */
+    LORA_ERR_SHAPE = -2,            /* width, stride or alignment not allowed  */
+    LORA_ERR_DTYPE = -3,            /* unsupported element type                */
+    LORA_ERR_RANK = -4,             /* rank < 1 or > max_rank                  */
+    LORA_ERR_CAPACITY = -5,         /* buffer or handle too small for request  */
+    LORA_ERR_UNKNOWN_ADAPTER = -6,  /* admitted id not resident in the pool    */
+    LORA_ERR_SLOT = -7,             /* slot 0 or outside 1..max_slots          */
+    LORA_ERR_MISMATCH = -8,         /* routing built for another pool shape    */
+    LORA_ERR_HIP = -9               /* a HIP runtime call failed               */
+} lora_status;
+
+typedef enum lora_dtype {
+    LORA_DTYPE_BF16 = 1,
+    LORA_DTYPE_FP16 = 2,
+    LORA_DTYPE_FP32 = 3
+} lora_dtype;
+
+#define LORA_MAX_SLICES 4
+#define LORA_MAX_RANK 256
+
+/*
+ * One lane: a projection the delta is added to.  For a row-parallel share
+ * (o_proj, down_proj, attention wo_b, shared-expert w2 under tensor
+ * parallelism) h_in is the number of input columns this GPU holds; A is cut
+ * by those columns and B is held whole (TensorFold PR #47, first commit
+ * message; xLLM PR #2014, LoRARowParallelLinear fused mode).
+ */
+typedef struct lora_lane_desc {
+    int32_t h_in;                     /* input width on this GPU, >0, %8 == 0 */
+    int32_t n_slices;                 /* 1..LORA_MAX_SLICES                   */
+    int32_t h_out[LORA_MAX_SLICES];   /* per-slice output width, %8 == 0      */
+    int32_t max_slots;                /* adapter slots 1..max_slots           */
+    int32_t max_rank;                 /* 1..LORA_MAX_RANK                     */
+    int32_t x_dtype;                  /* LORA_DTYPE_BF16 or LORA_DTYPE_FP16   */
+} lora_lane_desc;
+
+typedef struct lora_pool lora_pool;        /* opaque host handle */
+typedef struct lora_routing lora_routing;  /* opaque host handle */
+
+typedef struct lora_routing_info {
+    int32_t n_tokens;            /* rows covered by the candidate batch       */
+    int32_t n_active;            /* admitted rows with an adapter (slot != 0) */
+    int32_t n_segments;          /* decode + prefill segments                 */
+    int32_t n_decode_segments;   /* <= LORA_DECODE_SEG_ROWS rows, one slot    */
+    int32_t n_prefill_segments;  /* <= LORA_PREFILL_SEG_ROWS rows, one slot   */
+    int32_t n_distinct;          /* distinct adapters admitted (not base)     */
+    int32_t n_admitted_seqs;
+    int32_t n_seqs;
+} lora_routing_info;
+
+#define LORA_DECODE_SEG_ROWS 8
+#define LORA_PREFILL_SEG_ROWS 64
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char *lora_last_error(void);
+
+/* Library version string. */
+const char *lora_version(void);
+
+/* ------------------------------------------------------------------ pool --
+ * Device-resident adapter factors of one lane (xLLM PR #2014, "New
+ * subsystems": LoRARuntime keeps a per-projection device pool; tokenspeed PR
+ * #976, third commit message: a registry id travels on the request and maps
+ * to a recyclable GPU buffer slot).
+ *
+ * Pool memory is one caller-allocated device buffer of lora_pool_bytes()
+ * bytes (256-byte aligned).  It holds, per slot and slice, A as
+ * [rank_pad][h_in] bf16 and B transposed as [rank_pad][h_j] bf16, zero-padded
+ * from the adapter's rank to rank_pad = max_rank rounded up to 16, plus the
+ * per-slot rank and fp32 scale.  Slot 0 has no storage.
+ */
+int32_t lora_pool_bytes(const lora_lane_desc *desc, int64_t *bytes_out);
+
+/* Binds a pool handle to caller memory and clears the slot metadata (enqueued
+ * on `stream`).  Errors: ARG (null), SHAPE (widths), DTYPE (x_dtype), RANK
+ * (max_rank), CAPACITY (dev_bytes < lora_pool_bytes). */
+int32_t lora_pool_create(const lora_lane_desc *desc, void *dev_mem, int64_t dev_bytes,
+                         void *stream, lora_pool **pool_out);
+
+int32_t lora_pool_destroy(lora_pool *pool);
+
+/*
+ * Loads one adapter's factors for every slice of the lane into a slot.
+ *
+ *   adapter_id   registry id, > 0 (0 is the base model and cannot be loaded)
+ *   slot         1..max_slots, or -1 for the slot already holding this id,
+ *                else the lowest free slot.  A slot held by another id is
+ *                taken over (that id is evicted).
+ *   A[j]         PEFT lora_A of slice j, bf16 [rank[j]][lda[j]] row-major;
+ *                columns [a_col0, a_col0 + h_in) are this GPU's share
+ *   B[j]         PEFT lora_B of slice j, bf16 [h_out[j]][ldb[j]] row-major;
+ *                columns [0, rank[j]) are read
+ *   rank[j]      1..max_rank (per-module rank: TensorFold PR #47, first
+ *                commit message)
+ *   scale[j]     finite fp32 multiplier of slice j (PEFT lora_alpha / r,
+ *                times any strength the caller applies)
+ *   src_on_device 0: A/B are host pointers (packed on the host, copied, and
+ *                the call waits for the copy); 1: device pointers (packed by a
+ *                kernel on `stream`, no wait)
+ *   slot_out     optional; receives the slot used
+ *
+ * Errors: ARG, SLOT, RANK (rank out of range), SHAPE (lda < a_col0 + h_in,
+ * ldb < rank), CAPACITY (no free slot), HIP.
+ */
+int32_t lora_pool_load(lora_pool *pool, int32_t adapter_id, int32_t slot,
+                       const void *const *A, const int64_t *lda, int64_t a_col0,
+                       const void *const *B, const int64_t *ldb,
+                       const int32_t *rank, const float *scale,
+                       int32_t src_on_device, void *stream, int32_t *slot_out);
+
+/* Forgets an adapter id; its slot becomes free.  UNKNOWN_ADAPTER if absent. */
+int32_t lora_pool_unload(lora_pool *pool, int32_t adapter_id);
+
+/* Slot of a resident id (UNKNOWN_ADAPTER if absent). */
+int32_t lora_pool_slot_of(const lora_pool *pool, int32_t adapter_id, int32_t *slot_out);
+
+/* -------------------------------------------------------------- routing --
+ * Per-batch routing, built once per batch and reusable for every lane and
+ * layer whose pools hold the same id -> slot map.
+ *
+ * Routing memory is one caller-allocated device buffer of
+ * lora_routing_bytes(max_tokens) bytes.  The handle also owns two pinned host
+ * staging buffers, so building the next batch's routing can overlap the
+ * device work of the previous one.
+ */
+int32_t lora_routing_bytes(int32_t max_tokens, int64_t *bytes_out);
+
+int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
+                            int64_t dev_bytes, lora_routing **routing_out);
+
+int32_t lora_routing_destroy(lora_routing *routing);
+
+/*
+ * Admission, slot assignment and segments for one candidate batch.
+ *
+ *   seq_adapter_id  host int32 [n_seq]: registry id per sequence, 0 = base
+ *                   (xLLM PR #2014, "Wire-up": one id per sequence, aligned
+ *                   with the query lengths)
+ *   seq_len         host int32 [n_seq]: rows of the sequence in this batch
+ *                   (>= 0); sequence i covers rows [sum(seq_len[:i]), ...)
+ *   max_loras       distinct-adapter cap, 0 = no cap.  Sequences are walked
+ *                   in order; base sequences are never charged, an adapter
+ *                   already admitted costs nothing, a sequence that would
+ *                   bring a new adapter past the cap is deferred and the walk
+ *                   goes on (tokenspeed PR #976, first commit message).  Rows
+ *                   of deferred sequences are left untouched.
+ *   prefill_min_len sequences at least this long form prefill segments of
+ *                   <= LORA_PREFILL_SEG_ROWS contiguous rows with one slot
+ *                   (TensorFold PR #47: prompt chunks run one slot for all
+ *                   their rows) and take the matrix-core path; shorter ones
+ *                   are decode rows grouped by slot into segments of
+ *                   <= LORA_DECODE_SEG_ROWS rows.  The choice depends only on
+ *                   the sequence's own length.
+ *   admitted_out    optional host uint8 [n_seq]: 1 admitted, 0 deferred
+ *   n_distinct_out  optional: distinct adapters admitted
+ *
+ * The per-token slot array, the active-row list and the segment table are
+ * written to pinned staging and copied to the routing's device memory on
+ * `stream`.  Errors: ARG, SHAPE (negative length), CAPACITY (more than
+ * max_tokens rows or max_seqs sequences), UNKNOWN_ADAPTER (an admitted id not
+ * resident in `pool`: never treated as base; TensorFold PR #47, second commit
+ * message), HIP.  On error the routing keeps its previous contents.
+ */
+int32_t lora_build_routing(const lora_pool *pool, int32_t n_seq,
+                           const int32_t *seq_adapter_id, const int32_t *seq_len,
+                           int32_t max_loras, int32_t prefill_min_len,
+                           lora_routing *routing, uint8_t *admitted_out,
+                           int32_t *n_distinct_out, void *stream);
+
+int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *info_out);
+
+/*
+ * The host half of lora_build_routing with no device involved: the same
+ * admission, slot assignment and segments, resolved against an explicit table
+ * of resident ids and written to host memory.  lora_build_routing runs exactly
+ * this planning and then copies the words to the device.
+ *
+ *   resident_id/resident_slot  [n_resident] id -> slot (1..max_slots)
+ *   words_out     host int32 [words_capacity]; receives the packed tables:
+ *                 segments {slot, first active row, rows, kind (0 decode,
+ *                 1 prefill)} at word offsets_out[0], the token row of each
+ *                 active row at offsets_out[1], and one slot per token row at
+ *                 offsets_out[2]
+ *   offsets_out   host int32 [3]
+ *   info_out      counts, as lora_routing_get_info
+ *   admitted_out  optional host uint8 [n_seq]
+ *
+ * Errors as lora_build_routing, plus SLOT (bad resident entry) and CAPACITY
+ * (words_capacity too small; lora_routing_bytes(max_tokens) / 4 words always
+ * suffice).
+ */
+int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
+                          int32_t max_loras, int32_t prefill_min_len, int32_t n_resident,
+                          const int32_t *resident_id, const int32_t *resident_slot,
+                          int32_t max_slots, int32_t max_tokens, int32_t *words_out,
+                          int64_t words_capacity, int32_t *offsets_out,
+                          lora_routing_info *info_out, uint8_t *admitted_out);
+
+/* Device pointer to the routing's per-token slot array (int32 [n_tokens]),
+ * valid after the copy enqueued by lora_build_routing has run. */
+int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **dev_ptr_out);
+
+/* --------------------------------------------------------------- compute --
+ * x:  [n_tokens][ldx] bf16 or fp16 (the lane's x_dtype), this GPU's input
+ *     columns; only rows of active tokens are read.
+ * y:  [n_tokens][ldy] fp32 partial sum; slice j occupies columns
+ *     [sum(h_out[:j]), sum(h_out[:j+1])).  Only active rows, columns
+ *     [0, sum(h_out)) are read and written.
+ * v:  [n_active][n_slices][rank_pad] fp32, rows in the routing's active-row
+ *     order: v[p][j][k] = fp32(scale[s][j] * (A[s][j] x)[k]) for k < rank;
+ *     entries at k >= rank are unspecified.
+ *
+ * Within a row every sum runs in an order fixed by the lane's widths and the
+ * adapter's rank alone, so a row's bits depend only on its own x row, its
+ * adapter's factors and its own path (decode or prefill), never on the other
+ * rows of the batch, the slot it sits in, max_rank or the launch shape
+ * (TensorFold PR #47, third commit message).
+ */
+
+/* v for all active rows (shrink: A @ x, times scale).  Errors: ARG, SHAPE,
+ * MISMATCH (routing built for a pool with more slots), HIP. */
+int32_t lora_shrink(const lora_pool *pool, const lora_routing *routing,
+                    const void *x, int64_t ldx, float *v, void *stream);
+
+/* y += B @ v for all active rows (expand).  Errors as lora_shrink. */
+int32_t lora_expand(const lora_pool *pool, const lora_routing *routing,
+                    const float *v, float *y, int64_t ldy, void *stream);
+
+/* Bytes of workspace lora_delta_apply needs for this pool and routing. */
+int32_t lora_workspace_bytes(const lora_pool *pool, const lora_routing *routing,
+                             int64_t *bytes_out);
+
+/*
+ * y += scale * B @ (A @ x) for all active rows: the result is bit-identical to
+ * lora_shrink followed by lora_expand.  The workspace (caller device memory,
+ * >= lora_workspace_bytes) holds v.  With no active row nothing is launched
+ * and LORA_OK is returned.  Errors as lora_shrink, plus CAPACITY (workspace).
+ */
+int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
+                         const void *x, int64_t ldx, float *y, int64_t ldy,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAPTER_DELTAS_LORA_H */

@@ -1,0 +1,87 @@
+"""Test helpers: run a workload lane through the C ABI and compare it with the
+fp64 oracle.
+
+Tolerance rule for real-valued inputs (bf16 or fp16 inputs, fp32 sums): per
+element, with d_gpu = y_gpu - y0 and d_ref the oracle's delta,
+    |d_gpu - d_ref| <= 1e-2 * |d_ref|   or   |d_gpu - d_ref| <= 2e-3 * N
+where N is the largest |d_ref| over the same row and output slice.  Rows the
+routing leaves alone (base model, deferred, outside the batch) must keep the
+exact bits of y0, and integer-mode inputs must give exact results.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_TOL = 1e-2
+NORM_ABS_TOL = 2e-3
+
+
+def seq_starts(lens):
+    lens = np.asarray(lens, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+
+
+def compare(y_gpu, y0, d_ref, h_out, rows=None):
+    """Tolerance check of active rows.  Returns a stats dict with 'ok'."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    y0 = np.asarray(y0, dtype=np.float64)
+    if rows is not None:
+        y_gpu, y0 = y_gpu[rows], y0[rows]
+    d_gpu = y_gpu - y0
+    err = np.abs(d_gpu - d_ref)
+    ok = np.ones_like(err, dtype=bool)
+    abs_branch = 0
+    max_rel = 0.0     # over elements with |d_ref| >= 1e-3 N
+    max_nabs = 0.0
+    col = 0
+    for hj in h_out:
+        ref = d_ref[:, col:col + hj]
+        e = err[:, col:col + hj]
+        N = np.abs(ref).max(axis=1, keepdims=True)
+        rel_ok = e <= REL_TOL * np.abs(ref)
+        abs_ok = e <= NORM_ABS_TOL * N
+        ok[:, col:col + hj] = rel_ok | abs_ok
+        abs_branch += int((~rel_ok & abs_ok).sum())
+        with np.errstate(divide="ignore", invalid="ignore"):
+            big = np.abs(ref) >= 1e-3 * N
+            rel = np.where(big, e / np.where(big, np.abs(ref), 1.0), 0.0)
+            nabs = np.where(N > 0, e / np.where(N > 0, N, 1.0), np.where(e > 0, np.inf, 0.0))
+        if rel.size:
+            max_rel = max(max_rel, float(rel.max()))
+            max_nabs = max(max_nabs, float(nabs.max()))
+        col += hj
+    return dict(ok=bool(ok.all()), n_bad=int((~ok).sum()), n=int(ok.size),
+                max_rel=max_rel, max_norm_abs=max_nabs, abs_branch=abs_branch)
+
+
+def load_lane_pool(Pool, workload, lane_name, max_slots=None, max_rank=None,
+                   slot_of=None, device="cuda", on_device=False):
+    """Pool for one lane with every adapter of the workload loaded.
+
+    slot_of: optional dict registry id -> slot (default: lowest free slot)."""
+    import torch
+    spec = workload.spec
+    lane = workload.lanes[lane_name].spec
+    ms = max_slots or spec.n_adapters
+    mr = max_rank or spec.max_rank
+    pool = Pool(lane.h_in, lane.h_out, ms, mr, lane.x_dtype, device=device)
+    for aid, ad in workload.adapters.items():
+        sl = ad.lanes[lane_name]
+        A = [s.A for s in sl]
+        B = [s.B for s in sl]
+        if on_device:
+            A = [torch.from_numpy(a.view(np.int16)).to(device) for a in A]
+            B = [torch.from_numpy(b.view(np.int16)).to(device) for b in B]
+        pool.load(aid, A, B, [s.rank for s in sl], [s.scale for s in sl],
+                  a_col0=lane.a_col0, slot=(slot_of or {}).get(aid, -1))
+    return pool
+
+
+def to_device_x(x_bits, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(device)
+
+
+def to_device_y(y, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(device)

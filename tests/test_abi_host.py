@@ -1,0 +1,161 @@
+"""CPU tests of the C ABI: the library loads, exports every function the header
+declares, validates arguments, and plans routing (admission under max_loras,
+per-token slots, segments) exactly as the oracle and the pages say."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import adapter_deltas_amd
+    return adapter_deltas_amd
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(m):
+    from adapter_deltas_amd import _lib
+    names = header_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_validation_errors_without_device(m):
+    with pytest.raises(m.LoraError) as e:
+        m.lora_pool_bytes(m.make_desc(100, [64], 4, 8))
+    assert e.value.status == "LORA_ERR_SHAPE"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_pool_bytes(m.make_desc(64, [60], 4, 8))
+    assert e.value.status == "LORA_ERR_SHAPE"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_pool_bytes(m.make_desc(64, [64], 4, 300))
+    assert e.value.status == "LORA_ERR_RANK"
+    d = m.make_desc(64, [64], 4, 8)
+    d.x_dtype = 3
+    with pytest.raises(m.LoraError) as e:
+        m.lora_pool_bytes(d)
+    assert e.value.status == "LORA_ERR_DTYPE"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_routing_bytes(0)
+    assert e.value.status == "LORA_ERR_SHAPE"
+    # pool creation with too little memory fails before touching the device
+    with pytest.raises(m.LoraError) as e:
+        m.lora_pool_create(m.make_desc(64, [64], 4, 8), 256, 16, stream=0)
+    assert e.value.status == "LORA_ERR_CAPACITY"
+    assert "needed" in m.lora_last_error()
+
+
+def test_pool_bytes_layout(m):
+    # A + B^T + B + two metadata tables, each 256-byte aligned
+    d = m.make_desc(4096, [4096, 1024, 1024], 8, 16)
+    a = 8 * 3 * 16 * 4096 * 2
+    b = 8 * 16 * 6144 * 2
+    meta = 9 * 4 * 4
+    rnd = lambda n: -(-n // 256) * 256
+    assert m.lora_pool_bytes(d) == rnd(a) + 2 * rnd(b) + 2 * rnd(meta)
+
+
+def test_plan_admission_matches_golden_and_oracle(m):
+    with open(os.path.join(GOLDEN, "admission_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        ids = c["ids"]
+        resident = {i: k + 1 for k, i in enumerate(sorted(set(ids) - {0}))}
+        p = m.lora_plan_routing(ids, [1] * len(ids), c["max_loras"], 64, resident,
+                                max(len(resident), 1), max(len(ids), 1))
+        assert list(p["admitted"]) == c["admitted"], c["name"]
+        assert p["info"]["n_distinct"] == len(c["distinct"])
+
+
+def _check_plan(p, ids, lens, resident, cap, pmin):
+    adm, _ = oracle.admit(ids, cap)
+    assert list(p["admitted"]) == adm
+    tok = oracle.token_adapters(ids, lens, adm)
+    slots = np.array([resident.get(int(a), 0) for a in tok], dtype=np.int32)
+    assert np.array_equal(p["tok_slot"], slots)
+    seg, rows = p["seg"], p["rows"]
+    info = p["info"]
+    assert info["n_tokens"] == int(np.sum(lens))
+    assert info["n_active"] == int((slots != 0).sum()) == len(rows)
+    # every active row appears exactly once, in a segment of its own slot
+    assert sorted(rows.tolist()) == np.nonzero(slots)[0].tolist()
+    seq_of = np.repeat(np.arange(len(lens)), lens)
+    covered = 0
+    for k, (s, b, n, kind) in enumerate(seg):
+        assert s >= 1 and n >= 1
+        assert b == covered
+        covered += n
+        r = rows[b:b + n]
+        assert np.all(slots[r] == s)
+        L = np.asarray(lens)[seq_of[r]]
+        if kind == 0:
+            assert k < info["n_decode_segments"] and n <= 8
+            assert np.all(L < pmin)
+            assert np.all(np.diff(r) > 0)
+        else:
+            assert k >= info["n_decode_segments"] and n <= 64
+            assert np.all(L >= pmin)
+            assert np.all(np.diff(r) == 1) and len(set(seq_of[r])) == 1
+            start = r[0] - np.concatenate([[0], np.cumsum(lens)])[seq_of[r[0]]]
+            assert start % 64 == 0     # chunking depends only on the sequence
+    assert covered == len(rows)
+    # decode rows of one slot sit in consecutive segments, token order inside
+    dec = seg[:info["n_decode_segments"]]
+    for s in set(dec[:, 0].tolist()):
+        ks = np.nonzero(dec[:, 0] == s)[0]
+        assert np.all(np.diff(ks) == 1)
+        r = np.concatenate([rows[b:b + n] for _, b, n, _ in dec[ks]])
+        assert np.all(np.diff(r) > 0)
+        assert np.all(dec[ks][:-1, 2] == 8)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_random_batches(m, seed):
+    rng = np.random.default_rng(seed)
+    n_ad = int(rng.integers(1, 12))
+    ids_pool = (np.arange(n_ad) * 13 + 5).tolist()
+    resident = {i: int(s) for i, s in zip(ids_pool, rng.permutation(40)[:n_ad] + 1)}
+    n_seq = int(rng.integers(0, 60))
+    ids = [0 if rng.random() < 0.3 else int(rng.choice(ids_pool)) for _ in range(n_seq)]
+    lens = rng.choice([0, 1, 1, 1, 2, 5, 63, 64, 65, 130], size=n_seq).tolist()
+    cap = int(rng.integers(0, n_ad + 1))
+    pmin = int(rng.choice([1, 16, 64, 2**31 - 1]))
+    T = max(int(np.sum(lens)), 1)
+    p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T)
+    _check_plan(p, ids, lens, resident, cap, pmin)
+
+
+def test_plan_errors(m):
+    with pytest.raises(m.LoraError) as e:
+        m.lora_plan_routing([5, 6], [1, 1], 0, 64, {5: 1}, 4, 4)
+    assert e.value.status == "LORA_ERR_UNKNOWN_ADAPTER"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_plan_routing([5], [9], 0, 64, {5: 1}, 4, 4)
+    assert e.value.status == "LORA_ERR_CAPACITY"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_plan_routing([5], [-1], 0, 64, {5: 1}, 4, 4)
+    assert e.value.status == "LORA_ERR_SHAPE"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_plan_routing([5], [1], 0, 64, {5: 9}, 4, 4)
+    assert e.value.status == "LORA_ERR_SLOT"
+    # an unknown id that the cap defers is never looked up
+    p = m.lora_plan_routing([5, 6], [1, 1], 1, 64, {5: 1}, 4, 4)
+    assert list(p["admitted"]) == [True, False]

@@ -1,0 +1,275 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Real-valued inputs are held to the tolerance rule in tests/harness.py;
+integer-mode inputs (every partial sum exact in binary32) must match exactly;
+rows the routing leaves alone must keep the exact bits of y0.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import (LaneSpec, WorkloadSpec, config_by_name, generate)
+
+from harness import compare, load_lane_pool, seq_starts, to_device_x, to_device_y
+
+pytestmark = pytest.mark.gpu
+
+MID = WorkloadSpec(
+    name="mid_ragged", seed=21,
+    lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
+           LaneSpec("fp16_share", 1544, (264,), "fp16", tp_size=2, tp_rank=1)),
+    n_adapters=5, ranks=(3, 12, 17, 1, 100), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=100,
+    decode_rows=90, base_prob=0.2, prefill_seqs=6, prefill_len=(1, 200))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import adapter_deltas_amd as m
+    return m
+
+
+def run_lane(m, w, lane_name, *, max_loras=None, prefill_min_len=64, path="apply",
+             pool=None, x=None, y0=None, seq_ids=None, seq_lens=None):
+    import torch
+    lane = w.lanes[lane_name]
+    if pool is None:
+        pool = load_lane_pool(m.Pool, w, lane_name)
+    ids = w.seq_adapter if seq_ids is None else seq_ids
+    lens = w.seq_len if seq_lens is None else seq_lens
+    T = int(np.sum(lens))
+    cap = w.spec.max_loras if max_loras is None else max_loras
+    routing = m.Routing(max(T, 1), max(len(ids), 1))
+    adm, nd = routing.build(pool, ids, lens, cap, prefill_min_len)
+    xd = to_device_x(lane.x if x is None else x)
+    yd = to_device_y(lane.y0 if y0 is None else y0)
+    if path == "apply":
+        m.delta_apply(pool, routing, xd, yd)
+    else:
+        info = routing.info()
+        v = torch.zeros(max(info["n_active"], 1) * pool.v_stride, dtype=torch.float32,
+                        device="cuda")
+        m.shrink(pool, routing, xd, v)
+        m.expand(pool, routing, v, yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy(), adm, routing.info()
+
+
+def inactive_rows(w, admitted, seq_ids=None, seq_lens=None):
+    ids = w.seq_adapter if seq_ids is None else seq_ids
+    lens = w.seq_len if seq_lens is None else seq_lens
+    mask = np.zeros(int(np.sum(lens)), dtype=bool)
+    for s0, n, aid, ok in zip(seq_starts(lens), lens, ids, admitted):
+        if aid == 0 or not ok:
+            mask[s0:s0 + n] = True
+    return mask
+
+
+def check_full(w, lane_name, y, adm, max_loras=None, prefill_min_len=64):
+    lane = w.lanes[lane_name]
+    d_ref, tok, adm_ref = oracle.workload_lane_delta(w, lane_name, max_loras)
+    assert list(adm) == list(adm_ref)
+    off = tok == 0
+    assert np.array_equal(y[off].view(np.uint32), lane.y0[off].view(np.uint32))
+    act = ~off
+    if w.mode == "int":
+        assert np.array_equal(y[act].astype(np.float64),
+                              lane.y0[act].astype(np.float64) + d_ref[act])
+        return None
+    st = compare(y, lane.y0, d_ref[act], lane.spec.h_out, rows=np.nonzero(act)[0])
+    assert st["ok"], st
+    return st
+
+
+# ------------------------------------------------------------- full parity
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("cfg,lane", [("tiny", "proj"), ("decode_mix", "qkv")])
+def test_small_configs_full_parity(lib, cfg, lane, mode):
+    w = generate(config_by_name(cfg), mode=mode)
+    y, adm, info = run_lane(lib, w, lane)
+    check_full(w, lane, y, adm)
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
+@pytest.mark.parametrize("prefill_min_len", [64, 1, 2**31 - 1])
+def test_ragged_full_parity(lib, lane, mode, prefill_min_len):
+    """h_in = 3 sub-chunks + 8, slices 520|136|8, ranks 1..100, sequences of
+    length 1..200 around the 64-row segment edges, both paths forced."""
+    w = generate(MID, mode=mode)
+    y, adm, info = run_lane(lib, w, lane, prefill_min_len=prefill_min_len)
+    if prefill_min_len == 1:
+        assert info["n_decode_segments"] == 0 and info["n_prefill_segments"] > 0
+    if prefill_min_len == 2**31 - 1:
+        assert info["n_prefill_segments"] == 0
+    check_full(w, lane, y, adm, prefill_min_len=prefill_min_len)
+
+
+def test_y0_zero_and_split_path_parity(lib):
+    w = generate(config_by_name("decode_mix"), y0="zeros")
+    y, adm, _ = run_lane(lib, w, "qkv", path="split")
+    check_full(w, "qkv", y, adm)
+
+
+# ------------------------------------------- full-size configs, sampled rows
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("cfg,lane", [("prefill", "o_proj"), ("prefill", "gate_up"),
+                                      ("many_tenants", "down_proj"),
+                                      ("many_tenants", "o_proj"),
+                                      ("tp_share", "attn_out"), ("tp_share", "shexp_w2")])
+def test_full_size_sampled(lib, cfg, lane, mode):
+    w = generate(config_by_name(cfg), mode=mode, lanes=(lane,))
+    y, adm, info = run_lane(lib, w, lane)
+    L = w.lanes[lane]
+    _, tok, adm_ref = oracle.workload_lane_delta(w, lane, rows=np.zeros(0, np.int64))
+    assert list(adm) == list(adm_ref)
+    off = tok == 0
+    assert np.array_equal(y[off].view(np.uint32), L.y0[off].view(np.uint32))
+    act = np.nonzero(~off)[0]
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([act[:3], act[-3:], rng.choice(act, 40, replace=False)]))
+    d_ref, _, _ = oracle.workload_lane_delta(w, lane, rows=rows)
+    if mode == "int":
+        assert np.array_equal(y[rows].astype(np.float64), L.y0[rows].astype(np.float64) + d_ref)
+    else:
+        st = compare(y, L.y0, d_ref, L.spec.h_out, rows=rows)
+        assert st["ok"], st
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_base_rows_not_read_or_written(lib):
+    """NaN in x and y of base rows: base rows keep their NaN payload bits and
+    nothing leaks into adapter rows."""
+    w = generate(config_by_name("decode_mix"))
+    L = w.lanes["qkv"]
+    y_ref, adm, _ = run_lane(lib, w, "qkv")
+    tok = oracle.token_adapters(w.seq_adapter, w.seq_len, adm)
+    x = L.x.copy()
+    y0 = L.y0.copy()
+    x[tok == 0] = 0x7FC1                                    # bf16 quiet NaN
+    y0.view(np.uint32)[tok == 0] = 0x7FC01234               # NaN with payload
+    y, _, _ = run_lane(lib, w, "qkv", x=x, y0=y0)
+    assert np.array_equal(y.view(np.uint32)[tok == 0], y0.view(np.uint32)[tok == 0])
+    assert np.array_equal(y.view(np.uint32)[tok != 0], y_ref.view(np.uint32)[tok != 0])
+
+
+@pytest.mark.parametrize("cfg,lane", [("decode_mix", "qkv"), ("mid", "qkv_like"),
+                                      ("mid", "fp16_share")])
+def test_permutation_and_solo_bit_exact(lib, cfg, lane):
+    w = generate(MID) if cfg == "mid" else generate(config_by_name(cfg))
+    L = w.lanes[lane]
+    pool = load_lane_pool(lib.Pool, w, lane)
+    y, adm, _ = run_lane(lib, w, lane, pool=pool)
+    # sequences in a shuffled order, rows moved with them
+    perm = np.random.default_rng(1).permutation(len(w.seq_len))
+    starts = seq_starts(w.seq_len)
+    rows = np.concatenate([np.arange(starts[i], starts[i] + w.seq_len[i]) for i in perm])
+    yp, _, _ = run_lane(lib, w, lane, pool=pool, x=L.x[rows], y0=L.y0[rows],
+                        seq_ids=w.seq_adapter[perm], seq_lens=w.seq_len[perm])
+    assert np.array_equal(yp.view(np.uint32), y[rows].view(np.uint32))
+    # a few sequences alone
+    for i in np.random.default_rng(2).choice(len(w.seq_len), 6, replace=False):
+        r = np.arange(starts[i], starts[i] + w.seq_len[i])
+        ys, _, _ = run_lane(lib, w, lane, pool=pool, x=L.x[r], y0=L.y0[r],
+                            seq_ids=w.seq_adapter[i:i + 1], seq_lens=w.seq_len[i:i + 1])
+        assert np.array_equal(ys.view(np.uint32), y[r].view(np.uint32)), i
+
+
+def test_run_to_run_relocation_and_split_bit_exact(lib):
+    w = generate(MID)
+    lane = "qkv_like"
+    y1, _, _ = run_lane(lib, w, lane)
+    y2, _, _ = run_lane(lib, w, lane)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    # other slots, more slots, larger max_rank, device-side packing
+    ids = w.adapter_ids
+    slot_of = {aid: 9 - i for i, aid in enumerate(ids)}
+    pool = load_lane_pool(lib.Pool, w, lane, max_slots=9, max_rank=160, slot_of=slot_of,
+                          on_device=True)
+    y3, _, _ = run_lane(lib, w, lane, pool=pool)
+    assert np.array_equal(y1.view(np.uint32), y3.view(np.uint32))
+    y4, _, _ = run_lane(lib, w, lane, path="split")
+    assert np.array_equal(y1.view(np.uint32), y4.view(np.uint32))
+
+
+def test_scale_zero_gives_y0(lib):
+    w = generate(MID)
+    lane = "qkv_like"
+    for ad in w.adapters.values():
+        for s in ad.lanes[lane]:
+            s.scale = 0.0
+    y, adm, _ = run_lane(lib, w, lane)
+    assert np.array_equal(y, w.lanes[lane].y0)   # numeric ==, -0.0 == +0.0
+
+
+# ------------------------------------------------------ admission and errors
+
+def test_max_loras_deferral(lib):
+    w = generate(config_by_name("decode_mix"))
+    y, adm, info = run_lane(lib, w, "qkv", max_loras=3)
+    assert info["n_distinct"] == 3 and not all(adm)
+    check_full(w, "qkv", y, adm, max_loras=3)
+
+
+def test_empty_and_all_base_batches_touch_nothing(lib):
+    import torch
+    w = generate(config_by_name("tiny"))
+    L = w.lanes["proj"]
+    pool = load_lane_pool(lib.Pool, w, "proj")
+    for ids, lens in [([], []), ([0, 0, 0], [1, 5, 2]), ([1037, 0], [0, 3])]:
+        T = int(sum(lens))
+        routing = lib.Routing(max(T, 1), 4)
+        routing.build(pool, ids, lens, 0, 64)
+        assert routing.info()["n_active"] == 0
+        yd = torch.full((max(T, 1), 64), 3.5, device="cuda")
+        xd = torch.zeros((max(T, 1), 64), dtype=torch.int16, device="cuda")
+        lib.delta_apply(pool, routing, xd, yd)
+        torch.cuda.synchronize()
+        assert bool((yd == 3.5).all())
+
+
+def test_unknown_adapter_is_an_error(lib):
+    w = generate(config_by_name("tiny"))
+    pool = load_lane_pool(lib.Pool, w, "proj")
+    routing = lib.Routing(8, 8)
+    with pytest.raises(lib.LoraError) as e:
+        routing.build(pool, [1037, 999], [1, 1], 0, 64)
+    assert e.value.status == "LORA_ERR_UNKNOWN_ADAPTER"
+    # a deferred unknown id is not an error: it is never admitted
+    adm, _ = routing.build(pool, [1037, 999], [1, 1], 1, 64)
+    assert list(adm) == [True, False]
+
+
+def test_load_errors(lib):
+    w = generate(config_by_name("tiny"))
+    pool = load_lane_pool(lib.Pool, w, "proj")
+    ad = next(iter(w.adapters.values()))
+    s = ad.lanes["proj"][0]
+    cases = [
+        (dict(adapter_id=0), "LORA_ERR_ARG"),
+        (dict(slot=0), "LORA_ERR_SLOT"),
+        (dict(slot=3), "LORA_ERR_SLOT"),
+        (dict(ranks=[5]), "LORA_ERR_RANK"),
+        (dict(scales=[float("nan")]), "LORA_ERR_ARG"),
+        (dict(a_col0=8), "LORA_ERR_SHAPE"),
+    ]
+    for kw, status in cases:
+        args = dict(adapter_id=77, A=[s.A], B=[s.B], ranks=[s.rank], scales=[s.scale],
+                    a_col0=0, slot=-1)
+        args.update(kw)
+        if "ranks" in kw:
+            args["A"] = [np.zeros((5, 64), np.uint16)]
+            args["B"] = [np.zeros((64, 5), np.uint16)]
+        with pytest.raises(lib.LoraError) as e:
+            pool.load(**args)
+        assert e.value.status == status, kw
+    # both slots are taken: a third id has no free slot
+    with pytest.raises(lib.LoraError) as e:
+        pool.load(77, [s.A], [s.B], [s.rank], [s.scale])
+    assert e.value.status == "LORA_ERR_CAPACITY"
