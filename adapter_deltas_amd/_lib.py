@@ -18,6 +18,7 @@ DTYPE = {"bf16": 1, "fp16": 2, "fp32": 3}
 MAX_SLICES = 4
 MAX_RANK = 256
 DECODE_SEG_ROWS = 8
+SEG_WORDS = 16
 PREFILL_SEG_ROWS = 64
 
 # every symbol include/lora.h declares
@@ -83,7 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lora_build_routing": (I32, [P, I32, PI32, PI32, I32, I32, P,
                                      ctypes.POINTER(ctypes.c_uint8), PI32, P]),
         "lora_routing_get_info": (I32, [P, ctypes.POINTER(RoutingInfo)]),
-        "lora_plan_routing": (I32, [I32, PI32, PI32, I32, I32, I32, PI32, PI32, I32, I32,
+        "lora_plan_routing": (I32, [I32, PI32, PI32, I32, I32, I32, PI32, PI32, PI32, I32, I32,
                                     PI32, I64, PI32, ctypes.POINTER(RoutingInfo),
                                     ctypes.POINTER(ctypes.c_uint8)]),
         "lora_routing_token_slots": (I32, [P, PP]),

@@ -6,174 +6,59 @@
 // per segment.  Both keep a per-row summation order fixed by the lane's
 // widths and the adapter's rank (TensorFold PR #47, third commit message:
 // fp32 sums in a fixed order, so a row's bits depend only on its own input and
-// its own adapter).
-//
-// Shrink order for u[k] = sum_i A[k][i] x[i] over h_in:
-//   h_in is cut into sub-chunks of kSubChunk = 512 elements; sub-chunk q
-//   belongs to part q % kParts.  Within a part, lane l of a wave accumulates
-//   elements [512 q + 8 l, 512 q + 8 l + 8) of its sub-chunks, q ascending,
-//   four bf16 pair-dot steps per sub-chunk (pairs 0-1, 2-3, 4-5, 6-7), into one
-//   fp32 sum.  The 64 lane sums are combined by a fixed reduce-scatter
-//   butterfly (lane masks 32, 16, 8, 4, 2, 1), and the part sums as
-//   (p0 + p1) + (p2 + p3).  v = fp32(scale * u).
-//   An fp16 input is split exactly into two bf16 values x = hi + lo (fp16
-//   carries 11 significant bits) and each pair-dot step is done for hi, then lo.
-// Expand order: d[o] = fma chain over k = 0 .. rank-1 starting from 0, then
-//   y[o] = y[o] + d[o].
-#include "lora_internal.h"
+// its own adapter); the order is spelled out in kernels_decode.h.
+#include "kernels_decode.h"
 
 namespace lora {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
-}
-
-// Exact split of two packed fp16 values into packed bf16 hi and lo words.
-__device__ __forceinline__ void split_f16x2(uint32_t w, uint32_t &hi, uint32_t &lo)
-{
-    const float f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-    const float f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-    const uint32_t u0 = __float_as_uint(f0), u1 = __float_as_uint(f1);
-    const uint32_t t0 = u0 & 0xffff0000u, t1 = u1 & 0xffff0000u;
-    const float l0 = f0 - __uint_as_float(t0);
-    const float l1 = f1 - __uint_as_float(t1);
-    hi = (u0 >> 16) | t1;
-    lo = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xffff0000u);
-}
-
-__device__ __forceinline__ uint4 ld16(const uint16_t *p)
-{
-    return *reinterpret_cast<const uint4 *>(p);
-}
-
-// In lane L: the sum over the wave's 64 lanes of val[L].  Fixed butterfly.
-__device__ __forceinline__ float wave_reduce_scatter64(float (&val)[64], int lane)
-{
-#pragma unroll
-    for (int s = 0; s < 6; ++s) {
-        const int m = 32 >> s;
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < m; ++i) {
-            const float send = upper ? val[i] : val[m + i];
-            const float keep = upper ? val[m + i] : val[i];
-            val[i] = keep + __shfl_xor(send, m, 64);
-        }
-    }
-    return val[0];
-}
-
 template <bool FP16X>
-__global__ __launch_bounds__(256) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                      int kb_per_slice,
-                                                      const uint16_t *__restrict__ x,
-                                                      int64_t ldx, float *__restrict__ v)
+__global__ __launch_bounds__(64 * kParts) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
+                                                              int kb_per_slice,
+                                                              const uint16_t *__restrict__ x,
+                                                              int64_t ldx, float *__restrict__ v)
 {
-    constexpr int C = kDecodeSegRows;
     const int per_seg = g.n_slices * kb_per_slice;
     const int task = blockIdx.x;
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / kb_per_slice;
     const int kb = rem - j * kb_per_slice;
-    const int4 sd = r.seg[si];
-    const int slot = sd.x;
-    const int rank = p.rank[slot * kMetaStride + j];
+    const Seg sd = load_seg(r.seg, si);
+    const int rank = sd.rank(j);
     const int k0 = kb * kKBlock;
     if (k0 >= rank) return;
-    const int n_rows = sd.z;
     const int kn = min(kKBlock, rank - k0);
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 
-    const uint16_t *Ab =
-        p.A + (int64_t)(slot - 1) * g.a_slot_stride + ((int64_t)j * g.rank_pad + k0) * g.h_in;
-    const uint16_t *xr[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) xr[c] = x + (int64_t)r.row_idx[sd.y + min(c, n_rows - 1)] * ldx;
-
-    float acc[C][kKBlock];
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int k = 0; k < kKBlock; ++k) acc[c][k] = 0.f;
-
-    const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
-    for (int q = wave; q < n_sub; q += kParts) {
-        const int e = q * kSubChunk + lane * 8;
-        if (e < g.h_in) {
-            uint32_t xw[C][FP16X ? 8 : 4];
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (c < n_rows) {
-                    const uint4 t = ld16(xr[c] + e);
-                    if constexpr (FP16X) {
-                        split_f16x2(t.x, xw[c][0], xw[c][4]);
-                        split_f16x2(t.y, xw[c][1], xw[c][5]);
-                        split_f16x2(t.z, xw[c][2], xw[c][6]);
-                        split_f16x2(t.w, xw[c][3], xw[c][7]);
-                    } else {
-                        xw[c][0] = t.x;
-                        xw[c][1] = t.y;
-                        xw[c][2] = t.z;
-                        xw[c][3] = t.w;
-                    }
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < kKBlock; ++k) {
-                if (k < kn) {
-                    const uint4 a = ld16(Ab + (int64_t)k * g.h_in + e);
-                    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                    for (int c = 0; c < C; ++c) {
-                        if (c < n_rows) {
-                            float s = acc[c][k];
-#pragma unroll
-                            for (int m = 0; m < 4; ++m) {
-                                s = dot2_bf16(aw[m], xw[c][m], s);
-                                if constexpr (FP16X) s = dot2_bf16(aw[m], xw[c][4 + m], s);
-                            }
-                            acc[c][k] = s;
-                        }
-                    }
-                }
-            }
-        }
-    }
-
-    float val[64];
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int k = 0; k < kKBlock; ++k) val[c * kKBlock + k] = acc[c][k];
-    const float red = wave_reduce_scatter64(val, lane);
-
+    // wave w owns part w
+    const float red = shrink_part<FP16X>(g, p, sd, j, k0, kn, wave, lane, x, ldx);
     __shared__ float part[kParts][64];
     part[wave][lane] = red;
     __syncthreads();
     if (wave == 0) {
-        const float u = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+        const float q0 = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+        const float q1 = (part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]);
         const int c = lane / kKBlock;
         const int k = lane % kKBlock;
-        if (c < n_rows && k < kn) {
-            const float scale = p.scale[slot * kMetaStride + j];
-            v[(int64_t)(sd.y + c) * g.v_stride + j * g.rank_pad + k0 + k] = scale * u;
+        if (c < sd.n_rows() && k < kn) {
+            const float scale = p.scale[sd.slot() * kMetaStride + j];
+            v[(int64_t)(sd.v_row() + c) * g.v_stride + j * g.rank_pad + k0 + k] = scale * (q0 + q1);
         }
     }
 }
 
-__global__ __launch_bounds__(64) void k_expand_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                     int tiles_per_slice,
-                                                     const float *__restrict__ v,
-                                                     float *__restrict__ y, int64_t ldy)
+constexpr int kExpandWaves = kDecodeSegRows / kExpandRows;   // waves per expand task
+
+__global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, PoolDev p,
+                                                                   RoutingDev r,
+                                                                   int tiles_per_slice,
+                                                                   const float *__restrict__ v,
+                                                                   float *__restrict__ y,
+                                                                   int64_t ldy)
 {
-    constexpr int C = kDecodeSegRows;
+    constexpr int C = kExpandRows;
     const int per_seg = g.n_slices * tiles_per_slice;
     const int task = blockIdx.x;
     const int si = task / per_seg;
@@ -182,63 +67,38 @@ __global__ __launch_bounds__(64) void k_expand_gemv(LaneGeom g, PoolDev p, Routi
     const int tile = rem - j * tiles_per_slice;
     const int hj = g.h_out[j];
     if (tile * kExpandTile >= hj) return;
-    const int4 sd = r.seg[si];
-    const int slot = sd.x;
-    const int n_rows = sd.z;
-    const int rank = p.rank[slot * kMetaStride + j];
-
-    __shared__ float4 vs[LORA_MAX_RANK][2];   // vs[k] = v of rows 0..7 at rank k
-    float *vsf = reinterpret_cast<float *>(vs);
-    for (int i = threadIdx.x; i < rank * C; i += 64) {
-        const int k = i / C, c = i % C;
-        vsf[i] = c < n_rows ? v[(int64_t)(sd.y + c) * g.v_stride + j * g.rank_pad + k] : 0.f;
-    }
-    __syncthreads();
-
-    const int o0 = tile * kExpandTile + threadIdx.x * 8;
-    if (o0 >= hj) return;
+    const Seg sd = load_seg(r.seg, si);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int c0 = wave * C;                    // first segment row of this wave
+    const int n_rows = sd.n_rows() - c0;        // rows of this wave (may be <= 0)
+    if (n_rows <= 0) return;
+    const int rank = sd.rank(j);
+    const int o0 = tile * kExpandTile + lane * 8;
+    const bool col_ok = o0 < hj;
+    const int oc = col_ok ? o0 : hj - 8;
+    static_assert(kExpandRows == 4 && kExpandWaves == 2, "row selection below");
+    const int trow[C] = {wave ? sd.row<4>() : sd.row<0>(), wave ? sd.row<5>() : sd.row<1>(),
+                         wave ? sd.row<6>() : sd.row<2>(), wave ? sd.row<7>() : sd.row<3>()};
+    float *const yp[C] = {y + (int64_t)trow[0] * ldy + g.col_off[j] + oc,
+                          y + (int64_t)trow[1] * ldy + g.col_off[j] + oc,
+                          y + (int64_t)trow[2] * ldy + g.col_off[j] + oc,
+                          y + (int64_t)trow[3] * ldy + g.col_off[j] + oc};
     const uint16_t *bt =
-        p.Bt + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j] + o0;
-    float acc[C][8];
+        p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j] + oc;
+    // v is read-only here and the same for every lane: constant-space reads
+    // become scalar loads.
+    typedef const __attribute__((address_space(4))) float cfloat;
+    const int64_t vrow0 = (int64_t)(sd.v_row() + c0) * g.v_stride + j * g.rank_pad;
+    auto vsrc = [&](int c, int kb, float (&out)[8]) {
+        cfloat *vr = (cfloat *)(v + vrow0 + (int64_t)min(c, n_rows - 1) * g.v_stride);
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-
-    for (int k = 0; k < rank; ++k) {
-        const uint4 b = ld16(bt + (int64_t)k * hj);
-        const float bf[8] = {__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
-                             __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u),
-                             __uint_as_float(b.z << 16), __uint_as_float(b.z & 0xffff0000u),
-                             __uint_as_float(b.w << 16), __uint_as_float(b.w & 0xffff0000u)};
-        const float4 va = vs[k][0], vb = vs[k][1];
-        const float vc[C] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            if (c < n_rows) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[c][e] = __builtin_fmaf(bf[e], vc[c], acc[c][e]);
-            }
+        for (int k = 0; k < 8; ++k) {
+            const float t = vr[kb + k];
+            out[k] = kb + k < rank ? t : 0.f;
         }
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        if (c < n_rows) {
-            const int t = r.row_idx[sd.y + c];
-            float4 *yp = reinterpret_cast<float4 *>(y + (int64_t)t * ldy + g.col_off[j] + o0);
-            float4 a = yp[0], b = yp[1];
-            a.x += acc[c][0];
-            a.y += acc[c][1];
-            a.z += acc[c][2];
-            a.w += acc[c][3];
-            b.x += acc[c][4];
-            b.y += acc[c][5];
-            b.z += acc[c][6];
-            b.w += acc[c][7];
-            yp[0] = a;
-            yp[1] = b;
-        }
-    }
+    };
+    expand_rows(yp, n_rows, bt, hj, rank, col_ok, [] {}, vsrc);
 }
 
 // ---- pool maintenance ----
@@ -300,11 +160,11 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
     if (g.x_fp16)
-        hipLaunchKernelGGL(k_shrink_gemv<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, p, r,
-                           kb_per_slice, xp, ldx, v);
+        hipLaunchKernelGGL(k_shrink_gemv<true>, dim3((unsigned)blocks), dim3(64 * kParts), 0, s,
+                           g, p, r, kb_per_slice, xp, ldx, v);
     else
-        hipLaunchKernelGGL(k_shrink_gemv<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, p, r,
-                           kb_per_slice, xp, ldx, v);
+        hipLaunchKernelGGL(k_shrink_gemv<false>, dim3((unsigned)blocks), dim3(64 * kParts), 0, s,
+                           g, p, r, kb_per_slice, xp, ldx, v);
     return hipGetLastError();
 }
 
@@ -315,8 +175,8 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_expand_gemv, dim3((unsigned)blocks), dim3(64), 0, s, g, p, r,
-                       tiles_per_slice, v, y, ldy);
+    hipLaunchKernelGGL(k_expand_gemv, dim3((unsigned)blocks), dim3(64 * kExpandWaves), 0, s, g,
+                       p, r, tiles_per_slice, v, y, ldy);
     return hipGetLastError();
 }
 

@@ -19,18 +19,13 @@
 // Every output element depends only on its own row of x (or v) and the
 // adapter's factors, and a sequence is cut into segments by its own length
 // only, so a row's bits do not depend on the rest of the batch.
-#include "lora_internal.h"
+#include "kernels_common.h"
 
 namespace lora {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ld16(const uint16_t *p)
-{
-    return *reinterpret_cast<const uint4 *>(p);
-}
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c)
 {
@@ -87,19 +82,19 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LaneGeom g, PoolDev p, Rout
     const int task = blockIdx.x;
     const int si = seg_begin + task / g.n_slices;
     const int j = task % g.n_slices;
-    const int4 sd = r.seg[si];
-    const int slot = sd.x;
-    const int n_rows = sd.z;
-    const int rank = p.rank[slot * kMetaStride + j];
+    const Seg sd = load_seg(r.seg, si);
+    const int slot = sd.slot();
+    const int n_rows = sd.n_rows();
+    const int rank = sd.rank(j);
     const int ntiles = (rank + 15) / 16;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r0 = wave * 16;
     if (r0 >= n_rows || ntiles > NT) return;
     const int li = lane & 15, lg = lane >> 4;
     const int row = r0 + li;
     const bool row_ok = row < n_rows;
-    const uint16_t *xrow = x + (int64_t)r.row_idx[sd.y + (row_ok ? row : r0)] * ldx;
+    const uint16_t *xrow = x + (int64_t)(sd.first_row() + (row_ok ? row : r0)) * ldx;
     const uint16_t *Ab = p.A + (int64_t)(slot - 1) * g.a_slot_stride +
                          (int64_t)j * g.rank_pad * g.h_in + (int64_t)li * g.h_in;
     const int64_t tile_stride = (int64_t)16 * g.h_in;
@@ -128,7 +123,7 @@ __global__ __launch_bounds__(256) void k_shrink_mfma(LaneGeom g, PoolDev p, Rout
 
     if (row_ok) {
         const float scale = p.scale[slot * kMetaStride + j];
-        float *vr = v + (int64_t)(sd.y + row) * g.v_stride + j * g.rank_pad + 4 * lg;
+        float *vr = v + (int64_t)(sd.v_row() + row) * g.v_stride + j * g.rank_pad + 4 * lg;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt < ntiles) {
@@ -158,18 +153,19 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, Rout
     const int hj = g.h_out[j];
     const int o_base = tile * (NS * 16);
     if (o_base >= hj) return;
-    const int4 sd = r.seg[si];
-    const int slot = sd.x;
-    const int n_rows = sd.z;
-    const int rank = p.rank[slot * kMetaStride + j];
-    const int wave = threadIdx.x >> 6;
+    const Seg sd = load_seg(r.seg, si);
+    const int slot = sd.slot();
+    const int n_rows = sd.n_rows();
+    const int rank = sd.rank(j);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r0 = wave * 16;
     if (r0 >= n_rows) return;
     const int li = lane & 15, lg = lane >> 4;
     const int row = r0 + li;
     const bool row_ok = row < n_rows;
-    const float *vrow = v + (int64_t)(sd.y + (row_ok ? row : r0)) * g.v_stride + j * g.rank_pad;
+    const float *vrow =
+        v + (int64_t)(sd.v_row() + (row_ok ? row : r0)) * g.v_stride + j * g.rank_pad;
     const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j];
 
     f32x4_t acc[NS];
@@ -202,7 +198,7 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, Rout
     }
 
     if (row_ok) {
-        const int t = r.row_idx[sd.y + row];
+        const int t = sd.first_row() + row;
         float *yrow = y + (int64_t)t * ldy + g.col_off[j];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {

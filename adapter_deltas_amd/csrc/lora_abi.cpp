@@ -125,8 +125,7 @@ PoolDev pool_dev(const lora_pool *p)
 
 RoutingDev routing_dev(const lora_routing *r)
 {
-    return RoutingDev{reinterpret_cast<const int4 *>(r->dev + r->off_seg), r->dev + r->off_row,
-                      r->dev + r->off_tok};
+    return RoutingDev{r->dev + r->off_seg, r->dev + r->off_tok};
 }
 
 // Largest rank over the routing's distinct slots and the lane's slices.
@@ -145,10 +144,19 @@ int32_t check_pair(const lora_pool *p, const lora_routing *r)
     if (r->pool_max_slots > p->desc.max_slots)
         return fail(LORA_ERR_MISMATCH, "routing resolved slots up to %d, pool has %d",
                     r->pool_max_slots, p->desc.max_slots);
-    for (int32_t s : r->distinct_slots)
+    for (size_t i = 0; i < r->distinct_slots.size(); ++i) {
+        const int32_t s = r->distinct_slots[i];
         if (s < 1 || s > p->desc.max_slots || p->slot_to_id[s] == 0)
             return fail(LORA_ERR_MISMATCH, "routing uses slot %d, which this pool does not hold",
                         s);
+        for (int j = 0; j < p->desc.n_slices; ++j)
+            if (r->slot_ranks[i * kMetaStride + j] != p->h_rank[(size_t)s * kMetaStride + j])
+                return fail(LORA_ERR_MISMATCH,
+                            "slot %d slice %d has rank %d in this pool but %d in the pool the "
+                            "routing was built against",
+                            s, j, p->h_rank[(size_t)s * kMetaStride + j],
+                            r->slot_ranks[i * kMetaStride + j]);
+    }
     return LORA_OK;
 }
 
@@ -222,12 +230,24 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     return LORA_OK;
 }
 
+template <class Ranks>
+void push_seg(std::vector<int32_t> &seg, int32_t slot, int32_t v_row, int32_t n, int32_t kind,
+              Ranks ranks)
+{
+    seg.push_back(slot);
+    seg.push_back(v_row);
+    seg.push_back(n);
+    seg.push_back(kind);
+    for (int j = 0; j < kMetaStride; ++j) seg.push_back(ranks(slot, j));
+}
+
 // Admission, per-token slots and segments of one candidate batch, on the host.
-// `resolve(id)` gives the slot of a resident id, or 0.
-template <class Resolve>
+// `resolve(id)` gives the slot of a resident id, or 0; `ranks(slot, j)` the
+// rank of slice j held in that slot.
+template <class Resolve, class Ranks>
 int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
                      int32_t max_loras, int32_t prefill_min_len, int32_t max_tokens,
-                     int32_t max_slots, Resolve resolve, Plan &pl)
+                     int32_t max_slots, Resolve resolve, Ranks ranks, Plan &pl)
 {
     if (n_seq < 0) return fail(LORA_ERR_SHAPE, "n_seq < 0");
     if (n_seq > 0 && (!seq_adapter_id || !seq_len))
@@ -315,13 +335,13 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
         }
         for (int32_t s : slot_order)
             for (int32_t b = 0; b < count[s]; b += kDecodeSegRows) {
-                pl.seg.push_back(s);
-                pl.seg.push_back(start[s] + b);
-                pl.seg.push_back(std::min(kDecodeSegRows, count[s] - b));
-                pl.seg.push_back(kSegDecode);
+                const int32_t n = std::min(kDecodeSegRows, count[s] - b);
+                push_seg(pl.seg, s, start[s] + b, n, kSegDecode, ranks);
+                for (int32_t c = 0; c < kDecodeSegRows; ++c)
+                    pl.seg.push_back(pl.rows[(size_t)(start[s] + b + std::min(c, n - 1))]);
             }
     }
-    const int32_t n_dec_seg = (int32_t)(pl.seg.size() / 4);
+    const int32_t n_dec_seg = (int32_t)(pl.seg.size() / kSegWords);
     // prefill sequences: contiguous chunks of kPrefillSegRows rows, one slot each
     {
         int64_t pos = n_dec;
@@ -331,16 +351,15 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
             if (s != 0 && L >= prefill_min_len)
                 for (int32_t b = 0; b < L; b += kPrefillSegRows) {
                     const int32_t n = std::min(kPrefillSegRows, L - b);
-                    pl.seg.push_back(s);
-                    pl.seg.push_back((int32_t)pos);
-                    pl.seg.push_back(n);
-                    pl.seg.push_back(kSegPrefill);
+                    push_seg(pl.seg, s, (int32_t)pos, n, kSegPrefill, ranks);
+                    pl.seg.push_back((int32_t)(row0 + b));
+                    for (int32_t c = 1; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
                     for (int32_t t = 0; t < n; ++t) pl.rows[(size_t)pos++] = (int32_t)(row0 + b + t);
                 }
             row0 += L;
         }
     }
-    const int32_t n_seg = (int32_t)(pl.seg.size() / 4);
+    const int32_t n_seg = (int32_t)(pl.seg.size() / kSegWords);
     pl.info.n_tokens = (int32_t)T;
     pl.info.n_active = (int32_t)(n_dec + n_pre);
     pl.info.n_segments = n_seg;
@@ -352,7 +371,12 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     for (int i = 0; i < n_seq; ++i) na += adm[i];
     pl.info.n_admitted_seqs = na;
     pl.distinct_slots.clear();
-    for (int32_t id : distinct_ids) pl.distinct_slots.push_back(id_slot[id]);
+    pl.slot_ranks.clear();
+    for (int32_t id : distinct_ids) {
+        const int32_t s = id_slot[id];
+        pl.distinct_slots.push_back(s);
+        for (int j = 0; j < kMetaStride; ++j) pl.slot_ranks.push_back(ranks(s, j));
+    }
     return LORA_OK;
 }
 
@@ -552,8 +576,8 @@ int32_t lora_routing_bytes(int32_t max_tokens, int64_t *bytes_out)
     if (max_tokens < 1 || max_tokens > (1 << 26))
         return fail(LORA_ERR_SHAPE, "max_tokens=%d outside 1..2^26", max_tokens);
     if (!bytes_out) return fail(LORA_ERR_ARG, "bytes_out is null");
-    // segments (4 words each, at most one per active row) + row list + token slots
-    *bytes_out = round_up((int64_t)max_tokens * 6 * 4 + 64, 256);
+    // segments (kSegWords each, at most one per active row) + row list + token slots
+    *bytes_out = round_up((int64_t)max_tokens * (kSegWords + 2) * 4 + 64, 256);
     return LORA_OK;
 }
 
@@ -622,8 +646,11 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
         auto it = p->id_to_slot.find(id);
         return it == p->id_to_slot.end() ? 0 : it->second;
     };
+    auto ranks = [p](int32_t slot, int j) -> int32_t {
+        return p->h_rank[(size_t)slot * kMetaStride + j];
+    };
     if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
-                                  r->max_tokens, p->desc.max_slots, resolve, pl))
+                                  r->max_tokens, p->desc.max_slots, resolve, ranks, pl))
         return rc;
 
     const int64_t words = pl.words();
@@ -647,6 +674,7 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
     r->info = pl.info;
     r->pool_max_slots = p->desc.max_slots;
     r->distinct_slots = pl.distinct_slots;
+    r->slot_ranks = pl.slot_ranks;
     if (admitted_out)
         for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
     if (n_distinct_out) *n_distinct_out = pl.info.n_distinct;
@@ -656,7 +684,8 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
 int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
                           int32_t max_loras, int32_t prefill_min_len, int32_t n_resident,
                           const int32_t *resident_id, const int32_t *resident_slot,
-                          int32_t max_slots, int32_t max_tokens, int32_t *words_out,
+                          const int32_t *resident_rank, int32_t max_slots, int32_t max_tokens,
+                          int32_t *words_out,
                           int64_t words_capacity, int32_t *offsets_out,
                           lora_routing_info *info_out, uint8_t *admitted_out)
 {
@@ -666,19 +695,27 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
         return fail(LORA_ERR_SHAPE, "max_slots=%d outside 1..65535", max_slots);
     if (max_tokens < 1) return fail(LORA_ERR_SHAPE, "max_tokens < 1");
     std::unordered_map<int32_t, int32_t> table;
+    std::vector<int32_t> rank_of((size_t)(max_slots + 1) * kMetaStride, 0);
     for (int i = 0; i < n_resident; ++i) {
         if (resident_id[i] <= 0 || resident_slot[i] < 1 || resident_slot[i] > max_slots)
             return fail(LORA_ERR_SLOT, "resident entry %d: id %d slot %d", i, resident_id[i],
                         resident_slot[i]);
         table[resident_id[i]] = resident_slot[i];
+        if (resident_rank)
+            for (int j = 0; j < kMetaStride; ++j)
+                rank_of[(size_t)resident_slot[i] * kMetaStride + j] =
+                    resident_rank[i * kMetaStride + j];
     }
     auto resolve = [&table](int32_t id) -> int32_t {
         auto it = table.find(id);
         return it == table.end() ? 0 : it->second;
     };
+    auto ranks = [&rank_of](int32_t slot, int j) -> int32_t {
+        return rank_of[(size_t)slot * kMetaStride + j];
+    };
     Plan pl;
     if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
-                                  max_tokens, max_slots, resolve, pl))
+                                  max_tokens, max_slots, resolve, ranks, pl))
         return rc;
     if (!words_out || !offsets_out || !info_out)
         return fail(LORA_ERR_ARG, "null output");

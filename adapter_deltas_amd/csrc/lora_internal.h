@@ -17,12 +17,21 @@ constexpr int kPrefillSegRows = LORA_PREFILL_SEG_ROWS;  // rows per prefill segm
 constexpr int kRankAlign = 16;                          // rank padding of the pool
 constexpr int kKBlock = 8;                              // ranks per decode shrink task
 constexpr int kSubChunk = 512;                          // h_in elements per wave pass
-constexpr int kParts = 4;                               // interleaved h_in parts
+constexpr int kParts = 8;                               // interleaved h_in parts (one wave each)
 constexpr int kExpandTile = 512;                        // columns per decode expand task
 constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
 enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1 };
+
+// A segment descriptor is kSegWords int32 words:
+//   [0] slot  [1] first active row (row of v)  [2] rows  [3] kind
+//   [4..7]  rank of slices 0..3 in the pool the routing was built against
+//   [8..15] decode: token row of each segment row (the last one repeated
+//           past the segment's rows); prefill: [8] = first token row, the
+//           segment's rows being consecutive.
+constexpr int kSegWords = 16;
+static_assert(kDecodeSegRows == 8, "descriptor holds 8 token rows");
 
 // Geometry of a lane's pool, passed by value to kernels.
 struct LaneGeom {
@@ -49,10 +58,9 @@ struct PoolDev {
     const float *scale;    // [max_slots + 1][kMetaStride]
 };
 
-// Device views of a routing.  seg[i] = {slot, row_begin, n_rows, kind}.
+// Device views of a routing.
 struct RoutingDev {
-    const int4 *seg;
-    const int32_t *row_idx;   // token row of each active row, segment order
+    const int32_t *seg;       // kSegWords words per segment
     const int32_t *tok_slot;  // slot per token row
 };
 
@@ -99,13 +107,14 @@ struct lora_pool {
 
 namespace lora {
 // Host tables of one batch's routing.  Packed layout (int32 words):
-// [segments: 4 per segment][active rows][pad to 4][token slots][pad to 4].
+// [segments: kSegWords each][active rows][pad to 4][token slots][pad to 4].
 struct Plan {
     std::vector<int32_t> seg, rows, tok;
+    std::vector<int32_t> slot_ranks;   // per distinct slot: kMetaStride ranks
     std::vector<uint8_t> adm;
     std::vector<int32_t> distinct_slots;
     lora_routing_info info{};
-    int64_t off_row() const { return (int64_t)seg.size(); }
+    int64_t off_row() const { return (int64_t)seg.size(); }  // multiple of 4
     int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
     int64_t words() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
     void pack(int32_t *w) const
@@ -133,5 +142,6 @@ struct lora_routing {
     lora_routing_info info;
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
     std::vector<int32_t> distinct_slots;
+    std::vector<int32_t> slot_ranks;  // kMetaStride per distinct slot
     lora::Plan plan;                  // host tables, reused between builds
 };

@@ -160,17 +160,22 @@ def lora_routing_get_info(routing) -> dict:
 
 
 def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resident,
-                      max_slots, max_tokens):
-    """Host-only routing plan.  `resident` maps registry id -> slot.
+                      max_slots, max_tokens, resident_rank=None):
+    """Host-only routing plan.  `resident` maps registry id -> slot and
+    `resident_rank` (optional) registry id -> per-slice ranks.
 
     Returns a dict with info counts, admitted (bool array), and the tables
-    seg (int32 [n_seg, 4]), rows (int32 [n_active]) and tok_slot (int32 [T]).
+    seg (int32 [n_seg, 16]), rows (int32 [n_active]) and tok_slot (int32 [T]).
     """
     i32p = ctypes.POINTER(ctypes.c_int32)
     ids = np.ascontiguousarray(seq_adapter_id, dtype=np.int32)
     lens = np.ascontiguousarray(seq_len, dtype=np.int32)
     rid = np.ascontiguousarray(list(resident.keys()), dtype=np.int32)
     rsl = np.ascontiguousarray(list(resident.values()), dtype=np.int32)
+    rrk = np.zeros((max(len(rid), 1), 4), dtype=np.int32)
+    for i, aid in enumerate(resident.keys()):
+        rk = (resident_rank or {}).get(aid, ())
+        rrk[i, :len(rk)] = rk
     cap = lora_routing_bytes(max_tokens) // 4
     words = np.zeros(cap, dtype=np.int32)
     offs = np.zeros(3, dtype=np.int32)
@@ -179,12 +184,13 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
     _check(_lib().lora_plan_routing(
         len(ids), ids.ctypes.data_as(i32p), lens.ctypes.data_as(i32p), max_loras,
         prefill_min_len, len(rid), rid.ctypes.data_as(i32p), rsl.ctypes.data_as(i32p),
-        max_slots, max_tokens, words.ctypes.data_as(i32p), cap, offs.ctypes.data_as(i32p),
+        rrk.ctypes.data_as(i32p), max_slots, max_tokens, words.ctypes.data_as(i32p), cap,
+        offs.ctypes.data_as(i32p),
         ctypes.byref(info), adm.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
     d = info.as_dict()
     return dict(
         info=d, admitted=adm[:len(ids)].astype(bool),
-        seg=words[offs[0]:offs[0] + 4 * d["n_segments"]].reshape(-1, 4).copy(),
+        seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
         tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy())
 

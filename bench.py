@@ -127,15 +127,18 @@ def main():
     layer_bytes = sum(p.nbytes + x.numel() * 2 + y.numel() * 4
                       for per in layers[:1] for (p, x, y) in per.values())
 
+    # one routing serves every lane: it is built against the pool with the most
+    # slices (the others hold the same ranks on their slices)
+    build_lane = max(lanes, key=lambda ln: len(w.lanes[ln].spec.h_out))
     routing = m.Routing(T, n_seq, device=dev)
-    adm, nd = routing.build(layers[0][lanes[0]][0], w.seq_adapter, w.seq_len,
+    adm, nd = routing.build(layers[0][build_lane][0], w.seq_adapter, w.seq_len,
                             spec.max_loras, args.prefill_min_len)
     info = routing.info()
     ws = {ln: m.workspace_for(layers[0][ln][0], routing, dev) for ln in lanes}
     torch.cuda.synchronize()
 
     def step():
-        routing.build(layers[0][lanes[0]][0], w.seq_adapter, w.seq_len, spec.max_loras,
+        routing.build(layers[0][build_lane][0], w.seq_adapter, w.seq_len, spec.max_loras,
                       args.prefill_min_len)
         for per in layers:
             for ln in lanes:

@@ -163,8 +163,12 @@ int32_t lora_pool_unload(lora_pool *pool, int32_t adapter_id);
 int32_t lora_pool_slot_of(const lora_pool *pool, int32_t adapter_id, int32_t *slot_out);
 
 /* -------------------------------------------------------------- routing --
- * Per-batch routing, built once per batch and reusable for every lane and
- * layer whose pools hold the same id -> slot map.
+ * Per-batch routing, built once per batch.  It records, per segment, the
+ * slot and the rank of each slice in the pool it was built against, and can
+ * be used with any pool (another layer, another lane) that holds the same
+ * ids in the same slots with the same ranks on that pool's slices; a compute
+ * call checks this and returns LORA_ERR_MISMATCH otherwise.  To serve lanes
+ * with different slice counts, build against the pool with the most slices.
  *
  * Routing memory is one caller-allocated device buffer of
  * lora_routing_bytes(max_tokens) bytes.  The handle also owns two pinned host
@@ -224,11 +228,14 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  * this planning and then copies the words to the device.
  *
  *   resident_id/resident_slot  [n_resident] id -> slot (1..max_slots)
+ *   resident_rank optional [n_resident][4]: rank of each slice (0 if NULL)
  *   words_out     host int32 [words_capacity]; receives the packed tables:
- *                 segments {slot, first active row, rows, kind (0 decode,
- *                 1 prefill)} at word offsets_out[0], the token row of each
- *                 active row at offsets_out[1], and one slot per token row at
- *                 offsets_out[2]
+ *                 16-word segments {slot, first active row, rows, kind
+ *                 (0 decode, 1 prefill), rank of slices 0..3, token rows
+ *                 (decode: one per row, the last repeated; prefill: the first,
+ *                 rows being consecutive)} at word offsets_out[0], the token
+ *                 row of each active row at offsets_out[1], and one slot per
+ *                 token row at offsets_out[2]
  *   offsets_out   host int32 [3]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]
@@ -240,7 +247,8 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
 int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
                           int32_t max_loras, int32_t prefill_min_len, int32_t n_resident,
                           const int32_t *resident_id, const int32_t *resident_slot,
-                          int32_t max_slots, int32_t max_tokens, int32_t *words_out,
+                          const int32_t *resident_rank, int32_t max_slots, int32_t max_tokens,
+                          int32_t *words_out,
                           int64_t words_capacity, int32_t *offsets_out,
                           lora_routing_info *info_out, uint8_t *admitted_out);
 
@@ -266,7 +274,8 @@ int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **de
  */
 
 /* v for all active rows (shrink: A @ x, times scale).  Errors: ARG, SHAPE,
- * MISMATCH (routing built for a pool with more slots), HIP. */
+ * MISMATCH (a slot of the routing is empty in this pool or holds other
+ * ranks), HIP. */
 int32_t lora_shrink(const lora_pool *pool, const lora_routing *routing,
                     const void *x, int64_t ldx, float *v, void *stream);
 
@@ -279,10 +288,11 @@ int32_t lora_workspace_bytes(const lora_pool *pool, const lora_routing *routing,
                              int64_t *bytes_out);
 
 /*
- * y += scale * B @ (A @ x) for all active rows: the result is bit-identical to
- * lora_shrink followed by lora_expand.  The workspace (caller device memory,
- * >= lora_workspace_bytes) holds v.  With no active row nothing is launched
- * and LORA_OK is returned.  Errors as lora_shrink, plus CAPACITY (workspace).
+ * y += scale * B @ (A @ x) for all active rows: lora_shrink followed by
+ * lora_expand on the same stream, so the result is bit-identical to calling
+ * them in turn.  The workspace (caller device memory, >= lora_workspace_bytes)
+ * holds v between the two.  With no active row nothing is launched and
+ * LORA_OK is returned.  Errors as lora_shrink, plus CAPACITY (workspace).
  */
 int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
                          const void *x, int64_t ldx, float *y, int64_t ldy,

@@ -99,7 +99,8 @@ def _check_plan(p, ids, lens, resident, cap, pmin):
     assert sorted(rows.tolist()) == np.nonzero(slots)[0].tolist()
     seq_of = np.repeat(np.arange(len(lens)), lens)
     covered = 0
-    for k, (s, b, n, kind) in enumerate(seg):
+    for k, d in enumerate(seg):
+        s, b, n, kind = d[:4]
         assert s >= 1 and n >= 1
         assert b == covered
         covered += n
@@ -110,10 +111,12 @@ def _check_plan(p, ids, lens, resident, cap, pmin):
             assert k < info["n_decode_segments"] and n <= 8
             assert np.all(L < pmin)
             assert np.all(np.diff(r) > 0)
+            assert list(d[8:8 + n]) == list(r) and np.all(d[8 + n:] == r[-1])
         else:
             assert k >= info["n_decode_segments"] and n <= 64
             assert np.all(L >= pmin)
             assert np.all(np.diff(r) == 1) and len(set(seq_of[r])) == 1
+            assert d[8] == r[0]
             start = r[0] - np.concatenate([[0], np.cumsum(lens)])[seq_of[r[0]]]
             assert start % 64 == 0     # chunking depends only on the sequence
     assert covered == len(rows)
@@ -122,7 +125,7 @@ def _check_plan(p, ids, lens, resident, cap, pmin):
     for s in set(dec[:, 0].tolist()):
         ks = np.nonzero(dec[:, 0] == s)[0]
         assert np.all(np.diff(ks) == 1)
-        r = np.concatenate([rows[b:b + n] for _, b, n, _ in dec[ks]])
+        r = np.concatenate([rows[d[1]:d[1] + d[2]] for d in dec[ks]])
         assert np.all(np.diff(r) > 0)
         assert np.all(dec[ks][:-1, 2] == 8)
 
@@ -139,8 +142,12 @@ def test_plan_random_batches(m, seed):
     cap = int(rng.integers(0, n_ad + 1))
     pmin = int(rng.choice([1, 16, 64, 2**31 - 1]))
     T = max(int(np.sum(lens)), 1)
-    p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T)
+    ranks = {i: [int(x) for x in rng.integers(1, 65, size=4)] for i in ids_pool}
+    p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T, resident_rank=ranks)
     _check_plan(p, ids, lens, resident, cap, pmin)
+    inv = {s: i for i, s in resident.items()}
+    for d in p["seg"]:
+        assert list(d[4:8]) == ranks[inv[d[0]]]
 
 
 def test_plan_errors(m):
