@@ -42,6 +42,19 @@ __device__ __forceinline__ Seg load_seg(const int32_t *seg, int si)
     return Seg{p[0], p[1], p[2], p[3]};
 }
 
+// Workgroups are handed to the 8 XCDs round-robin by block id, and each XCD
+// has its own L2.  This bijection on [0, n) gives XCD x the consecutive task
+// range of its share, so tasks that read the same rows or factor tiles (which
+// sit next to each other in task order) share an L2.  Placement only changes
+// speed, never results.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_task(int b, int n)
+{
+    const int q = n / kXcds, rem = n % kXcds;
+    const int xcd = b % kXcds, local = b / kXcds;
+    return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+}
+
 __device__ __forceinline__ uint4 ld16(const uint16_t *p)
 {
     return *reinterpret_cast<const uint4 *>(p);

@@ -12,14 +12,16 @@
 namespace lora {
 namespace {
 
-template <bool FP16X>
-__global__ __launch_bounds__(64 * kParts) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                              int kb_per_slice,
-                                                              const uint16_t *__restrict__ x,
-                                                              int64_t ldx, float *__restrict__ v)
+// W waves per task (1, 2, 4 or 8): wave w sums parts w, w + W, ... of the 8,
+// each reduced on its own, so the bits do not depend on W.
+template <bool FP16X, int W>
+__global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
+                                                         int kb_per_slice,
+                                                         const uint16_t *__restrict__ x,
+                                                         int64_t ldx, float *__restrict__ v)
 {
     const int per_seg = g.n_slices * kb_per_slice;
-    const int task = blockIdx.x;
+    const int task = xcd_task(blockIdx.x, gridDim.x);
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / kb_per_slice;
@@ -29,13 +31,18 @@ __global__ __launch_bounds__(64 * kParts) void k_shrink_gemv(LaneGeom g, PoolDev
     const int k0 = kb * kKBlock;
     if (k0 >= rank) return;
     const int kn = min(kKBlock, rank - k0);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
 
-    // wave w owns part w
-    const float red = shrink_part<FP16X>(g, p, sd, j, k0, kn, wave, lane, x, ldx);
     __shared__ float part[kParts][64];
-    part[wave][lane] = red;
+#pragma unroll
+    for (int pp = 0; pp < kParts / W; ++pp) {
+        const int pt = wave + pp * W;
+        // a part with no sub-chunk sums to zero
+        part[pt][lane] =
+            pt < n_sub ? shrink_part<FP16X>(g, p, sd, j, k0, kn, pt, lane, x, ldx) : 0.f;
+    }
     __syncthreads();
     if (wave == 0) {
         const float q0 = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
 {
     constexpr int C = kExpandRows;
     const int per_seg = g.n_slices * tiles_per_slice;
-    const int task = blockIdx.x;
+    const int task = xcd_task(blockIdx.x, gridDim.x);
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / tiles_per_slice;
@@ -159,12 +166,24 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
-    if (g.x_fp16)
-        hipLaunchKernelGGL(k_shrink_gemv<true>, dim3((unsigned)blocks), dim3(64 * kParts), 0, s,
-                           g, p, r, kb_per_slice, xp, ldx, v);
-    else
-        hipLaunchKernelGGL(k_shrink_gemv<false>, dim3((unsigned)blocks), dim3(64 * kParts), 0, s,
-                           g, p, r, kb_per_slice, xp, ldx, v);
+    // waves per task: enough for the sub-chunks of h_in, at most one per part
+    const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
+    const int w = n_sub >= 8 ? 8 : n_sub >= 4 ? 4 : n_sub >= 2 ? 2 : 1;
+    const dim3 grid((unsigned)blocks), block(64 * w);
+#define LAUNCH_SHRINK(F, W) \
+    hipLaunchKernelGGL((k_shrink_gemv<F, W>), grid, block, 0, s, g, p, r, kb_per_slice, xp, ldx, v)
+    if (g.x_fp16) {
+        if (w == 8) LAUNCH_SHRINK(true, 8);
+        else if (w == 4) LAUNCH_SHRINK(true, 4);
+        else if (w == 2) LAUNCH_SHRINK(true, 2);
+        else LAUNCH_SHRINK(true, 1);
+    } else {
+        if (w == 8) LAUNCH_SHRINK(false, 8);
+        else if (w == 4) LAUNCH_SHRINK(false, 4);
+        else if (w == 2) LAUNCH_SHRINK(false, 2);
+        else LAUNCH_SHRINK(false, 1);
+    }
+#undef LAUNCH_SHRINK
     return hipGetLastError();
 }
 

@@ -7,10 +7,12 @@
 // Both use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Each wave owns
 // 16 rows of the segment.
 //
-// Shrink:  u^T[k][t] = sum over K-steps of 32 (ascending) of one MFMA with
-//          the pool's A rows as the first operand and x rows as the second.
-//          An fp16 x is split exactly into bf16 hi + lo and each K-step does
-//          the hi product, then the lo product.  v = fp32(scale * u).
+// Shrink:  h_in is cut into K-steps of 32; K-step s belongs to part s % 4.
+//          S_w[t][k] = MFMA chain over the K-steps of part w, ascending, with
+//          the pool's A rows as the first operand and x rows as the second;
+//          u = (S_0 + S_1) + (S_2 + S_3) and v = fp32(scale * u).  An fp16 x
+//          is split exactly into bf16 hi + lo and each K-step does the hi
+//          product, then the lo product.  The order depends on h_in only.
 // Expand:  d^T[o][t] = sum over K-steps of 32 (ascending) of two MFMAs,
 //          B rows times v_hi then B rows times v_lo, where v = v_hi + v_lo with
 //          v_hi = bf16(v) and v_lo = bf16(v - v_hi) (both nearest-even), which
@@ -73,67 +75,123 @@ __device__ __forceinline__ void split_f32x8(const float (&f)[8], uint4 &hi, uint
                     l[6] | (l[7] << 16));
 }
 
-template <bool FP16X, int NT>
-__global__ __launch_bounds__(256) void k_shrink_mfma(LaneGeom g, PoolDev p, RoutingDev r,
-                                                      int seg_begin,
-                                                      const uint16_t *__restrict__ x,
-                                                      int64_t ldx, float *__restrict__ v)
+constexpr int kShrinkParts = 4;     // waves of a shrink task: one K-part each
+constexpr int kShrinkNG = 2;        // 16-rank tiles per shrink task
+constexpr int kShrinkDepth = 4;     // K-steps of loads in flight per wave
+constexpr int kRowTiles = kPrefillSegRows / 16;
+
+template <bool FP16X>
+__global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
+    LaneGeom g, PoolDev p, RoutingDev r, int seg_begin, int groups_per_slice,
+    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v)
 {
-    const int task = blockIdx.x;
-    const int si = seg_begin + task / g.n_slices;
-    const int j = task % g.n_slices;
+    constexpr int NG = kShrinkNG, D = kShrinkDepth;
+    const int per_seg = g.n_slices * groups_per_slice;
+    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int si = seg_begin + task / per_seg;
+    const int rem = task % per_seg;
+    const int j = rem / groups_per_slice;
+    const int grp = rem - j * groups_per_slice;
     const Seg sd = load_seg(r.seg, si);
-    const int slot = sd.slot();
     const int n_rows = sd.n_rows();
     const int rank = sd.rank(j);
     const int ntiles = (rank + 15) / 16;
+    const int t0 = grp * NG;
+    if (t0 >= ntiles) return;
+    const int nt_here = min(NG, ntiles - t0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int r0 = wave * 16;
-    if (r0 >= n_rows || ntiles > NT) return;
     const int li = lane & 15, lg = lane >> 4;
-    const int row = r0 + li;
-    const bool row_ok = row < n_rows;
-    const uint16_t *xrow = x + (int64_t)(sd.first_row() + (row_ok ? row : r0)) * ldx;
-    const uint16_t *Ab = p.A + (int64_t)(slot - 1) * g.a_slot_stride +
-                         (int64_t)j * g.rank_pad * g.h_in + (int64_t)li * g.h_in;
-    const int64_t tile_stride = (int64_t)16 * g.h_in;
+    const int n_rt = (n_rows + 15) / 16;
 
-    f32x4_t acc[NT];
+    // Operand rows of this lane: x row 16*rt + li (rows past the segment read
+    // row 0 and are zeroed), A row 16*(t0+nt) + li (inside rank_pad).
+    const uint16_t *xr[kRowTiles];
+    bool xok[kRowTiles];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+        const int row = 16 * rt + li;
+        xok[rt] = row < n_rows;
+        xr[rt] = x + (int64_t)(sd.first_row() + (xok[rt] ? row : 0)) * ldx;
+    }
+    const uint16_t *ar[NG];
+#pragma unroll
+    for (int nt = 0; nt < NG; ++nt)
+        ar[nt] = p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride +
+                 ((int64_t)j * g.rank_pad + 16 * (t0 + min(nt, nt_here - 1)) + li) * g.h_in;
 
+    f32x4_t acc[kRowTiles][NG];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NG; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // K-steps wave, wave + 4, ...; loads run kShrinkDepth steps ahead.  The
+    // loop is branch-free so the loads stay in flight: every load has a valid
+    // (clamped) address, and rows past the segment, K-steps past h_in and the
+    // padding steps that round a wave's count up to a multiple of the depth
+    // are multiplied as zeros.
+    const int n_ks = (g.h_in + 31) / 32;
+    const int my_steps = (n_ks - wave + kShrinkParts - 1) / kShrinkParts;
+    uint4 xs[D][kRowTiles], as[D][NG];
     const uint4 zero = make_uint4(0, 0, 0, 0);
-#pragma unroll 2
-    for (int k0 = 0; k0 < g.h_in; k0 += 32) {
-        const int e = k0 + lg * 8;
-        const bool e_ok = e < g.h_in;
-        const uint4 xv = (row_ok && e_ok) ? ld16(xrow + e) : zero;
-        uint4 xhi = xv, xlo = zero;
-        if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
+    auto load = [&](uint4 (&xt)[kRowTiles], uint4 (&at)[NG], int step) {
+        const int e = min((wave + kShrinkParts * step) * 32 + lg * 8, g.h_in - 8);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt < ntiles) {
-                const uint4 av = e_ok ? ld16(Ab + nt * tile_stride + e) : zero;
-                acc[nt] = mfma16x16x32(av, xhi, acc[nt]);
-                if constexpr (FP16X) acc[nt] = mfma16x16x32(av, xlo, acc[nt]);
+        for (int rt = 0; rt < kRowTiles; ++rt) xt[rt] = ld16(xr[rt] + e);
+#pragma unroll
+        for (int nt = 0; nt < NG; ++nt) at[nt] = ld16(ar[nt] + e);
+    };
+    auto mma = [&](const uint4 (&xt)[kRowTiles], const uint4 (&at)[NG], int step) {
+        const bool e_ok = (wave + kShrinkParts * step) * 32 + lg * 8 < g.h_in;
+#pragma unroll
+        for (int rt = 0; rt < kRowTiles; ++rt) {
+            const uint4 xv = (e_ok && xok[rt]) ? xt[rt] : zero;
+            uint4 xhi = xv, xlo = zero;
+            if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
+#pragma unroll
+            for (int nt = 0; nt < NG; ++nt) {
+                const uint4 av = e_ok ? at[nt] : zero;
+                acc[rt][nt] = mfma16x16x32(av, xhi, acc[rt][nt]);
+                if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(av, xlo, acc[rt][nt]);
             }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(xs[s], as[s], s);
+    for (int base = 0; base < my_steps; base += D) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            mma(xs[s], as[s], base + s);
+            load(xs[s], as[s], base + s + D);
         }
     }
 
-    if (row_ok) {
-        const float scale = p.scale[slot * kMetaStride + j];
-        float *vr = v + (int64_t)(sd.v_row() + row) * g.v_stride + j * g.rank_pad + 4 * lg;
+    // u = (S0 + S1) + (S2 + S3) through LDS.  Lane l holds, per (rt, nt),
+    // u^T[rank 16*nt + 4*lg + i][row 16*rt + li].
+    __shared__ float red[kShrinkParts][kPrefillSegRows][NG * 16];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (nt < ntiles) {
-                float4 o;
-                o.x = scale * acc[nt][0];
-                o.y = scale * acc[nt][1];
-                o.z = scale * acc[nt][2];
-                o.w = scale * acc[nt][3];
-                *reinterpret_cast<float4 *>(vr + nt * 16) = o;
-            }
+    for (int rt = 0; rt < kRowTiles; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NG; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                red[wave][16 * rt + li][16 * nt + 4 * lg + i] = acc[rt][nt][i];
+    __syncthreads();
+    const float scale = p.scale[sd.slot() * kMetaStride + j];
+    constexpr int kOut = kPrefillSegRows * NG * 16;      // outputs of the task
+    for (int o = threadIdx.x * 4; o < kOut; o += 64 * kShrinkParts * 4) {
+        const int row = o / (NG * 16);
+        const int k = o % (NG * 16);
+        if (row < n_rows && k < nt_here * 16) {
+            float4 u;
+            float *uf = &u.x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                uf[i] = scale * ((red[0][row][k + i] + red[1][row][k + i]) +
+                                 (red[2][row][k + i] + red[3][row][k + i]));
+            *reinterpret_cast<float4 *>(v + (int64_t)(sd.v_row() + row) * g.v_stride +
+                                        j * g.rank_pad + 16 * t0 + k) = u;
         }
     }
 }
@@ -144,17 +202,19 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, Rout
                                                       const float *__restrict__ v,
                                                       float *__restrict__ y, int64_t ldy)
 {
+    constexpr int COLS = NS * 16;                  // columns of the task
+    constexpr int LDT = COLS + 4;                  // padded LDS row
+    static_assert(COLS == 128, "two rows of y per wave instruction");
     const int per_seg = g.n_slices * tiles_per_slice;
-    const int task = blockIdx.x;
+    const int task = xcd_task(blockIdx.x, gridDim.x);
     const int si = seg_begin + task / per_seg;
     const int rem = task % per_seg;
     const int j = rem / tiles_per_slice;
     const int tile = rem - j * tiles_per_slice;
     const int hj = g.h_out[j];
-    const int o_base = tile * (NS * 16);
+    const int o_base = tile * COLS;
     if (o_base >= hj) return;
     const Seg sd = load_seg(r.seg, si);
-    const int slot = sd.slot();
     const int n_rows = sd.n_rows();
     const int rank = sd.rank(j);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,11 +222,26 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, Rout
     const int r0 = wave * 16;
     if (r0 >= n_rows) return;
     const int li = lane & 15, lg = lane >> 4;
+
+    // y of this wave's 16 rows, two whole 128-column rows per instruction:
+    // lane l takes row 2q + l/32, columns 4 * (l % 32) .. + 3.
+    const int yc = o_base + 4 * (lane & 31);
+    const bool yc_ok = yc < hj;
+    float4 yv[8];
+    float *yp[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = r0 + 2 * q + (lane >> 5);
+        const bool ok = row < n_rows && yc_ok;
+        yp[q] = ok ? y + (int64_t)(sd.first_row() + row) * ldy + g.col_off[j] + yc : nullptr;
+        if (ok) yv[q] = *reinterpret_cast<const float4 *>(yp[q]);
+    }
+
     const int row = r0 + li;
     const bool row_ok = row < n_rows;
     const float *vrow =
         v + (int64_t)(sd.v_row() + (row_ok ? row : r0)) * g.v_stride + j * g.rank_pad;
-    const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+    const uint16_t *Bn = p.Bn + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j];
 
     f32x4_t acc[NS];
 #pragma unroll
@@ -197,21 +272,31 @@ __global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, Rout
         }
     }
 
-    if (row_ok) {
-        const int t = sd.first_row() + row;
-        float *yrow = y + (int64_t)t * ldy + g.col_off[j];
+    // d of (row li, columns 16 s + 4 lg ..) -> LDS -> the y layout above
+    __shared__ float dt[4][16][LDT];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int oc = o_base + s * 16 + 4 * lg;
-            if (oc < hj) {
-                float4 *yp = reinterpret_cast<float4 *>(yrow + oc);
-                float4 yv = *yp;
-                yv.x += acc[s][0];
-                yv.y += acc[s][1];
-                yv.z += acc[s][2];
-                yv.w += acc[s][3];
-                *yp = yv;
-            }
+    for (int s = 0; s < NS; ++s) {
+        float4 d;
+        d.x = acc[s][0];
+        d.y = acc[s][1];
+        d.z = acc[s][2];
+        d.w = acc[s][3];
+        *reinterpret_cast<float4 *>(&dt[wave][li][16 * s + 4 * lg]) = d;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (yp[q]) {
+            const float4 d =
+                *reinterpret_cast<const float4 *>(&dt[wave][2 * q + (lane >> 5)][4 * (lane & 31)]);
+            float4 o = yv[q];
+            o.x += d.x;
+            o.y += d.y;
+            o.z += d.z;
+            o.w += d.w;
+            *reinterpret_cast<float4 *>(yp[q]) = o;
         }
     }
 }
@@ -222,23 +307,18 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               int seg_begin, int n_seg, int nt_per_slice, const void *x,
                               int64_t ldx, float *v, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)n_seg * g.n_slices;
-    if (blocks <= 0 || nt_per_slice <= 0) return hipSuccess;
-    if (blocks > INT32_MAX || nt_per_slice > 16) return hipErrorInvalidConfiguration;
+    const int groups = (nt_per_slice + kShrinkNG - 1) / kShrinkNG;
+    const int64_t blocks = (int64_t)n_seg * g.n_slices * groups;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
-    const dim3 grid((unsigned)blocks), block(256);
-#define LAUNCH_SHRINK(F, N) \
-    hipLaunchKernelGGL((k_shrink_mfma<F, N>), grid, block, 0, s, g, p, r, seg_begin, xp, ldx, v)
-    if (g.x_fp16) {
-        if (nt_per_slice <= 4) LAUNCH_SHRINK(true, 4);
-        else if (nt_per_slice <= 8) LAUNCH_SHRINK(true, 8);
-        else LAUNCH_SHRINK(true, 16);
-    } else {
-        if (nt_per_slice <= 4) LAUNCH_SHRINK(false, 4);
-        else if (nt_per_slice <= 8) LAUNCH_SHRINK(false, 8);
-        else LAUNCH_SHRINK(false, 16);
-    }
-#undef LAUNCH_SHRINK
+    const dim3 grid((unsigned)blocks), block(64 * kShrinkParts);
+    if (g.x_fp16)
+        hipLaunchKernelGGL(k_shrink_mfma<true>, grid, block, 0, s, g, p, r, seg_begin, groups, xp,
+                           ldx, v);
+    else
+        hipLaunchKernelGGL(k_shrink_mfma<false>, grid, block, 0, s, g, p, r, seg_begin, groups, xp,
+                           ldx, v);
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,23 +36,124 @@ def log(msg):
 
 
 def algorithmic(w, lane_name, admitted):
-    """Bytes and flops the delta of one lane must move / compute for a batch:
-    x of active rows, read+write of their fp32 y, A and B once per distinct
-    adapter, one 4-byte slot id per token row."""
-    import oracle
+    """Bytes and flops the delta of one lane must move / compute for a batch,
+    split by step.  Shrink: x of active rows, A once per distinct (adapter,
+    slice), one 4-byte slot id per token row.  Expand: read + write of the
+    active rows' fp32 y, B once per distinct (adapter, slice)."""
     L = w.lanes[lane_name].spec
-    tok = oracle.token_adapters(w.seq_adapter, w.seq_len, admitted)
+    tok = np.repeat(np.where(admitted, w.seq_adapter, 0), w.seq_len)
     act = int((tok != 0).sum())
-    bx = 2
-    H = L.h_out_total
-    nbytes = act * (L.h_in * bx + 8 * H) + 4 * len(tok)
-    flops = 0
+    sb = act * L.h_in * 2 + 4 * len(tok)
+    eb = act * 8 * L.h_out_total
+    sf_ = ef = 0
     for aid in set(tok.tolist()) - {0}:
         n = int((tok == aid).sum())
         for sf, hj in zip(w.adapters[aid].lanes[lane_name], L.h_out):
-            nbytes += 2 * sf.rank * (L.h_in + hj)
-            flops += n * 2 * sf.rank * (L.h_in + hj)
-    return nbytes, flops, act
+            sb += 2 * sf.rank * L.h_in
+            eb += 2 * sf.rank * hj
+            sf_ += n * 2 * sf.rank * L.h_in
+            ef += n * 2 * sf.rank * hj
+    return {"shrink": (sb, sf_), "expand": (eb, ef), "active": act}
+
+
+KERNEL_SOURCES = ("include/lora.h", "adapter_deltas_amd/csrc")
+COPY_CALIBRATION_BYTES = 268435456
+
+
+def call_kernels(call: str, info) -> str:
+    """The kernels one lora_shrink / lora_expand call launches."""
+    ks = []
+    if info["n_decode_segments"]:
+        ks.append(f"k_{call}_gemv")
+    if info["n_prefill_segments"]:
+        ks.append(f"k_{call}_mfma")
+    return f"lora_{call}: " + " + ".join(ks)
+
+
+def summarize_pmc(pmc_dir: str, configs):
+    """profiles/traffic.json from rocprofv3 --pmc runs: per workload and call,
+    the HBM bytes per launch, FETCH_SIZE and WRITE_SIZE each scaled by what
+    the same counter reads for a plain copy of COPY_CALIBRATION_BYTES."""
+    import csv
+    import statistics
+
+    def per_kernel(run):
+        out = {}
+        with open(os.path.join(pmc_dir, run, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    def copy_kib(run):
+        vals = [statistics.median(v) for k, v in per_kernel(run).items() if "copyBuffer" in k]
+        return vals[0]
+    fetch_scale = COPY_CALIBRATION_BYTES / (copy_kib("copy_fetch") * 1024)
+    write_scale = COPY_CALIBRATION_BYTES / (copy_kib("copy_write") * 1024)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    doc = json.load(open(path)) if os.path.exists(path) else {}
+    for cfg in configs:
+        fetch = per_kernel(f"{cfg}_fetch")
+        write = per_kernel(f"{cfg}_write")
+        entry = {}
+        for call in ("shrink", "expand"):
+            names = [k for k in fetch if f"k_{call}_" in k]
+            if not names:
+                continue
+            f_kib = sum(statistics.median(fetch[k]) for k in names)
+            w_kib = sum(statistics.median(write[k]) for k in names)
+            entry[call] = {
+                "kernels": sorted({re.search(r"k_\w+", k).group(0) for k in names}),
+                "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+                "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+                "hbm_bytes_per_launch": int(f_kib * 1024 * fetch_scale +
+                                            w_kib * 1024 * write_scale),
+                "sources_sha256": sources_digest(),
+                "commands": [
+                    f"rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py "
+                    f"--copy-calibration {COPY_CALIBRATION_BYTES}",
+                    f"rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py "
+                    f"--copy-calibration {COPY_CALIBRATION_BYTES}",
+                    f"rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py "
+                    f"--config {cfg} --steps 2 --warmup 1 --layers 8 --graph-reps 1 "
+                    f"--cpu-seconds 0.1",
+                    f"rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py "
+                    f"--config {cfg} --steps 2 --warmup 1 --layers 8 --graph-reps 1 "
+                    f"--cpu-seconds 0.1"],
+            }
+        doc[cfg] = entry
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+    print(json.dumps(doc, indent=1))
+
+
+def sources_digest() -> str:
+    """sha256 over the library's sources: a counter summary taken from other
+    sources no longer describes the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    for top in KERNEL_SOURCES:
+        path = os.path.join(ROOT, top)
+        files = [path] if os.path.isfile(path) else sorted(
+            os.path.join(path, f) for f in os.listdir(path)
+            if f.endswith((".h", ".hip", ".cpp")))
+        for f in files:
+            h.update(os.path.relpath(f, ROOT).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json, if that
+    summary was taken from the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(config, {}).get(kernel)
+    if not rec or rec.get("sources_sha256") != sources_digest():
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def cpu_baseline(w, lanes, seconds):
@@ -81,7 +183,28 @@ def main():
     ap.add_argument("--graph-reps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill-min-len", type=int, default=64)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 10 times (the "
+                         "reference kernel that scales HBM byte counters)")
+    ap.add_argument("--summarize-pmc", default="", metavar="DIR",
+                    help="only write profiles/traffic.json from rocprofv3 --pmc output "
+                         "in DIR for the workloads given with --config (comma list)")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.config.split(","))
+        return
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 10}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -167,42 +290,54 @@ def main():
     delta_rows = info["n_active"] * len(lanes) * args.layers
     value = delta_rows / (ms_per_step * 1e-3)
 
-    # kernel timing: the layer launches captured once and replayed
-    log("graph replay timing")
-    g = torch.cuda.CUDAGraph()
+    # Kernel timing: each call's launches for every layer and lane captured
+    # once as a graph and replayed; HIP events on the launching stream.
     side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        for per in layers:
-            for ln in lanes:
-                pool, x, y = per[ln]
-                m.delta_apply(pool, routing, x, y, ws[ln])
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        for per in layers:
-            for ln in lanes:
-                pool, x, y = per[ln]
-                m.delta_apply(pool, routing, x, y, ws[ln])
-    g.replay()
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.graph_reps):
-        g.replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    per_apply_us = g0.elapsed_time(g1) * 1e3 / (args.graph_reps * args.layers * len(lanes))
+    vbuf = {ln: torch.empty(max(info["n_active"], 1) * layers[0][ln][0].v_stride,
+                            dtype=torch.float32, device=dev) for ln in lanes}
 
-    nbytes = flops = 0
+    def graph_us(call):
+        def body():
+            for per in layers:
+                for ln in lanes:
+                    pool, x, y = per[ln]
+                    call(ln, pool, x, y)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            body()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.graph_reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) * 1e3 / (args.graph_reps * args.layers * len(lanes))
+
+    log("graph replay timing")
+    per_apply_us = graph_us(lambda ln, pool, x, y: m.delta_apply(pool, routing, x, y, ws[ln]))
+    shrink_us = graph_us(lambda ln, pool, x, y: m.shrink(pool, routing, x, vbuf[ln]))
+    expand_us = graph_us(lambda ln, pool, x, y: m.expand(pool, routing, vbuf[ln], y))
+
+    alg = {"shrink": [0, 0], "expand": [0, 0]}
     for ln in lanes:
-        b, f, _ = algorithmic(w, ln, adm)
-        nbytes += b
-        flops += f
-    nbytes /= len(lanes)
-    flops /= len(lanes)
-    achieved_gbs = nbytes / (per_apply_us * 1e-6) / 1e9
+        a = algorithmic(w, ln, adm)
+        for k in ("shrink", "expand"):
+            alg[k][0] += a[k][0] / len(lanes)
+            alg[k][1] += a[k][1] / len(lanes)
+    dominant = "expand" if expand_us >= shrink_us else "shrink"
+    dom_us = expand_us if dominant == "expand" else shrink_us
+    dom_bytes = alg[dominant][0]
+    achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    total_bytes = alg["shrink"][0] + alg["expand"][0]
+    traffic = recorded_traffic(spec.name, dominant)
 
     log(f"cpu baseline ~{args.cpu_seconds}s")
     cpu_rate, cpu_dt, cpu_reps = cpu_baseline(w, lanes, args.cpu_seconds)
@@ -231,14 +366,22 @@ def main():
             "step": "routing build + delta_apply on every lane of every layer",
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
-        "kernel_us_per_lane_layer": round(per_apply_us, 3),
         "roofline": {
-            "kernel": "delta_apply (all launches of one lane-layer)",
+            "kernel": call_kernels(dominant, info),
             "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_launch": int(nbytes),
-            "algorithmic_flops_per_launch": int(flops),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(dom_bytes),
+            "us_per_launch": round(dom_us, 3),
+        },
+        "per_lane_layer": {
+            "delta_apply_us": round(per_apply_us, 3),
+            "shrink_us": round(shrink_us, 3), "expand_us": round(expand_us, 3),
+            "algorithmic_bytes": int(total_bytes),
+            "delta_apply_gbs": round(total_bytes / (per_apply_us * 1e-6) / 1e9, 1),
+            "shrink_gbs": round(alg["shrink"][0] / (shrink_us * 1e-6) / 1e9, 1),
+            "expand_gbs": round(alg["expand"][0] / (expand_us * 1e-6) / 1e9, 1),
+            "flops": int(alg["shrink"][1] + alg["expand"][1]),
         },
         "cpu_baseline": {
             "value": round(cpu_rate, 1), "unit": "delta tokens/s", "cores": 1,
