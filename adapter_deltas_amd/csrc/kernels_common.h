@@ -36,10 +36,15 @@ struct Seg {
     __device__ int first_row() const { return lo.x; }
 };
 
+// Descriptors are read-only while kernels run, so they are read through the
+// constant address space: a uniform index then gives scalar loads, which
+// neither take vector registers nor wait behind the vector loads in flight.
 __device__ __forceinline__ Seg load_seg(const int32_t *seg, int si)
 {
-    const int4 *p = reinterpret_cast<const int4 *>(seg + (int64_t)si * kSegWords);
-    return Seg{p[0], p[1], p[2], p[3]};
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    cint *p = (cint *)(seg + (int64_t)si * kSegWords);
+    return Seg{make_int4(p[0], p[1], p[2], p[3]), make_int4(p[4], p[5], p[6], p[7]),
+               make_int4(p[8], p[9], p[10], p[11]), make_int4(p[12], p[13], p[14], p[15])};
 }
 
 // Workgroups are handed to the 8 XCDs round-robin by block id, and each XCD

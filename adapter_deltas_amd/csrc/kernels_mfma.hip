@@ -196,108 +196,189 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     }
 }
 
-template <int NS>
-__global__ __launch_bounds__(256) void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
-                                                      int seg_begin, int tiles_per_slice,
+// A task is one 128-column tile of one slice over a group of consecutive
+// prefill segments.  The tile's B rows (128 outputs x 32*NK ranks, zero past
+// the slot's rank) are staged in LDS once and kept while the slot stays the
+// same, so a group that covers one prompt reads its B tile from HBM once.
+// Wave w multiplies rows 16w .. 16w + 15 of each segment.
+template <int NK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
+void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
+                                                      int seg_begin, int seg_end, int group,
+                                                      int tiles_per_slice,
                                                       const float *__restrict__ v,
                                                       float *__restrict__ y, int64_t ldy)
 {
-    constexpr int COLS = NS * 16;                  // columns of the task
-    constexpr int LDT = COLS + 4;                  // padded LDS row
+    constexpr int NS = kMfmaExpandCols / 16;      // 16-column MFMA tiles of a task
+    constexpr int COLS = kMfmaExpandCols;
+    constexpr int LDT = COLS + 4;                 // padded LDS row of d
+    constexpr int KR = 32 * NK;                   // staged ranks
+    constexpr int LDB = KR + 8;                   // padded LDS row of B (bf16)
+    constexpr int CPR = KR / 8;                   // 16-byte chunks per staged B row
     static_assert(COLS == 128, "two rows of y per wave instruction");
-    const int per_seg = g.n_slices * tiles_per_slice;
+    const int per_grp = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, gridDim.x);
-    const int si = seg_begin + task / per_seg;
-    const int rem = task % per_seg;
+    const int grp = task / per_grp;
+    const int rem = task - grp * per_grp;
     const int j = rem / tiles_per_slice;
     const int tile = rem - j * tiles_per_slice;
     const int hj = g.h_out[j];
     const int o_base = tile * COLS;
     if (o_base >= hj) return;
-    const Seg sd = load_seg(r.seg, si);
-    const int n_rows = sd.n_rows();
-    const int rank = sd.rank(j);
+    const int s_first = seg_begin + grp * group;
+    const int s_last = min(s_first + group, seg_end);
+
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int r0 = wave * 16;
-    if (r0 >= n_rows) return;
     const int li = lane & 15, lg = lane >> 4;
-
-    // y of this wave's 16 rows, two whole 128-column rows per instruction:
-    // lane l takes row 2q + l/32, columns 4 * (l % 32) .. + 3.
+    const int r0 = wave * 16;
     const int yc = o_base + 4 * (lane & 31);
     const bool yc_ok = yc < hj;
-    float4 yv[8];
-    float *yp[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = r0 + 2 * q + (lane >> 5);
-        const bool ok = row < n_rows && yc_ok;
-        yp[q] = ok ? y + (int64_t)(sd.first_row() + row) * ldy + g.col_off[j] + yc : nullptr;
-        if (ok) yv[q] = *reinterpret_cast<const float4 *>(yp[q]);
-    }
 
-    const int row = r0 + li;
-    const bool row_ok = row < n_rows;
-    const float *vrow =
-        v + (int64_t)(sd.v_row() + (row_ok ? row : r0)) * g.v_stride + j * g.rank_pad;
-    const uint16_t *Bn = p.Bn + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+    __shared__ __align__(16) uint16_t bs[COLS][LDB];
+    __shared__ __align__(16) float dt[4][16][LDT];
 
-    f32x4_t acc[NS];
+    // y of this wave's 16 rows of a segment, two whole 128-column rows per
+    // instruction: lane l takes row 2q + l/32, columns 4 * (l % 32) .. + 3.
+    // Loads are branch-free: rows past the segment read its last row and
+    // columns past the slice its last four columns (h_out is a multiple of 8);
+    // only the stores are masked.
+    auto y_row = [&](int q) { return r0 + 2 * q + (lane >> 5); };
+    auto y_base = [&](Seg sd) {
+        return y + (int64_t)sd.first_row() * ldy + g.col_off[j] + min(yc, hj - 4);
+    };
+    // v of row r0 + li, ranks 32 ks + 8 lg .. + 7 (raw; the rank and row
+    // masks are applied when the rows are used).  The addresses stay inside
+    // the row.
+    auto load_v = [&](Seg sd, float4 (&vr)[2 * NK]) {
+        const float *vrow = v + (int64_t)(sd.v_row() + min(r0 + li, sd.n_rows() - 1)) * g.v_stride +
+                            j * g.rank_pad;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int k0 = 0; k0 < rank; k0 += 32) {
-        const int kk = k0 + lg * 8;
-        float vf[8];
-        if (row_ok && kk + 8 <= rank) {
-            const float4 a = *reinterpret_cast<const float4 *>(vrow + kk);
-            const float4 b = *reinterpret_cast<const float4 *>(vrow + kk + 4);
-            vf[0] = a.x; vf[1] = a.y; vf[2] = a.z; vf[3] = a.w;
-            vf[4] = b.x; vf[5] = b.y; vf[6] = b.z; vf[7] = b.w;
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) vf[m] = (row_ok && kk + m < rank) ? vrow[kk + m] : 0.f;
+        for (int ks = 0; ks < NK; ++ks) {
+            const int kc = min(32 * ks + 8 * lg, g.rank_pad - 8);
+            vr[2 * ks] = *reinterpret_cast<const float4 *>(vrow + kc);
+            vr[2 * ks + 1] = *reinterpret_cast<const float4 *>(vrow + kc + 4);
         }
-        uint4 vhi, vlo;
-        split_f32x8(vf, vhi, vlo);
-        const bool k_ok = kk + 8 <= g.rank_pad;
+    };
+    // Rows of the next segment that load while the current one is worked on:
+    // y always, v too when it is small (up to 64 ranks).  v is loaded before
+    // y since it is needed first and loads complete in issue order.
+    constexpr bool kPrefetchV = NK <= 2;
+    auto load_rows = [&](Seg sd, float4 (&yv)[8], float4 (&vr)[2 * NK]) {
+        if constexpr (kPrefetchV) load_v(sd, vr);
+        const float *yb = y_base(sd);
+        const int last = sd.n_rows() - 1;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int o = o_base + s * 16 + li;
-            const uint4 bv = (k_ok && o < hj) ? ld16(Bn + (int64_t)o * g.rank_pad + kk) : zero;
-            acc[s] = mfma16x16x32(bv, vhi, acc[s]);
-            acc[s] = mfma16x16x32(bv, vlo, acc[s]);
-        }
-    }
+        for (int q = 0; q < 8; ++q)
+            yv[q] = *reinterpret_cast<const float4 *>(yb + (int64_t)min(y_row(q), last) * ldy);
+    };
 
-    // d of (row li, columns 16 s + 4 lg ..) -> LDS -> the y layout above
-    __shared__ float dt[4][16][LDT];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        float4 d;
-        d.x = acc[s][0];
-        d.y = acc[s][1];
-        d.z = acc[s][2];
-        d.w = acc[s][3];
-        *reinterpret_cast<float4 *>(&dt[wave][li][16 * s + 4 * lg]) = d;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        if (yp[q]) {
-            const float4 d =
-                *reinterpret_cast<const float4 *>(&dt[wave][2 * q + (lane >> 5)][4 * (lane & 31)]);
-            float4 o = yv[q];
-            o.x += d.x;
-            o.y += d.y;
-            o.z += d.z;
-            o.w += d.w;
-            *reinterpret_cast<float4 *>(yp[q]) = o;
+    int staged = 0;                               // slot whose B tile is in bs
+    auto stage_b = [&](Seg sd) {           // uniform over the workgroup
+        const int slot = sd.slot();
+        if (slot == staged) return;
+        __syncthreads();
+        const int rank = sd.rank(j);
+        const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+        for (int c = threadIdx.x; c < COLS * CPR; c += 256) {
+            const int ol = c / CPR, kc = (c - ol * CPR) * 8;
+            const int o = o_base + ol;
+            // kc < rank <= rank_pad (a multiple of 16): the chunk lies in the
+            // row, and past the rank it holds the pool's zero padding
+            const uint4 w = (o < hj && kc < rank) ? ld16(Bn + (int64_t)o * g.rank_pad + kc)
+                                                   : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(&bs[ol][kc]) = w;
         }
+        __syncthreads();
+        staged = slot;
+    };
+
+    // One segment: multiply with the rows loaded into (yv, vf) while the rows
+    // of the next segment of the group load into (yn, vn).
+    auto step = [&](int si, Seg sd, float4 (&yv)[8], float4 (&vr)[2 * NK],
+                    float4 (&yn)[8], float4 (&vn)[2 * NK]) {
+        const bool act = r0 < sd.n_rows();
+        if constexpr (!kPrefetchV)
+            if (act) load_v(sd, vr);
+        stage_b(sd);
+        f32x4_t acc[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (act) {
+            // v is zero past the rank and for rows past the segment; K-steps
+            // past the rank multiply zeros and leave acc unchanged.
+            const int rank = sd.rank(j);
+            const bool row_ok = r0 + li < sd.n_rows();
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+                const int kk = 32 * ks + 8 * lg;
+                const float4 a = vr[2 * ks], b = vr[2 * ks + 1];
+                const float t[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float f[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) f[m] = (row_ok && kk + m < rank) ? t[m] : 0.f;
+                uint4 vhi, vlo;
+                split_f32x8(f, vhi, vlo);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const uint4 bv =
+                        *reinterpret_cast<const uint4 *>(&bs[16 * s + li][32 * ks + 8 * lg]);
+                    acc[s] = mfma16x16x32(bv, vhi, acc[s]);
+                    acc[s] = mfma16x16x32(bv, vlo, acc[s]);
+                }
+            }
+        }
+        if (si + 1 < s_last) {
+            const Seg nx = load_seg(r.seg, si + 1);
+            if (r0 < nx.n_rows()) load_rows(nx, yn, vn);
+        }
+        if (act) {
+            // d of (row li, columns 16 s + 4 lg ..) -> LDS -> the y layout.
+            // The first barrier keeps the previous segment's reads of dt
+            // ahead of these writes.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                float4 d;
+                d.x = acc[s][0];
+                d.y = acc[s][1];
+                d.z = acc[s][2];
+                d.w = acc[s][3];
+                *reinterpret_cast<float4 *>(&dt[wave][li][16 * s + 4 * lg]) = d;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float *yb = y_base(sd);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float4 d = *reinterpret_cast<const float4 *>(
+                    &dt[wave][2 * q + (lane >> 5)][4 * (lane & 31)]);
+                float4 o = yv[q];
+                o.x += d.x;
+                o.y += d.y;
+                o.z += d.z;
+                o.w += d.w;
+                if (yc_ok && y_row(q) < sd.n_rows())
+                    *reinterpret_cast<float4 *>(yb + (int64_t)y_row(q) * ldy) = o;
+            }
+        }
+    };
+
+    // Two register sets alternate, so no set is copied while its loads are
+    // in flight.
+    float4 ya[8], yb[8];
+    float4 va[2 * NK], vb[2 * NK];
+    {
+        const Seg sd = load_seg(r.seg, s_first);
+        if (r0 < sd.n_rows()) load_rows(sd, ya, va);
+    }
+    for (int si = s_first; si < s_last; si += 2) {
+        step(si, load_seg(r.seg, si), ya, va, yb, vb);
+        if (si + 1 >= s_last) break;
+        step(si + 1, load_seg(r.seg, si + 1), yb, vb, ya, va);
     }
 }
 
@@ -323,14 +404,29 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
 }
 
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int tiles_per_slice, const float *v,
-                              float *y, int64_t ldy, hipStream_t s)
+                              int seg_begin, int n_seg, int group, int tiles_per_slice,
+                              int max_rank, const float *v, float *y, int64_t ldy, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
-    if (blocks <= 0) return hipSuccess;
+    if (n_seg <= 0) return hipSuccess;
+    if (group < 1 || max_rank < 1 || max_rank > 256) return hipErrorInvalidValue;
+    const int64_t groups = (n_seg + group - 1) / group;
+    const int64_t blocks = groups * g.n_slices * tiles_per_slice;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_expand_mfma<kMfmaExpandCols / 16>), dim3((unsigned)blocks), dim3(256),
-                       0, s, g, p, r, seg_begin, tiles_per_slice, v, y, ldy);
+    const dim3 grid((unsigned)blocks), block(256);
+    const int seg_end = seg_begin + n_seg;
+    const int nk = (max_rank + 31) / 32;
+    if (nk <= 1)
+        hipLaunchKernelGGL(k_expand_mfma<1>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
+                           group, tiles_per_slice, v, y, ldy);
+    else if (nk <= 2)
+        hipLaunchKernelGGL(k_expand_mfma<2>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
+                           group, tiles_per_slice, v, y, ldy);
+    else if (nk <= 4)
+        hipLaunchKernelGGL(k_expand_mfma<4>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
+                           group, tiles_per_slice, v, y, ldy);
+    else
+        hipLaunchKernelGGL(k_expand_mfma<8>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
+                           group, tiles_per_slice, v, y, ldy);
     return hipGetLastError();
 }
 

@@ -222,9 +222,15 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
     }
     if (I.n_prefill_segments > 0) {
-        int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
+        // Consecutive segments share a task (and its staged B tile) while the
+        // grid still has about kExpandTargetBlocks workgroups.
+        const int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
+        const int64_t per_group = (int64_t)p->desc.n_slices * tiles;
+        const int64_t fit = (int64_t)I.n_prefill_segments * per_group / kExpandTargetBlocks;
+        const int group = (int)std::max<int64_t>(1, std::min<int64_t>(kExpandMaxGroup, fit));
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, I.n_decode_segments,
-                                          I.n_prefill_segments, tiles, v, y, ldy, s);
+                                          I.n_prefill_segments, group, tiles,
+                                          batch_max_rank(p, r), v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (prefill) launch");
     }
     return LORA_OK;

@@ -20,6 +20,11 @@ constexpr int kSubChunk = 512;                          // h_in elements per wav
 constexpr int kParts = 8;                               // interleaved h_in parts (one wave each)
 constexpr int kExpandTile = 512;                        // columns per decode expand task
 constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
+#ifndef LORA_EXPAND_BLOCKS
+#define LORA_EXPAND_BLOCKS 8192
+#endif
+constexpr int kExpandTargetBlocks = LORA_EXPAND_BLOCKS; // prefill expand grid to aim for
+constexpr int kExpandMaxGroup = 32;                     // prefill segments per expand task
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
 enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1 };
@@ -75,8 +80,8 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               int seg_begin, int n_seg, int nt_per_slice, const void *x,
                               int64_t ldx, float *v, hipStream_t s);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int tiles_per_slice, const float *v,
-                              float *y, int64_t ldy, hipStream_t s);
+                              int seg_begin, int n_seg, int group, int tiles_per_slice,
+                              int max_rank, const float *v, float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
                          int rank, int rank_pad, int h_in, hipStream_t s);
 hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,
