@@ -76,24 +76,40 @@ __device__ __forceinline__ void split_f32x8(const float (&f)[8], uint4 &hi, uint
 }
 
 constexpr int kShrinkParts = 4;     // waves of a shrink task: one K-part each
-constexpr int kShrinkNG = 2;        // 16-rank tiles per shrink task
-constexpr int kShrinkDepth = 4;     // K-steps of loads in flight per wave
+constexpr int kShrinkDepth = 3;     // K-steps of loads in flight per wave
 constexpr int kRowTiles = kPrefillSegRows / 16;
 
-template <bool FP16X>
+// Position of 16-byte chunk c of staged row `row`: an XOR swizzle that keeps
+// both the coalesced writes and the operand reads at two LDS passes per
+// 16 lanes.
+__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1) & 3); }
+
+// Shrink task: RT 16-row tiles of one prefill segment, one slice, NG 16-rank
+// tiles.  Wave w owns K-part w.  Each K-step loads the segment's x rows and
+// the tiles' A rows coalesced (four consecutive lanes read one row's 64
+// bytes), and reorders them through the wave's own LDS into the MFMA operand
+// layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
+template <bool FP16X, int NG, int RT>
 __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     LaneGeom g, PoolDev p, RoutingDev r, int seg_begin, int groups_per_slice,
     const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v)
 {
-    constexpr int NG = kShrinkNG, D = kShrinkDepth;
-    const int per_seg = g.n_slices * groups_per_slice;
+    constexpr int D = kShrinkDepth, ROWS = 16 * RT;
+    static_assert(kRowTiles % RT == 0, "row chunks tile the segment");
+    // task order within a segment: row chunk, slice, rank group
+    const int per_chunk = g.n_slices * groups_per_slice;
+    const int per_seg = per_chunk * (kRowTiles / RT);
     const int task = xcd_task(blockIdx.x, gridDim.x);
     const int si = seg_begin + task / per_seg;
     const int rem = task % per_seg;
-    const int j = rem / groups_per_slice;
-    const int grp = rem - j * groups_per_slice;
+    const int rc = rem / per_chunk;
+    const int rem2 = rem - rc * per_chunk;
+    const int j = rem2 / groups_per_slice;
+    const int grp = rem2 - j * groups_per_slice;
     const Seg sd = load_seg(r.seg, si);
-    const int n_rows = sd.n_rows();
+    const int rb = rc * ROWS;                       // first segment row of the task
+    const int n_rows = sd.n_rows() - rb;            // rows of the task, if positive
+    if (n_rows <= 0) return;
     const int rank = sd.rank(j);
     const int ntiles = (rank + 15) / 16;
     const int t0 = grp * NG;
@@ -101,97 +117,133 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     const int nt_here = min(NG, ntiles - t0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int li = lane & 15, lg = lane >> 4;
-    const int n_rt = (n_rows + 15) / 16;
+    const int q = lane & 3, a = lane >> 2;          // load layout: row a, chunk q
+    const int li = lane & 15, lg = lane >> 4;       // operand layout: row li, chunk lg
 
-    // Operand rows of this lane: x row 16*rt + li (rows past the segment read
-    // row 0 and are zeroed), A row 16*(t0+nt) + li (inside rank_pad).
-    const uint16_t *xr[kRowTiles];
-    bool xok[kRowTiles];
+    // Row pointers of the load layout.  Rows past the segment read its last
+    // row and A rows past rank_pad the last padded row: their products only
+    // reach outputs that are not stored.
+    const uint16_t *xr[RT];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-        const int row = 16 * rt + li;
-        xok[rt] = row < n_rows;
-        xr[rt] = x + (int64_t)(sd.first_row() + (xok[rt] ? row : 0)) * ldx;
-    }
+    for (int i = 0; i < RT; ++i)
+        xr[i] = x + (int64_t)(sd.first_row() + rb + min(16 * i + a, n_rows - 1)) * ldx;
+    const uint16_t *a_slice =
+        p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
     const uint16_t *ar[NG];
 #pragma unroll
-    for (int nt = 0; nt < NG; ++nt)
-        ar[nt] = p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride +
-                 ((int64_t)j * g.rank_pad + 16 * (t0 + min(nt, nt_here - 1)) + li) * g.h_in;
+    for (int i = 0; i < NG; ++i)
+        ar[i] = a_slice + (int64_t)min(16 * (t0 + i) + a, g.rank_pad - 1) * g.h_in;
 
-    f32x4_t acc[kRowTiles][NG];
+    __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][4];   // per wave: x rows, then A rows
+    uint4(*const lw)[4] = lds[wave];
+
+    f32x4_t acc[RT][NG];
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NG; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // K-steps wave, wave + 4, ...; loads run kShrinkDepth steps ahead.  The
     // loop is branch-free so the loads stay in flight: every load has a valid
-    // (clamped) address, and rows past the segment, K-steps past h_in and the
-    // padding steps that round a wave's count up to a multiple of the depth
-    // are multiplied as zeros.
+    // (clamped) address, and K-steps past h_in and the padding steps that
+    // round a wave's count up to a multiple of the depth multiply zeros.
     const int n_ks = (g.h_in + 31) / 32;
     const int my_steps = (n_ks - wave + kShrinkParts - 1) / kShrinkParts;
-    uint4 xs[D][kRowTiles], as[D][NG];
+    uint4 xs[D][RT], as[D][NG];
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    auto load = [&](uint4 (&xt)[kRowTiles], uint4 (&at)[NG], int step) {
-        const int e = min((wave + kShrinkParts * step) * 32 + lg * 8, g.h_in - 8);
+    auto load = [&](uint4 (&xt)[RT], uint4 (&at)[NG], int step) {
+        const int e = min((wave + kShrinkParts * step) * 32 + 8 * q, g.h_in - 8);
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) xt[rt] = ld16(xr[rt] + e);
+        for (int i = 0; i < RT; ++i) xt[i] = ld16(xr[i] + e);
 #pragma unroll
-        for (int nt = 0; nt < NG; ++nt) at[nt] = ld16(ar[nt] + e);
+        for (int i = 0; i < NG; ++i) at[i] = ld16(ar[i] + e);
     };
-    auto mma = [&](const uint4 (&xt)[kRowTiles], const uint4 (&at)[NG], int step) {
-        const bool e_ok = (wave + kShrinkParts * step) * 32 + lg * 8 < g.h_in;
+    auto mma = [&](const uint4 (&xt)[RT], const uint4 (&at)[NG], int step) {
+        // chunks past h_in are staged as zeros, in both operands
+        const bool e_ok = (wave + kShrinkParts * step) * 32 + 8 * q < g.h_in;
+        auto keep = [&](uint4 w) {   // by value: a select between lvalues spills
+            return e_ok ? w : make_uint4(0, 0, 0, 0);
+        };
 #pragma unroll
-        for (int rt = 0; rt < kRowTiles; ++rt) {
-            const uint4 xv = (e_ok && xok[rt]) ? xt[rt] : zero;
+        for (int i = 0; i < RT; ++i) lw[16 * i + a][chunk_pos(a, q)] = keep(xt[i]);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) lw[16 * (RT + i) + a][chunk_pos(a, q)] = keep(at[i]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint4 af[NG];
+#pragma unroll
+        for (int nt = 0; nt < NG; ++nt) af[nt] = lw[16 * (RT + nt) + li][chunk_pos(li, lg)];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint4 xv = lw[16 * rt + li][chunk_pos(li, lg)];
             uint4 xhi = xv, xlo = zero;
             if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
 #pragma unroll
             for (int nt = 0; nt < NG; ++nt) {
-                const uint4 av = e_ok ? at[nt] : zero;
-                acc[rt][nt] = mfma16x16x32(av, xhi, acc[rt][nt]);
-                if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(av, xlo, acc[rt][nt]);
+                acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
+                if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
             }
         }
+        // the next step's writes stay behind these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
+    // The scheduling fences keep every load group in source order, in the
+    // first fill as in the loop, and each refill after the step that reads
+    // the registers it overwrites.  The loads of a pass are then consumed in
+    // the next pass and stay in flight across the loop's back edge.
 #pragma unroll
-    for (int s = 0; s < D; ++s) load(xs[s], as[s], s);
+    for (int s = 0; s < D; ++s) {
+        load(xs[s], as[s], s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int base = 0; base < my_steps; base += D) {
 #pragma unroll
         for (int s = 0; s < D; ++s) {
             mma(xs[s], as[s], base + s);
+            __builtin_amdgcn_sched_barrier(0);
             load(xs[s], as[s], base + s + D);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // u = (S0 + S1) + (S2 + S3) through LDS.  Lane l holds, per (rt, nt),
-    // u^T[rank 16*nt + 4*lg + i][row 16*rt + li].
-    __shared__ float red[kShrinkParts][kPrefillSegRows][NG * 16];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NG; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                red[wave][16 * rt + li][16 * nt + 4 * lg + i] = acc[rt][nt][i];
-    __syncthreads();
+    // u = (S0 + S1) + (S2 + S3), one 16-rank tile at a time through the
+    // staging LDS.  Lane l holds, per (rt, nt),
+    // u^T[rank 16 nt + 4 lg + i][row 16 rt + li].
+    static_assert(sizeof(lds) >= kShrinkParts * ROWS * 16 * sizeof(float),
+                  "reduction tile fits the staging LDS");
+    float(*const red)[ROWS][16] = reinterpret_cast<float(*)[ROWS][16]>(&lds[0][0][0]);
     const float scale = p.scale[sd.slot() * kMetaStride + j];
-    constexpr int kOut = kPrefillSegRows * NG * 16;      // outputs of the task
-    for (int o = threadIdx.x * 4; o < kOut; o += 64 * kShrinkParts * 4) {
-        const int row = o / (NG * 16);
-        const int k = o % (NG * 16);
-        if (row < n_rows && k < nt_here * 16) {
+    static_assert(kShrinkParts == 4, "the combine below adds four parts");
+    const int orow = threadIdx.x >> 2, ok4 = (threadIdx.x & 3) * 4;
+    float *const vrow =
+        v + (int64_t)(sd.v_row() + rb + orow) * g.v_stride + j * g.rank_pad + 16 * t0 + ok4;
+#pragma unroll
+    for (int nt = 0; nt < NG; ++nt) {
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float4 d;
+            d.x = acc[rt][nt][0];
+            d.y = acc[rt][nt][1];
+            d.z = acc[rt][nt][2];
+            d.w = acc[rt][nt][3];
+            *reinterpret_cast<float4 *>(&red[wave][16 * rt + li][4 * lg]) = d;
+        }
+        __syncthreads();
+        if (orow < n_rows && orow < ROWS && nt < nt_here) {
             float4 u;
             float *uf = &u.x;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                uf[i] = scale * ((red[0][row][k + i] + red[1][row][k + i]) +
-                                 (red[2][row][k + i] + red[3][row][k + i]));
-            *reinterpret_cast<float4 *>(v + (int64_t)(sd.v_row() + row) * g.v_stride +
-                                        j * g.rank_pad + 16 * t0 + k) = u;
+            for (int i = 0; i < 4; ++i) {
+                float t[kShrinkParts];
+#pragma unroll
+                for (int w = 0; w < kShrinkParts; ++w) t[w] = red[w][orow][ok4 + i];
+                uf[i] = scale * ((t[0] + t[1]) + (t[2] + t[3]));
+            }
+            *reinterpret_cast<float4 *>(vrow + 16 * nt) = u;
         }
     }
 }
@@ -384,22 +436,55 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
 
 }  // namespace
 
+template <int NG, int RT>
+static void launch_shrink_t(bool fp16, dim3 grid, hipStream_t s, const LaneGeom &g,
+                            const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
+                            const uint16_t *x, int64_t ldx, float *v)
+{
+    const dim3 block(64 * kShrinkParts);
+    if (fp16)
+        hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT>), grid, block, 0, s, g, p, r, seg_begin,
+                           groups, x, ldx, v);
+    else
+        hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT>), grid, block, 0, s, g, p, r, seg_begin,
+                           groups, x, ldx, v);
+}
+
+template <int NG>
+static void launch_shrink_ng(int rt, bool fp16, dim3 grid, hipStream_t s, const LaneGeom &g,
+                             const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
+                             const uint16_t *x, int64_t ldx, float *v)
+{
+    if (rt == 1) launch_shrink_t<NG, 1>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+    else if (rt == 2) launch_shrink_t<NG, 2>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+    else launch_shrink_t<NG, 4>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+}
+
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int seg_begin, int n_seg, int nt_per_slice, const void *x,
                               int64_t ldx, float *v, hipStream_t s)
 {
-    const int groups = (nt_per_slice + kShrinkNG - 1) / kShrinkNG;
-    const int64_t blocks = (int64_t)n_seg * g.n_slices * groups;
-    if (blocks <= 0) return hipSuccess;
+    if (n_seg <= 0) return hipSuccess;
+    // Task shape: whole segments and up to 4 rank tiles (x and A read the
+    // fewest times), made finer -- rows first, then ranks -- while the grid
+    // is under kShrinkMinBlocks workgroups.
+    int ng = nt_per_slice <= 1 ? 1 : nt_per_slice <= 2 ? 2 : 4, rt = kRowTiles;
+    auto blocks_of = [&](int ng_, int rt_) {
+        return (int64_t)n_seg * g.n_slices * ((nt_per_slice + ng_ - 1) / ng_) * (kRowTiles / rt_);
+    };
+    while (blocks_of(ng, rt) < kShrinkMinBlocks && (ng > 1 || rt > 1)) {
+        if (rt > 1 && (rt >= ng || ng == 1)) rt /= 2;
+        else ng /= 2;
+    }
+    const int groups = (nt_per_slice + ng - 1) / ng;
+    const int64_t blocks = blocks_of(ng, rt);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
-    const dim3 grid((unsigned)blocks), block(64 * kShrinkParts);
-    if (g.x_fp16)
-        hipLaunchKernelGGL(k_shrink_mfma<true>, grid, block, 0, s, g, p, r, seg_begin, groups, xp,
-                           ldx, v);
-    else
-        hipLaunchKernelGGL(k_shrink_mfma<false>, grid, block, 0, s, g, p, r, seg_begin, groups, xp,
-                           ldx, v);
+    const dim3 grid((unsigned)blocks);
+    const bool fp16 = g.x_fp16 != 0;
+    if (ng == 1) launch_shrink_ng<1>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+    else if (ng == 2) launch_shrink_ng<2>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+    else launch_shrink_ng<4>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
     return hipGetLastError();
 }
 

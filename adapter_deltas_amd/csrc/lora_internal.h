@@ -25,6 +25,7 @@ constexpr int kMfmaExpandCols = 128;                    // columns per prefill e
 #endif
 constexpr int kExpandTargetBlocks = LORA_EXPAND_BLOCKS; // prefill expand grid to aim for
 constexpr int kExpandMaxGroup = 32;                     // prefill segments per expand task
+constexpr int kShrinkMinBlocks = 128;                   // prefill shrink grid below which tasks shrink
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
 enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1 };
