@@ -1,5 +1,4 @@
-// Decode-path device code shared by the standalone shrink/expand kernels and
-// the fused delta kernel, so both run the same arithmetic in the same order.
+// Decode-path device code of the GEMV shrink and expand kernels.
 //
 // Shrink order for u[k] = sum_i A[k][i] x[i] over h_in:
 //   h_in is cut into sub-chunks of kSubChunk = 512 elements; sub-chunk q
@@ -20,7 +19,7 @@
 
 namespace lora {
 
-constexpr int kExpandRows = 4;       // segment rows per expanding wave
+constexpr int kExpandRows = 2;       // segment rows per expanding wave
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -203,14 +202,15 @@ __device__ __forceinline__ void widen_bf16x8(uint4 b, float (&f)[8])
 }
 
 // Expand of kExpandRows rows of a decode segment over 8 columns per lane.
-//   trow[c]  token row of y for row c (valid for every c)
-//   n_rows   rows of the 4 that belong to the segment (1..4)
+//   yp[c]    y of segment row c at this lane's columns (valid for every c)
+//   n_rows   rows of the kExpandRows that belong to the segment (may exceed
+//            kExpandRows; rows from kExpandRows on are not this wave's)
 //   bt       B^T of the slice at this lane's columns: bt[k * hj]
 //   wait     called once, after the loads of y and of the first B block are
 //            issued and before v is first read
 //   vsrc     vsrc(c, kb, out) fills out[0..8) with v of row c, ranks kb..kb+7
 //            (ranks at or past `rank` must come back as zero)
-// y[trow[c]][cols] += sum_k B[k] v[c][k] for c < n_rows, when store is true.
+// y[row c][cols] += sum_k B[k] v[c][k] for c < n_rows, when store is true.
 template <class Wait, class VSrc>
 __device__ __forceinline__ void expand_rows(float *const (&yp)[kExpandRows], int n_rows,
                                             const uint16_t *bt, int hj, int rank, bool store,

@@ -84,13 +84,18 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
     const int o0 = tile * kExpandTile + lane * 8;
     const bool col_ok = o0 < hj;
     const int oc = col_ok ? o0 : hj - 8;
-    static_assert(kExpandRows == 4 && kExpandWaves == 2, "row selection below");
-    const int trow[C] = {wave ? sd.row<4>() : sd.row<0>(), wave ? sd.row<5>() : sd.row<1>(),
-                         wave ? sd.row<6>() : sd.row<2>(), wave ? sd.row<7>() : sd.row<3>()};
-    float *const yp[C] = {y + (int64_t)trow[0] * ldy + g.col_off[j] + oc,
-                          y + (int64_t)trow[1] * ldy + g.col_off[j] + oc,
-                          y + (int64_t)trow[2] * ldy + g.col_off[j] + oc,
-                          y + (int64_t)trow[3] * ldy + g.col_off[j] + oc};
+    // token rows c0 .. c0 + C - 1 of the segment (wave-uniform selection)
+    const int all[kDecodeSegRows] = {sd.row<0>(), sd.row<1>(), sd.row<2>(), sd.row<3>(),
+                                     sd.row<4>(), sd.row<5>(), sd.row<6>(), sd.row<7>()};
+    float *yp[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        int t = all[c];
+#pragma unroll
+        for (int w = 1; w < kExpandWaves; ++w)
+            if (wave == w) t = all[w * C + c];
+        yp[c] = y + (int64_t)t * ldy + g.col_off[j] + oc;
+    }
     const uint16_t *bt =
         p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j] + oc;
     // v is read-only here and the same for every lane: constant-space reads
