@@ -19,6 +19,7 @@ MAX_SLICES = 4
 MAX_RANK = 256
 DECODE_SEG_ROWS = 8
 SEG_WORDS = 16
+GATHER_MIN_RANK = 128         # LORA_GATHER_MIN_RANK
 PREFILL_SEG_ROWS = 64
 
 # every symbol include/lora.h declares
@@ -47,7 +48,8 @@ class LaneDesc(ctypes.Structure):
 class RoutingInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_tokens", "n_active", "n_segments", "n_decode_segments",
-        "n_prefill_segments", "n_distinct", "n_admitted_seqs", "n_seqs")]
+        "n_prefill_segments", "n_distinct", "n_admitted_seqs", "n_seqs",
+        "n_gather_segments")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -89,7 +89,7 @@ __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1
 // the tiles' A rows coalesced (four consecutive lanes read one row's 64
 // bytes), and reorders them through the wave's own LDS into the MFMA operand
 // layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
-template <bool FP16X, int NG, int RT>
+template <bool FP16X, int NG, int RT, bool GATHER>
 __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     LaneGeom g, PoolDev p, RoutingDev r, int seg_begin, int groups_per_slice,
     const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v)
@@ -125,8 +125,11 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     // reach outputs that are not stored.
     const uint16_t *xr[RT];
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
-        xr[i] = x + (int64_t)(sd.first_row() + rb + min(16 * i + a, n_rows - 1)) * ldx;
+    for (int i = 0; i < RT; ++i) {
+        const int sr = rb + min(16 * i + a, n_rows - 1);       // segment row
+        const int tok = GATHER ? r.rows[sd.v_row() + sr] : sd.first_row() + sr;
+        xr[i] = x + (int64_t)tok * ldx;
+    }
     const uint16_t *a_slice =
         p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
     const uint16_t *ar[NG];
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
 // the slot's rank) are staged in LDS once and kept while the slot stays the
 // same, so a group that covers one prompt reads its B tile from HBM once.
 // Wave w multiplies rows 16w .. 16w + 15 of each segment.
-template <int NK>
+template <int NK, bool GATHER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
 void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
                                                       int seg_begin, int seg_end, int group,
@@ -292,12 +295,24 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
 
     // y of this wave's 16 rows of a segment, two whole 128-column rows per
     // instruction: lane l takes row 2q + l/32, columns 4 * (l % 32) .. + 3.
-    // Loads are branch-free: rows past the segment read its last row and
+    // Loads are branch-free: rows past the segment read one of its rows and
     // columns past the slice its last four columns (h_out is a multiple of 8);
     // only the stores are masked.
     auto y_row = [&](int q) { return r0 + 2 * q + (lane >> 5); };
-    auto y_base = [&](Seg sd) {
-        return y + (int64_t)sd.first_row() * ldy + g.col_off[j] + min(yc, hj - 4);
+    const int ycol = g.col_off[j] + min(yc, hj - 4);
+    // token row of this lane's y row q of segment sd
+    auto y_tok = [&](Seg sd, int q) -> int {
+        const int last = sd.n_rows() - 1;
+        if constexpr (GATHER) {
+            // the wave's 16 entries of the row table, through scalar loads
+            // (entries past the segment are read but not used)
+            typedef const __attribute__((address_space(4))) int32_t cint;
+            cint *t = (cint *)(r.rows + sd.v_row() + r0);
+            const int e0 = t[2 * q], e1 = t[2 * q + 1], first = t[0];
+            return y_row(q) <= last ? ((lane >> 5) ? e1 : e0) : first;
+        } else {
+            return sd.first_row() + min(y_row(q), last);
+        }
     };
     // v of row r0 + li, ranks 32 ks + 8 lg .. + 7 (raw; the rank and row
     // masks are applied when the rows are used).  The addresses stay inside
@@ -318,11 +333,9 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     constexpr bool kPrefetchV = NK <= 2;
     auto load_rows = [&](Seg sd, float4 (&yv)[8], float4 (&vr)[2 * NK]) {
         if constexpr (kPrefetchV) load_v(sd, vr);
-        const float *yb = y_base(sd);
-        const int last = sd.n_rows() - 1;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            yv[q] = *reinterpret_cast<const float4 *>(yb + (int64_t)min(y_row(q), last) * ldy);
+            yv[q] = *reinterpret_cast<const float4 *>(y + (int64_t)y_tok(sd, q) * ldy + ycol);
     };
 
     int staged = 0;                               // slot whose B tile is in bs
@@ -403,7 +416,6 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float *yb = y_base(sd);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const float4 d = *reinterpret_cast<const float4 *>(
@@ -414,7 +426,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
                 o.z += d.z;
                 o.w += d.w;
                 if (yc_ok && y_row(q) < sd.n_rows())
-                    *reinterpret_cast<float4 *>(yb + (int64_t)y_row(q) * ldy) = o;
+                    *reinterpret_cast<float4 *>(y + (int64_t)y_tok(sd, q) * ldy + ycol) = o;
             }
         }
     };
@@ -437,32 +449,41 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
 }  // namespace
 
 template <int NG, int RT>
-static void launch_shrink_t(bool fp16, dim3 grid, hipStream_t s, const LaneGeom &g,
+static void launch_shrink_t(bool fp16, bool gather, dim3 grid, hipStream_t s, const LaneGeom &g,
                             const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
                             const uint16_t *x, int64_t ldx, float *v)
 {
     const dim3 block(64 * kShrinkParts);
-    if (fp16)
-        hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT>), grid, block, 0, s, g, p, r, seg_begin,
-                           groups, x, ldx, v);
+    if (fp16 && gather)
+        hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, true>), grid, block, 0, s, g, p, r,
+                           seg_begin, groups, x, ldx, v);
+    else if (fp16)
+        hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, false>), grid, block, 0, s, g, p, r,
+                           seg_begin, groups, x, ldx, v);
+    else if (gather)
+        hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, true>), grid, block, 0, s, g, p, r,
+                           seg_begin, groups, x, ldx, v);
     else
-        hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT>), grid, block, 0, s, g, p, r, seg_begin,
-                           groups, x, ldx, v);
+        hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, false>), grid, block, 0, s, g, p, r,
+                           seg_begin, groups, x, ldx, v);
 }
 
 template <int NG>
-static void launch_shrink_ng(int rt, bool fp16, dim3 grid, hipStream_t s, const LaneGeom &g,
-                             const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
-                             const uint16_t *x, int64_t ldx, float *v)
+static void launch_shrink_ng(int rt, bool fp16, bool gather, dim3 grid, hipStream_t s,
+                             const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                             int seg_begin, int groups, const uint16_t *x, int64_t ldx, float *v)
 {
-    if (rt == 1) launch_shrink_t<NG, 1>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
-    else if (rt == 2) launch_shrink_t<NG, 2>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
-    else launch_shrink_t<NG, 4>(fp16, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+    if (rt == 1)
+        launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+    else if (rt == 2)
+        launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+    else
+        launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
 }
 
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int nt_per_slice, const void *x,
-                              int64_t ldx, float *v, hipStream_t s)
+                              bool gather, int seg_begin, int n_seg, int nt_per_slice,
+                              const void *x, int64_t ldx, float *v, hipStream_t s)
 {
     if (n_seg <= 0) return hipSuccess;
     // Task shape: whole segments and up to 4 rank tiles (x and A read the
@@ -482,36 +503,53 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
     const uint16_t *xp = static_cast<const uint16_t *>(x);
     const dim3 grid((unsigned)blocks);
     const bool fp16 = g.x_fp16 != 0;
-    if (ng == 1) launch_shrink_ng<1>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
-    else if (ng == 2) launch_shrink_ng<2>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
-    else launch_shrink_ng<4>(rt, fp16, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+    if (ng == 1)
+        launch_shrink_ng<1>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+    else if (ng == 2)
+        launch_shrink_ng<2>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+    else
+        launch_shrink_ng<4>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
     return hipGetLastError();
 }
 
+template <int NK>
+static void launch_expand_nk(bool gather, dim3 grid, hipStream_t s, const LaneGeom &g,
+                             const PoolDev &p, const RoutingDev &r, int seg_begin, int seg_end,
+                             int group, int tiles_per_slice, const float *v, float *y, int64_t ldy)
+{
+    if (gather)
+        hipLaunchKernelGGL((k_expand_mfma<NK, true>), grid, dim3(256), 0, s, g, p, r, seg_begin,
+                           seg_end, group, tiles_per_slice, v, y, ldy);
+    else
+        hipLaunchKernelGGL((k_expand_mfma<NK, false>), grid, dim3(256), 0, s, g, p, r, seg_begin,
+                           seg_end, group, tiles_per_slice, v, y, ldy);
+}
+
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int group, int tiles_per_slice,
-                              int max_rank, const float *v, float *y, int64_t ldy, hipStream_t s)
+                              bool gather, int seg_begin, int n_seg, int group,
+                              int tiles_per_slice, int max_rank, const float *v, float *y,
+                              int64_t ldy, hipStream_t s)
 {
     if (n_seg <= 0) return hipSuccess;
     if (group < 1 || max_rank < 1 || max_rank > 256) return hipErrorInvalidValue;
     const int64_t groups = (n_seg + group - 1) / group;
     const int64_t blocks = groups * g.n_slices * tiles_per_slice;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks), block(256);
+    const dim3 grid((unsigned)blocks);
     const int seg_end = seg_begin + n_seg;
     const int nk = (max_rank + 31) / 32;
     if (nk <= 1)
-        hipLaunchKernelGGL(k_expand_mfma<1>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
-                           group, tiles_per_slice, v, y, ldy);
+        launch_expand_nk<1>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
+                            v, y, ldy);
     else if (nk <= 2)
-        hipLaunchKernelGGL(k_expand_mfma<2>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
-                           group, tiles_per_slice, v, y, ldy);
+        launch_expand_nk<2>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
+                            v, y, ldy);
     else if (nk <= 4)
-        hipLaunchKernelGGL(k_expand_mfma<4>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
-                           group, tiles_per_slice, v, y, ldy);
+        launch_expand_nk<4>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
+                            v, y, ldy);
     else
-        hipLaunchKernelGGL(k_expand_mfma<8>, grid, block, 0, s, g, p, r, seg_begin, seg_end,
-                           group, tiles_per_slice, v, y, ldy);
+        launch_expand_nk<8>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
+                            v, y, ldy);
     return hipGetLastError();
 }
 

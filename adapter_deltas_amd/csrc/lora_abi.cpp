@@ -125,7 +125,7 @@ PoolDev pool_dev(const lora_pool *p)
 
 RoutingDev routing_dev(const lora_routing *r)
 {
-    return RoutingDev{r->dev + r->off_seg, r->dev + r->off_tok};
+    return RoutingDev{r->dev + r->off_seg, r->dev + r->off_tok, r->dev + r->off_row};
 }
 
 // Largest rank over the routing's distinct slots and the lane's slices.
@@ -199,11 +199,17 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
         hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
+    const int nt = (kmax + 15) / 16;
     if (I.n_prefill_segments > 0) {
-        int nt = (kmax + 15) / 16;
-        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, I.n_decode_segments,
+        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, false, I.n_decode_segments,
                                           I.n_prefill_segments, nt, x, ldx, v, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill) launch");
+    }
+    if (I.n_gather_segments > 0) {
+        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true,
+                                          I.n_decode_segments + I.n_prefill_segments,
+                                          I.n_gather_segments, nt, x, ldx, v, s);
+        if (e != hipSuccess) return hip_fail(e, "shrink (gather) launch");
     }
     return LORA_OK;
 }
@@ -221,17 +227,27 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
     }
+    // Consecutive segments share a task (and its staged B tile) while the
+    // grid still has about kExpandTargetBlocks workgroups.
+    const int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
+    const int64_t per_group = (int64_t)p->desc.n_slices * tiles;
+    auto group_for = [&](int n) {
+        const int64_t fit = (int64_t)n * per_group / kExpandTargetBlocks;
+        return (int)std::max<int64_t>(1, std::min<int64_t>(kExpandMaxGroup, fit));
+    };
+    const int kmax = batch_max_rank(p, r);
     if (I.n_prefill_segments > 0) {
-        // Consecutive segments share a task (and its staged B tile) while the
-        // grid still has about kExpandTargetBlocks workgroups.
-        const int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
-        const int64_t per_group = (int64_t)p->desc.n_slices * tiles;
-        const int64_t fit = (int64_t)I.n_prefill_segments * per_group / kExpandTargetBlocks;
-        const int group = (int)std::max<int64_t>(1, std::min<int64_t>(kExpandMaxGroup, fit));
-        hipError_t e = launch_expand_mfma(p->geom, pd, rd, I.n_decode_segments,
-                                          I.n_prefill_segments, group, tiles,
-                                          batch_max_rank(p, r), v, y, ldy, s);
+        hipError_t e = launch_expand_mfma(p->geom, pd, rd, false, I.n_decode_segments,
+                                          I.n_prefill_segments, group_for(I.n_prefill_segments),
+                                          tiles, kmax, v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (prefill) launch");
+    }
+    if (I.n_gather_segments > 0) {
+        hipError_t e = launch_expand_mfma(p->geom, pd, rd, true,
+                                          I.n_decode_segments + I.n_prefill_segments,
+                                          I.n_gather_segments, group_for(I.n_gather_segments),
+                                          tiles, kmax, v, y, ldy, s);
+        if (e != hipSuccess) return hip_fail(e, "expand (gather) launch");
     }
     return LORA_OK;
 }
@@ -319,17 +335,35 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
         }
         row0 += L;
     }
+    // Decode rows of an adapter with a slice rank >= kGatherMinRank take the
+    // matrix-core path in gather segments; the others the GEMV path.
+    auto gathered = [&](int32_t s) {
+        int32_t m = 0;
+        for (int j = 0; j < kMetaStride; ++j) m = std::max(m, ranks(s, j));
+        return m >= kGatherMinRank;
+    };
+    // Active rows (the rows of v): GEMV decode rows by slot in order of first
+    // appearance, then prefill rows, then gathered decode rows by slot.
     std::vector<int32_t> start((size_t)max_slots + 1, 0);
+    int64_t n_dec_gemv = 0;
     {
-        int32_t acc = 0;
-        for (int32_t s : slot_order) {
-            start[s] = acc;
-            acc += count[s];
-        }
+        int64_t acc = 0;
+        for (int32_t s : slot_order)
+            if (!gathered(s)) {
+                start[s] = (int32_t)acc;
+                acc += count[s];
+            }
+        n_dec_gemv = acc;
+        acc += n_pre;
+        for (int32_t s : slot_order)
+            if (gathered(s)) {
+                start[s] = (int32_t)acc;
+                acc += count[s];
+            }
     }
     pl.rows.assign((size_t)(n_dec + n_pre), 0);
     pl.seg.clear();
-    // decode rows: grouped by slot, token order within a slot, chunks of kDecodeSegRows
+    // decode rows: token order within a slot; GEMV slots in chunks of kDecodeSegRows
     {
         std::vector<int32_t> fill = start;
         row0 = 0;
@@ -340,17 +374,18 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
             row0 += L;
         }
         for (int32_t s : slot_order)
-            for (int32_t b = 0; b < count[s]; b += kDecodeSegRows) {
-                const int32_t n = std::min(kDecodeSegRows, count[s] - b);
-                push_seg(pl.seg, s, start[s] + b, n, kSegDecode, ranks);
-                for (int32_t c = 0; c < kDecodeSegRows; ++c)
-                    pl.seg.push_back(pl.rows[(size_t)(start[s] + b + std::min(c, n - 1))]);
-            }
+            if (!gathered(s))
+                for (int32_t b = 0; b < count[s]; b += kDecodeSegRows) {
+                    const int32_t n = std::min(kDecodeSegRows, count[s] - b);
+                    push_seg(pl.seg, s, start[s] + b, n, kSegDecode, ranks);
+                    for (int32_t c = 0; c < kDecodeSegRows; ++c)
+                        pl.seg.push_back(pl.rows[(size_t)(start[s] + b + std::min(c, n - 1))]);
+                }
     }
     const int32_t n_dec_seg = (int32_t)(pl.seg.size() / kSegWords);
     // prefill sequences: contiguous chunks of kPrefillSegRows rows, one slot each
     {
-        int64_t pos = n_dec;
+        int64_t pos = n_dec_gemv;
         row0 = 0;
         for (int i = 0; i < n_seq; ++i) {
             const int32_t L = seq_len[i], s = seq_slot[i];
@@ -365,12 +400,22 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
             row0 += L;
         }
     }
+    const int32_t n_pre_seg = (int32_t)(pl.seg.size() / kSegWords) - n_dec_seg;
+    // gathered decode rows: chunks of kPrefillSegRows rows of one slot
+    for (int32_t s : slot_order)
+        if (gathered(s))
+            for (int32_t b = 0; b < count[s]; b += kPrefillSegRows) {
+                const int32_t n = std::min(kPrefillSegRows, count[s] - b);
+                push_seg(pl.seg, s, start[s] + b, n, kSegGather, ranks);
+                for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
+            }
     const int32_t n_seg = (int32_t)(pl.seg.size() / kSegWords);
     pl.info.n_tokens = (int32_t)T;
     pl.info.n_active = (int32_t)(n_dec + n_pre);
     pl.info.n_segments = n_seg;
     pl.info.n_decode_segments = n_dec_seg;
-    pl.info.n_prefill_segments = n_seg - n_dec_seg;
+    pl.info.n_prefill_segments = n_pre_seg;
+    pl.info.n_gather_segments = n_seg - n_dec_seg - n_pre_seg;
     pl.info.n_distinct = (int32_t)distinct_ids.size();
     pl.info.n_seqs = n_seq;
     int32_t na = 0;

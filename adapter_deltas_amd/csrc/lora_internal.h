@@ -28,14 +28,16 @@ constexpr int kExpandMaxGroup = 32;                     // prefill segments per 
 constexpr int kShrinkMinBlocks = 128;                   // prefill shrink grid below which tasks shrink
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
-enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1 };
+enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1, kSegGather = 2 };
+constexpr int kGatherMinRank = LORA_GATHER_MIN_RANK;
 
 // A segment descriptor is kSegWords int32 words:
 //   [0] slot  [1] first active row (row of v)  [2] rows  [3] kind
 //   [4..7]  rank of slices 0..3 in the pool the routing was built against
 //   [8..15] decode: token row of each segment row (the last one repeated
 //           past the segment's rows); prefill: [8] = first token row, the
-//           segment's rows being consecutive.
+//           segment's rows being consecutive; gather: unused, the token row
+//           of segment row r being the row table's entry [1] + r.
 constexpr int kSegWords = 16;
 static_assert(kDecodeSegRows == 8, "descriptor holds 8 token rows");
 
@@ -68,6 +70,7 @@ struct PoolDev {
 struct RoutingDev {
     const int32_t *seg;       // kSegWords words per segment
     const int32_t *tok_slot;  // slot per token row
+    const int32_t *rows;      // token row of each active row
 };
 
 // ---- launchers (kernels_*.hip) ----
@@ -78,11 +81,12 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
                               int n_seg, int tiles_per_slice, const float *v, float *y,
                               int64_t ldy, hipStream_t s);
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int nt_per_slice, const void *x,
-                              int64_t ldx, float *v, hipStream_t s);
+                              bool gather, int seg_begin, int n_seg, int nt_per_slice,
+                              const void *x, int64_t ldx, float *v, hipStream_t s);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int seg_begin, int n_seg, int group, int tiles_per_slice,
-                              int max_rank, const float *v, float *y, int64_t ldy, hipStream_t s);
+                              bool gather, int seg_begin, int n_seg, int group,
+                              int tiles_per_slice, int max_rank, const float *v, float *y,
+                              int64_t ldy, hipStream_t s);
 hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
                          int rank, int rank_pad, int h_in, hipStream_t s);
 hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,

@@ -65,7 +65,7 @@ def call_kernels(call: str, info) -> str:
     ks = []
     if info["n_decode_segments"]:
         ks.append(f"k_{call}_gemv")
-    if info["n_prefill_segments"]:
+    if info["n_prefill_segments"] or info["n_gather_segments"]:
         ks.append(f"k_{call}_mfma")
     return f"lora_{call}: " + " + ".join(ks)
 
@@ -361,6 +361,7 @@ def main():
             "tokens": T, "active_rows": info["n_active"], "distinct_adapters": nd,
             "decode_segments": info["n_decode_segments"],
             "prefill_segments": info["n_prefill_segments"],
+            "gather_segments": info["n_gather_segments"],
             "layers_per_step": args.layers,
             "layer_buffer_bytes": layer_bytes,
             "step": "routing build + delta_apply on every lane of every layer",

@@ -88,16 +88,21 @@ typedef struct lora_routing lora_routing;  /* opaque host handle */
 typedef struct lora_routing_info {
     int32_t n_tokens;            /* rows covered by the candidate batch       */
     int32_t n_active;            /* admitted rows with an adapter (slot != 0) */
-    int32_t n_segments;          /* decode + prefill segments                 */
+    int32_t n_segments;          /* decode + prefill + gather segments        */
     int32_t n_decode_segments;   /* <= LORA_DECODE_SEG_ROWS rows, one slot    */
     int32_t n_prefill_segments;  /* <= LORA_PREFILL_SEG_ROWS rows, one slot   */
     int32_t n_distinct;          /* distinct adapters admitted (not base)     */
     int32_t n_admitted_seqs;
     int32_t n_seqs;
+    int32_t n_gather_segments;   /* <= LORA_PREFILL_SEG_ROWS rows, one slot   */
 } lora_routing_info;
 
 #define LORA_DECODE_SEG_ROWS 8
 #define LORA_PREFILL_SEG_ROWS 64
+/* Decode rows of an adapter whose largest slice rank is at least this go to
+ * gather segments and the matrix-core path; the others to decode segments
+ * and the GEMV path.  The choice depends only on the row's own adapter. */
+#define LORA_GATHER_MIN_RANK 128
 
 /* Thread-local text of the last error on this thread ("" if none). */
 const char *lora_last_error(void);
@@ -200,9 +205,13 @@ int32_t lora_routing_destroy(lora_routing *routing);
  *                   <= LORA_PREFILL_SEG_ROWS contiguous rows with one slot
  *                   (TensorFold PR #47: prompt chunks run one slot for all
  *                   their rows) and take the matrix-core path; shorter ones
- *                   are decode rows grouped by slot into segments of
- *                   <= LORA_DECODE_SEG_ROWS rows.  The choice depends only on
- *                   the sequence's own length.
+ *                   are decode rows, grouped by slot (in order of first
+ *                   appearance, token order within a slot) into segments of
+ *                   <= LORA_DECODE_SEG_ROWS rows for the GEMV path, or, for
+ *                   an adapter with a slice rank >= LORA_GATHER_MIN_RANK, into
+ *                   gather segments of <= LORA_PREFILL_SEG_ROWS rows for the
+ *                   matrix-core path.  The choice depends only on the
+ *                   sequence's own length and adapter.
  *   admitted_out    optional host uint8 [n_seq]: 1 admitted, 0 deferred
  *   n_distinct_out  optional: distinct adapters admitted
  *
@@ -231,11 +240,13 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  *   resident_rank optional [n_resident][4]: rank of each slice (0 if NULL)
  *   words_out     host int32 [words_capacity]; receives the packed tables:
  *                 16-word segments {slot, first active row, rows, kind
- *                 (0 decode, 1 prefill), rank of slices 0..3, token rows
- *                 (decode: one per row, the last repeated; prefill: the first,
- *                 rows being consecutive)} at word offsets_out[0], the token
- *                 row of each active row at offsets_out[1], and one slot per
- *                 token row at offsets_out[2]
+ *                 (0 decode, 1 prefill, 2 gather), rank of slices 0..3, token
+ *                 rows (decode: one per row, the last repeated; prefill: the
+ *                 first, rows being consecutive; gather: unused, the token
+ *                 rows being those of its active rows)} at word
+ *                 offsets_out[0], decode segments first, then prefill, then
+ *                 gather; the token row of each active row at offsets_out[1];
+ *                 and one slot per token row at offsets_out[2]
  *   offsets_out   host int32 [3]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]

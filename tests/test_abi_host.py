@@ -22,6 +22,13 @@ def m():
     return adapter_deltas_amd
 
 
+def header_define(name):
+    return int(re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read()).group(1))
+
+
+GATHER_MIN_RANK = header_define("LORA_GATHER_MIN_RANK")
+
+
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -36,6 +43,13 @@ def test_every_declared_symbol_is_exported(m):
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(_lib.EXPORTS) == names
+    # constants and the info struct mirrored by the binding
+    assert _lib.GATHER_MIN_RANK == GATHER_MIN_RANK
+    assert _lib.SEG_WORDS == 16 and _lib.DECODE_SEG_ROWS == header_define("LORA_DECODE_SEG_ROWS")
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct lora_routing_info \{(.*?)\}", text, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert [n for n, _ in _lib.RoutingInfo._fields_] == fields
 
 
 def test_validation_errors_without_device(m):
@@ -85,7 +99,7 @@ def test_plan_admission_matches_golden_and_oracle(m):
         assert p["info"]["n_distinct"] == len(c["distinct"])
 
 
-def _check_plan(p, ids, lens, resident, cap, pmin):
+def _check_plan(p, ids, lens, resident, cap, pmin, ranks=None):
     adm, _ = oracle.admit(ids, cap)
     assert list(p["admitted"]) == adm
     tok = oracle.token_adapters(ids, lens, adm)
@@ -98,6 +112,12 @@ def _check_plan(p, ids, lens, resident, cap, pmin):
     # every active row appears exactly once, in a segment of its own slot
     assert sorted(rows.tolist()) == np.nonzero(slots)[0].tolist()
     seq_of = np.repeat(np.arange(len(lens)), lens)
+    # an adapter's decode rows take gather segments iff one of its slice ranks
+    # reaches the gather threshold (a property of the adapter alone)
+    inv = {sl: i for i, sl in resident.items()}
+    big = {sl: max((ranks or {}).get(inv[sl], [0])) >= GATHER_MIN_RANK for sl in inv}
+    n_dec, n_pre = info["n_decode_segments"], info["n_prefill_segments"]
+    assert info["n_segments"] == n_dec + n_pre + info["n_gather_segments"] == len(seg)
     covered = 0
     for k, d in enumerate(seg):
         s, b, n, kind = d[:4]
@@ -108,26 +128,31 @@ def _check_plan(p, ids, lens, resident, cap, pmin):
         assert np.all(slots[r] == s)
         L = np.asarray(lens)[seq_of[r]]
         if kind == 0:
-            assert k < info["n_decode_segments"] and n <= 8
+            assert k < n_dec and n <= 8 and not big[s]
             assert np.all(L < pmin)
             assert np.all(np.diff(r) > 0)
             assert list(d[8:8 + n]) == list(r) and np.all(d[8 + n:] == r[-1])
-        else:
-            assert k >= info["n_decode_segments"] and n <= 64
+        elif kind == 1:
+            assert n_dec <= k < n_dec + n_pre and n <= 64
             assert np.all(L >= pmin)
             assert np.all(np.diff(r) == 1) and len(set(seq_of[r])) == 1
             assert d[8] == r[0]
             start = r[0] - np.concatenate([[0], np.cumsum(lens)])[seq_of[r[0]]]
             assert start % 64 == 0     # chunking depends only on the sequence
+        else:
+            assert kind == 2 and k >= n_dec + n_pre and n <= 64 and big[s]
+            assert np.all(L < pmin)
+            assert np.all(np.diff(r) > 0)
+            assert np.all(d[8:] == 0)
     assert covered == len(rows)
     # decode rows of one slot sit in consecutive segments, token order inside
-    dec = seg[:info["n_decode_segments"]]
-    for s in set(dec[:, 0].tolist()):
-        ks = np.nonzero(dec[:, 0] == s)[0]
-        assert np.all(np.diff(ks) == 1)
-        r = np.concatenate([rows[d[1]:d[1] + d[2]] for d in dec[ks]])
-        assert np.all(np.diff(r) > 0)
-        assert np.all(dec[ks][:-1, 2] == 8)
+    for part, full in ((seg[:n_dec], 8), (seg[n_dec + n_pre:], 64)):
+        for s in set(part[:, 0].tolist()):
+            ks = np.nonzero(part[:, 0] == s)[0]
+            assert np.all(np.diff(ks) == 1)
+            r = np.concatenate([rows[d[1]:d[1] + d[2]] for d in part[ks]])
+            assert np.all(np.diff(r) > 0)
+            assert np.all(part[ks][:-1, 2] == full)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -142,9 +167,9 @@ def test_plan_random_batches(m, seed):
     cap = int(rng.integers(0, n_ad + 1))
     pmin = int(rng.choice([1, 16, 64, 2**31 - 1]))
     T = max(int(np.sum(lens)), 1)
-    ranks = {i: [int(x) for x in rng.integers(1, 65, size=4)] for i in ids_pool}
+    ranks = {i: [int(x) for x in rng.integers(1, 100, size=4)] for i in ids_pool}
     p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T, resident_rank=ranks)
-    _check_plan(p, ids, lens, resident, cap, pmin)
+    _check_plan(p, ids, lens, resident, cap, pmin, ranks)
     inv = {s: i for i, s in resident.items()}
     for d in p["seg"]:
         assert list(d[4:8]) == ranks[inv[d[0]]]

@@ -18,8 +18,8 @@ MID = WorkloadSpec(
     name="mid_ragged", seed=21,
     lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
            LaneSpec("fp16_share", 1544, (264,), "fp16", tp_size=2, tp_rank=1)),
-    n_adapters=5, ranks=(3, 12, 17, 1, 100), rank_mode="list",
-    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=100,
+    n_adapters=5, ranks=(3, 12, 17, 1, 130), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=130,
     decode_rows=90, base_prob=0.2, prefill_seqs=6, prefill_len=(1, 200))
 
 
@@ -97,12 +97,16 @@ def test_small_configs_full_parity(lib, cfg, lane, mode):
 @pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
 @pytest.mark.parametrize("prefill_min_len", [64, 1, 2**31 - 1])
 def test_ragged_full_parity(lib, lane, mode, prefill_min_len):
-    """h_in = 3 sub-chunks + 8, slices 520|136|8, ranks 1..100, sequences of
+    """h_in = 3 sub-chunks + 8, slices 520|136|8, ranks 1..130, sequences of
     length 1..200 around the 64-row segment edges, both paths forced."""
     w = generate(MID, mode=mode)
     y, adm, info = run_lane(lib, w, lane, prefill_min_len=prefill_min_len)
     if prefill_min_len == 1:
         assert info["n_decode_segments"] == 0 and info["n_prefill_segments"] > 0
+        assert info["n_gather_segments"] == 0
+    else:
+        # the rank-130 adapter's decode rows take the gather (matrix-core) path
+        assert info["n_gather_segments"] > 0 and info["n_decode_segments"] > 0
     if prefill_min_len == 2**31 - 1:
         assert info["n_prefill_segments"] == 0
     check_full(w, lane, y, adm, prefill_min_len=prefill_min_len)
