@@ -72,8 +72,8 @@ def call_kernels(call: str, info) -> str:
 
 def summarize_pmc(pmc_dir: str, configs):
     """profiles/traffic.json from rocprofv3 --pmc runs: per workload and call,
-    the HBM bytes per launch, FETCH_SIZE and WRITE_SIZE each scaled by what
-    the same counter reads for a plain copy of COPY_CALIBRATION_BYTES."""
+    the mean HBM bytes per launch, FETCH_SIZE and WRITE_SIZE each scaled by
+    what the same counter reads for a plain copy of COPY_CALIBRATION_BYTES."""
     import csv
     import statistics
 
@@ -99,8 +99,10 @@ def summarize_pmc(pmc_dir: str, configs):
             names = [k for k in fetch if f"k_{call}_" in k]
             if not names:
                 continue
-            f_kib = sum(statistics.median(fetch[k]) for k in names)
-            w_kib = sum(statistics.median(write[k]) for k in names)
+            # mean over dispatches: lanes of one workload differ in size, and
+            # the algorithmic bytes of a call are the mean over its lanes
+            f_kib = sum(statistics.mean(fetch[k]) for k in names)
+            w_kib = sum(statistics.mean(write[k]) for k in names)
             entry[call] = {
                 "kernels": sorted({re.search(r"k_\w+", k).group(0) for k in names}),
                 "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
