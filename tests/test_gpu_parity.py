@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 MID = WorkloadSpec(
     name="mid_ragged", seed=21,
     lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
-           LaneSpec("fp16_share", 1544, (264,), "fp16", tp_size=2, tp_rank=1)),
+           LaneSpec("fp16_share", 1544, (264,), "fp16", tp_size=2, tp_rank=1),
+           LaneSpec("wide_in", 4616, (136,))),
     n_adapters=5, ranks=(3, 12, 17, 1, 130), rank_mode="list",
     scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=130,
     decode_rows=90, base_prob=0.2, prefill_seqs=6, prefill_len=(1, 200))
@@ -94,11 +95,12 @@ def test_small_configs_full_parity(lib, cfg, lane, mode):
 
 
 @pytest.mark.parametrize("mode", ["real", "int"])
-@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
+@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share", "wide_in"])
 @pytest.mark.parametrize("prefill_min_len", [64, 1, 2**31 - 1])
 def test_ragged_full_parity(lib, lane, mode, prefill_min_len):
-    """h_in = 3 sub-chunks + 8, slices 520|136|8, ranks 1..130, sequences of
-    length 1..200 around the 64-row segment edges, both paths forced."""
+    """h_in = 3 sub-chunks + 8 (wide_in: 9 + 8, so a GEMV part holds two
+    sub-chunks), slices 520|136|8, ranks 1..130, sequences of length 1..200
+    around the 64-row segment edges, both paths forced."""
     w = generate(MID, mode=mode)
     y, adm, info = run_lane(lib, w, lane, prefill_min_len=prefill_min_len)
     if prefill_min_len == 1:
@@ -164,7 +166,7 @@ def test_base_rows_not_read_or_written(lib):
 
 
 @pytest.mark.parametrize("cfg,lane", [("decode_mix", "qkv"), ("mid", "qkv_like"),
-                                      ("mid", "fp16_share")])
+                                      ("mid", "fp16_share"), ("mid", "wide_in")])
 def test_permutation_and_solo_bit_exact(lib, cfg, lane):
     w = generate(MID) if cfg == "mid" else generate(config_by_name(cfg))
     L = w.lanes[lane]
@@ -277,3 +279,36 @@ def test_load_errors(lib):
     with pytest.raises(lib.LoraError) as e:
         pool.load(77, [s.A], [s.B], [s.rank], [s.scale])
     assert e.value.status == "LORA_ERR_CAPACITY"
+
+
+def test_graph_replays_match_eager(lib):
+    """delta_apply captured in a HIP graph, together with the reset of y, gives
+    the eager bits on every replay, with other device work run in between.
+    MID routes rows through the decode GEMV, prefill and gather kernels."""
+    import torch
+    w = generate(MID)
+    for lane in ("qkv_like", "wide_in"):
+        L = w.lanes[lane]
+        pool = load_lane_pool(lib.Pool, w, lane)
+        routing = lib.Routing(int(np.sum(w.seq_len)), len(w.seq_len))
+        routing.build(pool, w.seq_adapter, w.seq_len, w.spec.max_loras)
+        info = routing.info()
+        assert info["n_decode_segments"] and info["n_prefill_segments"]
+        assert info["n_gather_segments"]
+        xd, y0 = to_device_x(L.x), to_device_y(L.y0)
+        ws = lib.workspace_for(pool, routing)
+        ye = y0.clone()
+        lib.delta_apply(pool, routing, xd, ye, ws)
+        torch.cuda.synchronize()
+        ref = ye.cpu().numpy().view(np.uint32)
+        yg = torch.empty_like(y0)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            yg.copy_(y0)
+            lib.delta_apply(pool, routing, xd, yg, ws)
+        for i in range(4):
+            yg.fill_(float("nan"))
+            torch.randn(1 << 20, device="cuda").sum().item()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(yg.cpu().numpy().view(np.uint32), ref), (lane, i)
