@@ -206,8 +206,8 @@ __device__ __forceinline__ void widen_bf16x8(uint4 b, float (&f)[8])
 //   n_rows   rows of the kExpandRows that belong to the segment (may exceed
 //            kExpandRows; rows from kExpandRows on are not this wave's)
 //   bt       B^T of the slice at this lane's columns: bt[k * hj]
-//   wait     called once, after the loads of y and of the first B block are
-//            issued and before v is first read
+//   wait     called once, after the loads of the first two B blocks and of y
+//            are issued and before v is first read
 //   vsrc     vsrc(c, kb, out) fills out[0..8) with v of row c, ranks kb..kb+7
 //            (ranks at or past `rank` must come back as zero)
 // y[row c][cols] += sum_k B[k] v[c][k] for c < n_rows, when store is true.
@@ -217,7 +217,19 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[kExpandRows], int
                                             Wait wait, VSrc vsrc)
 {
     constexpr int C = kExpandRows;
-    // y first: the largest transfer, in flight while B and v arrive.
+    // Ranks in blocks of 8 (pool rows past the rank are zero and in bounds;
+    // v past the rank is zero), the next block's B loads in flight.  Loads
+    // complete in issue order, so the first two B blocks (rows 0..15, inside
+    // rank_pad) are issued before y: their products then run while y is
+    // still on its way from HBM.
+    uint4 b0[8], b1[8];
+    auto load_b = [&](uint4 (&b)[8], int kb) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) b[k] = ld16(bt + (int64_t)(kb + k) * hj);
+    };
+    load_b(b0, 0);
+    load_b(b1, 8);
+    __builtin_amdgcn_sched_barrier(0);   // keeps the y loads behind them
     float4 ya[C], yb[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -229,13 +241,6 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[kExpandRows], int
     for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-    // Ranks in blocks of 8 (pool rows past the rank are zero and in bounds;
-    // v past the rank is zero), the next block's B loads in flight.
-    uint4 b0[8], b1[8];
-    auto load_b = [&](uint4 (&b)[8], int kb) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) b[k] = ld16(bt + (int64_t)(kb + k) * hj);
-    };
     auto fma_b = [&](const uint4 (&b)[8], int kb) {
         float vk[C][8];
 #pragma unroll
@@ -250,14 +255,13 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[kExpandRows], int
                 for (int e = 0; e < 8; ++e) acc[c][e] = __builtin_fmaf(bf[e], vk[c][k], acc[c][e]);
         }
     };
-    load_b(b0, 0);
     wait();
     for (int kb = 0; kb < rank; kb += 16) {
-        if (kb + 8 < rank) load_b(b1, kb + 8);
         fma_b(b0, kb);
         if (kb + 8 >= rank) break;
         if (kb + 16 < rank) load_b(b0, kb + 16);
         fma_b(b1, kb + 8);
+        if (kb + 24 < rank) load_b(b1, kb + 24);
     }
     if (store) {
 #pragma unroll
