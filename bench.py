@@ -99,10 +99,19 @@ def summarize_pmc(pmc_dir: str, configs):
             names = [k for k in fetch if f"k_{call}_" in k]
             if not names:
                 continue
-            # mean over dispatches: lanes of one workload differ in size, and
-            # the algorithmic bytes of a call are the mean over its lanes
-            f_kib = sum(statistics.mean(fetch[k]) for k in names)
-            w_kib = sum(statistics.mean(write[k]) for k in names)
+            # A call launches one kernel per segment kind present (decode
+            # GEMV, prefill MFMA, gather MFMA), and lanes may use different
+            # template instances of them; the mean per call is the total over
+            # all dispatches divided by the number of calls, which is the
+            # dispatch count of any one kind.
+            def kind(k):
+                return "gemv" if "_gemv" in k else ("gather" if "true>" in k else "mfma")
+            counts = {}
+            for k in names:
+                counts[kind(k)] = counts.get(kind(k), 0) + len(fetch[k])
+            calls = max(counts.values())
+            f_kib = sum(sum(fetch[k]) for k in names) / calls
+            w_kib = sum(sum(write[k]) for k in names) / calls
             entry[call] = {
                 "kernels": sorted({re.search(r"k_\w+", k).group(0) for k in names}),
                 "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
