@@ -279,9 +279,11 @@ int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **de
  *
  * Within a row every sum runs in an order fixed by the lane's widths and the
  * adapter's rank alone, so a row's bits depend only on its own x row, its
- * adapter's factors and its own path (decode or prefill), never on the other
- * rows of the batch, the slot it sits in, max_rank or the launch shape
- * (TensorFold PR #47, third commit message).
+ * adapter's factors and its own path (GEMV for decode rows; matrix cores for
+ * prefill rows and for the decode rows of an adapter with a slice rank >=
+ * LORA_GATHER_MIN_RANK), never on the other rows of the batch, the slot it
+ * sits in, max_rank or the launch shape (TensorFold PR #47, third commit
+ * message).
  */
 
 /* v for all active rows (shrink: A @ x, times scale).  Errors: ARG, SHAPE,
