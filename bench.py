@@ -5,8 +5,9 @@ A step is one batch through the whole hot path: the batch's routing is built
 once (admission, slots, segments, copied to the device) and the delta is then
 applied on every lane of the workload for each of --layers independent layer
 buffers (pool, x, y), as a decode step of a model with that many layers would.
-The layer buffers together exceed the 256 MB last-level cache several times,
-so every layer's factors and activations come from HBM.
+By default there are enough layers for the buffers to total at least 1 GiB,
+four times the 256 MB last-level cache, so every layer's factors and
+activations come from HBM.
 
 Printed: one JSON line with the step throughput (delta tokens/s: active rows x
 lanes x layers per second), the roofline of the delta kernels measured with
@@ -138,10 +139,12 @@ def summarize_pmc(pmc_dir: str, configs):
 
 
 def sources_digest() -> str:
-    """sha256 over the library's sources: a counter summary taken from other
-    sources no longer describes the kernels that run."""
+    """sha256 over the library's code: a counter summary taken from other code
+    no longer describes the kernels that run.  Comments and whitespace are
+    left out, so edits to the documentation keep the summary valid."""
     import hashlib
     h = hashlib.sha256()
+    comment = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
     for top in KERNEL_SOURCES:
         path = os.path.join(ROOT, top)
         files = [path] if os.path.isfile(path) else sorted(
@@ -149,8 +152,9 @@ def sources_digest() -> str:
             if f.endswith((".h", ".hip", ".cpp")))
         for f in files:
             h.update(os.path.relpath(f, ROOT).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+            with open(f, encoding="utf-8") as fh:
+                code = comment.sub(" ", fh.read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()
 
 
@@ -167,21 +171,54 @@ def recorded_traffic(config: str, kernel: str):
     return rec["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(w, lanes, seconds):
-    """The fp64 oracle, as it is, on the same batch, repeated for ~seconds."""
+def cpu_baseline(w, lanes, seconds, threads=1):
+    """The fp64 oracle, as it is, on the same batch, repeated for ~seconds.
+    With threads > 1 the batch's active rows are split into chunks that the
+    oracle computes on that many threads at once (its C loop runs without the
+    interpreter lock)."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = {}
+    for ln in lanes:
+        _, tok, _ = oracle.workload_lane_delta(w, ln, rows=np.zeros(0, dtype=np.int64))
+        act = np.nonzero(tok)[0]
+        chunks[ln] = (len(act), [c for c in np.array_split(act, 4 * threads) if len(c)])
     t0 = time.perf_counter()
     rows = 0
     reps = 0
-    while True:
-        for ln in lanes:
-            d, tok, _ = oracle.workload_lane_delta(w, ln)
-            rows += int((tok != 0).sum())
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            for ln in lanes:
+                n, parts = chunks[ln]
+                if threads == 1:
+                    oracle.workload_lane_delta(w, ln)
+                else:
+                    list(ex.map(lambda r: oracle.workload_lane_delta(w, ln, rows=r), parts))
+                rows += n
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
     dt = time.perf_counter() - t0
     return rows / dt, dt, reps
+
+
+def stream_copy_gbs(dev, nbytes=1 << 30, reps=10):
+    """Read + write bandwidth of a plain device copy of nbytes (context for the
+    achievable fraction of the 8 TB/s peak)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def main():
@@ -190,7 +227,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_mix")
-    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer buffer sets (default: enough for 1 GiB, at least 16)")
     ap.add_argument("--graph-reps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill-min-len", type=int, default=64)
@@ -240,15 +278,13 @@ def main():
     n_seq = len(w.seq_len)
 
     # layer buffers: each layer has its own pool, x and y per lane
-    log(f"building {args.layers} layers x {len(lanes)} lanes")
     fac = {}
     for ln in lanes:
         fac[ln] = {aid: ([torch.from_numpy(s.A.view(np.int16)).to(dev) for s in ad.lanes[ln]],
                          [torch.from_numpy(s.B.view(np.int16)).to(dev) for s in ad.lanes[ln]],
                          [s.rank for s in ad.lanes[ln]], [s.scale for s in ad.lanes[ln]])
                    for aid, ad in w.adapters.items()}
-    layers = []
-    for li in range(args.layers):
+    def make_layer():
         per = {}
         for ln in lanes:
             L = w.lanes[ln].spec
@@ -256,10 +292,16 @@ def main():
             for aid, (A, B, rk, sc) in fac[ln].items():
                 pool.load(aid, A, B, rk, sc, a_col0=L.a_col0)
             per[ln] = (pool, to_device_x(w.lanes[ln].x, dev), to_device_y(w.lanes[ln].y0, dev))
-        layers.append(per)
-    torch.cuda.synchronize()
+        return per
+    layers = [make_layer()]
     layer_bytes = sum(p.nbytes + x.numel() * 2 + y.numel() * 4
-                      for per in layers[:1] for (p, x, y) in per.values())
+                      for (p, x, y) in layers[0].values())
+    if args.layers <= 0:
+        args.layers = max(16, -(-(1 << 30) // layer_bytes))
+    log(f"building {args.layers} layers x {len(lanes)} lanes, {layer_bytes} bytes each")
+    while len(layers) < args.layers:
+        layers.append(make_layer())
+    torch.cuda.synchronize()
 
     # one routing serves every lane: it is built against the pool with the most
     # slices (the others hold the same ranks on their slices)
@@ -352,6 +394,11 @@ def main():
 
     log(f"cpu baseline ~{args.cpu_seconds}s")
     cpu_rate, cpu_dt, cpu_reps = cpu_baseline(w, lanes, args.cpu_seconds)
+    n_thr = max(1, min(16, os.cpu_count() or 1))
+    log(f"cpu baseline on {n_thr} threads ~{args.cpu_seconds / 2}s")
+    par_rate, par_dt, par_reps = cpu_baseline(w, lanes, args.cpu_seconds / 2, n_thr)
+    log("stream copy context")
+    copy_gbs = stream_copy_gbs(dev)
 
     out = {
         "metric": "LoRA-delta tokens/s + achieved HBM GB/s fraction of peak, mixed-adapter decode",
@@ -401,6 +448,16 @@ def main():
             "sample": f"fp64 C oracle over the whole {spec.name} batch "
                       f"({info['n_active']} active rows x {len(lanes)} lanes), "
                       f"{cpu_reps} repetitions in {cpu_dt:.1f} s",
+        },
+        "cpu_baseline_threads": {
+            "value": round(par_rate, 1), "unit": "delta tokens/s", "cores": n_thr,
+            "kind": "oracle",
+            "sample": f"the same oracle on row chunks of the batch over {n_thr} threads, "
+                      f"{par_reps} repetitions in {par_dt:.1f} s",
+        },
+        "context": {
+            "stream_copy_gbs": round(copy_gbs, 1),
+            "stream_copy": "torch copy of 1 GiB, read + write bytes per second",
         },
     }
     print(json.dumps(out), flush=True)
