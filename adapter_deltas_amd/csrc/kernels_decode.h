@@ -201,22 +201,21 @@ __device__ __forceinline__ void widen_bf16x8(uint4 b, float (&f)[8])
     f[7] = __uint_as_float(b.w & 0xffff0000u);
 }
 
-// Expand of kExpandRows rows of a decode segment over 8 columns per lane.
+// Expand of C rows of a decode segment over 8 columns per lane.
 //   yp[c]    y of segment row c at this lane's columns (valid for every c)
-//   n_rows   rows of the kExpandRows that belong to the segment (may exceed
-//            kExpandRows; rows from kExpandRows on are not this wave's)
+//   n_rows   rows of the C that belong to the segment (may exceed C, rows
+//            from C on being another wave's, or be <= 0: nothing is stored)
 //   bt       B^T of the slice at this lane's columns: bt[k * hj]
 //   wait     called once, after the loads of the first two B blocks and of y
 //            are issued and before v is first read
 //   vsrc     vsrc(c, kb, out) fills out[0..8) with v of row c, ranks kb..kb+7
 //            (ranks at or past `rank` must come back as zero)
 // y[row c][cols] += sum_k B[k] v[c][k] for c < n_rows, when store is true.
-template <class Wait, class VSrc>
-__device__ __forceinline__ void expand_rows(float *const (&yp)[kExpandRows], int n_rows,
+template <int C, class Wait, class VSrc>
+__device__ __forceinline__ void expand_rows(float *const (&yp)[C], int n_rows,
                                             const uint16_t *bt, int hj, int rank, bool store,
                                             Wait wait, VSrc vsrc)
 {
-    constexpr int C = kExpandRows;
     // Ranks in blocks of 8 (pool rows past the rank are zero and in bounds;
     // v past the rank is zero), the next block's B loads in flight.  Loads
     // complete in issue order, so the first two B blocks (rows 0..15, inside

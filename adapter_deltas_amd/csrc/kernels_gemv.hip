@@ -110,7 +110,85 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
             out[k] = kb + k < rank ? t : 0.f;
         }
     };
-    expand_rows(yp, n_rows, bt, hj, rank, col_ok, [] {}, vsrc);
+    expand_rows<C>(yp, n_rows, bt, hj, rank, col_ok, [] {}, vsrc);
+}
+
+// Shrink and expand of decode segments in one launch, for ranks up to
+// kFusedMaxRank and slices of at most kFusedMaxTiles column tiles.  A task is the expand's (segment, slice, 512 columns); its
+// eight waves first compute the segment's v for the slice exactly as
+// k_shrink_gemv does (wave w sums part w with shrink_part, the parts are
+// combined in the same order, v = fp32(scale * u)) into LDS, while the
+// task's y rows and first B blocks are already loading, and then expand one
+// segment row each with expand_rows.  Every value is the one the two kernels
+// produce, so the result is bit-identical to lora_shrink then lora_expand.
+// The column tiles of a slice recompute the same v: cheap next to a second
+// launch while the rank and the number of tiles are small (8 rows x 64
+// columns: 6.2 -> 5.0 us per call), too costly for a 4096-wide slice (8
+// tiles: 12 -> 21 us).
+template <bool FP16X>
+__global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev p, RoutingDev r,
+                                                            int tiles_per_slice,
+                                                            const uint16_t *__restrict__ x,
+                                                            int64_t ldx, float *__restrict__ y,
+                                                            int64_t ldy)
+{
+    constexpr int KB = kFusedMaxRank / kKBlock;   // rank blocks at most
+    static_assert(kParts == kDecodeSegRows, "one part and one row per wave");
+    const int per_seg = g.n_slices * tiles_per_slice;
+    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int si = task / per_seg;
+    const int rem = task - si * per_seg;
+    const int j = rem / tiles_per_slice;
+    const int tile = rem - j * tiles_per_slice;
+    const int hj = g.h_out[j];
+    if (tile * kExpandTile >= hj) return;       // the whole workgroup
+    const Seg sd = load_seg(r.seg, si);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int rank = sd.rank(j);
+    const int n_kb = (rank + kKBlock - 1) / kKBlock;
+    const int o0 = tile * kExpandTile + lane * 8;
+    const bool col_ok = o0 < hj;
+    const int oc = col_ok ? o0 : hj - 8;
+    // this wave's segment row (past the segment: the descriptor's repeat of
+    // the last row, loaded but not stored)
+    const int all[kDecodeSegRows] = {sd.row<0>(), sd.row<1>(), sd.row<2>(), sd.row<3>(),
+                                     sd.row<4>(), sd.row<5>(), sd.row<6>(), sd.row<7>()};
+    int trow = all[0];
+#pragma unroll
+    for (int w = 1; w < kDecodeSegRows; ++w)
+        if (wave == w) trow = all[w];
+    float *const yp[1] = {y + (int64_t)trow * ldy + g.col_off[j] + oc};
+    const uint16_t *bt =
+        p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j] + oc;
+
+    __shared__ float part[KB][kParts][64];
+    __shared__ float vl[kDecodeSegRows][KB * kKBlock];
+    const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
+    auto shrink = [&] {
+        for (int kb = 0; kb < n_kb; ++kb) {
+            const int k0 = kb * kKBlock;
+            // a part with no sub-chunk sums to zero
+            part[kb][wave][lane] =
+                wave < n_sub ? shrink_part<FP16X>(g, p, sd, j, k0, min(kKBlock, rank - k0), wave,
+                                                  lane, x, ldx)
+                             : 0.f;
+        }
+        __syncthreads();
+        if (threadIdx.x < n_kb * 64) {
+            const int kb = threadIdx.x >> 6, l = threadIdx.x & 63;
+            const float q0 = (part[kb][0][l] + part[kb][1][l]) + (part[kb][2][l] + part[kb][3][l]);
+            const float q1 = (part[kb][4][l] + part[kb][5][l]) + (part[kb][6][l] + part[kb][7][l]);
+            const float scale = p.scale[sd.slot() * kMetaStride + j];
+            vl[l / kKBlock][kb * kKBlock + l % kKBlock] = scale * (q0 + q1);
+        }
+        __syncthreads();
+    };
+    auto vsrc = [&](int, int kb, float (&out)[8]) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) out[k] = kb + k < rank ? vl[wave][kb + k] : 0.f;
+    };
+    expand_rows<1>(yp, sd.n_rows() - wave, bt, hj, rank, col_ok, shrink, vsrc);
 }
 
 // ---- pool maintenance ----
@@ -189,6 +267,24 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
         else LAUNCH_SHRINK(false, 1);
     }
 #undef LAUNCH_SHRINK
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                             int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
+                             int64_t ldy, hipStream_t s)
+{
+    const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const uint16_t *xp = static_cast<const uint16_t *>(x);
+    const dim3 grid((unsigned)blocks), block(64 * kParts);
+    if (g.x_fp16)
+        hipLaunchKernelGGL(k_delta_gemv<true>, grid, block, 0, s, g, p, r, tiles_per_slice, xp, ldx,
+                           y, ldy);
+    else
+        hipLaunchKernelGGL(k_delta_gemv<false>, grid, block, 0, s, g, p, r, tiles_per_slice, xp,
+                           ldx, y, ldy);
     return hipGetLastError();
 }
 

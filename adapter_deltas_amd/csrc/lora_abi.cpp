@@ -187,14 +187,16 @@ int32_t check_v(const float *v)
     return LORA_OK;
 }
 
+// The kernels of each call.  With decode = false the decode segments are left
+// to the caller (the one-launch decode delta of lora_delta_apply).
 int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
-                       float *v, hipStream_t s)
+                       float *v, hipStream_t s, bool decode = true)
 {
     const lora_routing_info &I = r->info;
     const int kmax = batch_max_rank(p, r);
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
-    if (I.n_decode_segments > 0) {
+    if (decode && I.n_decode_segments > 0) {
         int kb = (kmax + kKBlock - 1) / kKBlock;
         hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
@@ -215,14 +217,14 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
 }
 
 int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v, float *y,
-                       int64_t ldy, hipStream_t s)
+                       int64_t ldy, hipStream_t s, bool decode = true)
 {
     const lora_routing_info &I = r->info;
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
     int hmax = 0;
     for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
-    if (I.n_decode_segments > 0) {
+    if (decode && I.n_decode_segments > 0) {
         int tiles = (hmax + kExpandTile - 1) / kExpandTile;
         hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
@@ -844,8 +846,22 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
                     (long long)workspace_bytes, (long long)need);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *v = static_cast<float *>(workspace);
-    if (int32_t rc = enqueue_shrink(p, r, x, ldx, v, st)) return rc;
-    return enqueue_expand(p, r, v, y, ldy, st);
+    // Decode segments of small ranks and narrow slices: shrink and expand in
+    // one launch, with the same arithmetic as the two kernels (bit-identical
+    // results).  Each column tile of a slice recomputes the segment's v, so
+    // wide slices keep the two launches.
+    int hmax = 0;
+    for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
+    const int tiles = (hmax + kExpandTile - 1) / kExpandTile;
+    const bool fused = r->info.n_decode_segments > 0 && tiles <= kFusedMaxTiles &&
+                       batch_max_rank(p, r) <= kFusedMaxRank;
+    if (fused) {
+        hipError_t e = launch_delta_gemv(p->geom, pool_dev(p), routing_dev(r),
+                                         r->info.n_decode_segments, tiles, x, ldx, y, ldy, st);
+        if (e != hipSuccess) return hip_fail(e, "delta (decode) launch");
+    }
+    if (int32_t rc = enqueue_shrink(p, r, x, ldx, v, st, !fused)) return rc;
+    return enqueue_expand(p, r, v, y, ldy, st, !fused);
 }
 
 }  // extern "C"

@@ -19,6 +19,8 @@ constexpr int kKBlock = 8;                              // ranks per decode shri
 constexpr int kSubChunk = 512;                          // h_in elements per wave pass
 constexpr int kParts = 8;                               // interleaved h_in parts (one wave each)
 constexpr int kExpandTile = 512;                        // columns per decode expand task
+constexpr int kFusedMaxRank = 16;                       // ranks of the one-launch decode delta
+constexpr int kFusedMaxTiles = 2;                       // and its column tiles per slice
 constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
 #ifndef LORA_EXPAND_BLOCKS
 #define LORA_EXPAND_BLOCKS 8192
@@ -77,6 +79,9 @@ struct RoutingDev {
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
                               float *v, hipStream_t s);
+hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                             int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
+                             int64_t ldy, hipStream_t s);
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int tiles_per_slice, const float *v, float *y,
                               int64_t ldy, hipStream_t s);

@@ -118,6 +118,33 @@ def test_y0_zero_and_split_path_parity(lib):
     w = generate(config_by_name("decode_mix"), y0="zeros")
     y, adm, _ = run_lane(lib, w, "qkv", path="split")
     check_full(w, "qkv", y, adm)
+    ya, _, _ = run_lane(lib, w, "qkv")
+    assert np.array_equal(ya.view(np.uint32), y.view(np.uint32))
+
+
+# Decode rows only, ranks up to 16 and slices of at most 1024 columns (the
+# one-launch decode delta of delta_apply), ragged widths, bf16 and fp16 x,
+# some parts of h_in empty or holding two sub-chunks.
+SMALL_RANK = WorkloadSpec(
+    name="small_rank_ragged", seed=22,
+    lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
+           LaneSpec("fp16_share", 4616, (264,), "fp16", tp_size=2, tp_rank=1)),
+    n_adapters=5, ranks=(3, 12, 16, 1, 9), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=16,
+    decode_rows=150, base_prob=0.2, prefill_seqs=0, prefill_len=(1, 1))
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
+def test_one_launch_decode_delta_matches_split(lib, lane, mode):
+    """delta_apply (shrink and expand in one launch) is bit-identical to
+    lora_shrink then lora_expand, and both match the oracle."""
+    w = generate(SMALL_RANK, mode=mode)
+    ya, adm, info = run_lane(lib, w, lane)
+    assert info["n_decode_segments"] > 0 and info["n_prefill_segments"] == 0
+    ys, _, _ = run_lane(lib, w, lane, path="split")
+    assert np.array_equal(ya.view(np.uint32), ys.view(np.uint32))
+    check_full(w, lane, ya, adm)
 
 
 # ------------------------------------------- full-size configs, sampled rows
