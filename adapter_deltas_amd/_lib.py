@@ -20,6 +20,7 @@ MAX_RANK = 256
 DECODE_SEG_ROWS = 8
 SEG_WORDS = 16
 GATHER_MIN_RANK = 128         # LORA_GATHER_MIN_RANK
+DEVICE_ROUTING_MAX_TOKENS = 4096   # LORA_DEVICE_ROUTING_MAX_TOKENS
 PREFILL_SEG_ROWS = 64
 
 # every symbol include/lora.h declares
@@ -29,7 +30,7 @@ EXPORTS = (
     "lora_pool_unload", "lora_pool_slot_of",
     "lora_routing_bytes", "lora_routing_create", "lora_routing_destroy",
     "lora_build_routing", "lora_routing_get_info", "lora_plan_routing",
-    "lora_routing_token_slots",
+    "lora_routing_token_slots", "lora_build_routing_device", "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
 )
 
@@ -90,6 +91,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                     PI32, I64, PI32, ctypes.POINTER(RoutingInfo),
                                     ctypes.POINTER(ctypes.c_uint8)]),
         "lora_routing_token_slots": (I32, [P, PP]),
+        "lora_build_routing_device": (I32, [P, P, I32, P, P]),
+        "lora_routing_device_counts": (I32, [P, PP]),
         "lora_shrink": (I32, [P, P, P, I64, P, P]),
         "lora_expand": (I32, [P, P, P, P, I64, P]),
         "lora_workspace_bytes": (I32, [P, P, PI64]),

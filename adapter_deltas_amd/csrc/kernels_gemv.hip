@@ -26,6 +26,7 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
     const int rem = task - si * per_seg;
     const int j = rem / kb_per_slice;
     const int kb = rem - j * kb_per_slice;
+    if (r.counts && si >= r.counts[kCntDecode]) return;    // device-built routing
     const Seg sd = load_seg(r.seg, si);
     const int rank = sd.rank(j);
     const int k0 = kb * kKBlock;
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
     const int tile = rem - j * tiles_per_slice;
     const int hj = g.h_out[j];
     if (tile * kExpandTile >= hj) return;
+    if (r.counts && si >= r.counts[kCntDecode]) return;    // device-built routing
     const Seg sd = load_seg(r.seg, si);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
     const int tile = rem - j * tiles_per_slice;
     const int hj = g.h_out[j];
     if (tile * kExpandTile >= hj) return;       // the whole workgroup
+    if (r.counts && si >= r.counts[kCntDecode]) return;
     const Seg sd = load_seg(r.seg, si);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;

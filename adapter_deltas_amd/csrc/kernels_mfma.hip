@@ -106,6 +106,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     const int rem2 = rem - rc * per_chunk;
     const int j = rem2 / groups_per_slice;
     const int grp = rem2 - j * groups_per_slice;
+    if (r.counts && si - seg_begin >= r.counts[kCntGather]) return;   // device-built routing
     const Seg sd = load_seg(r.seg, si);
     const int rb = rc * ROWS;                       // first segment row of the task
     const int n_rows = sd.n_rows() - rb;            // rows of the task, if positive
@@ -281,7 +282,9 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     const int o_base = tile * COLS;
     if (o_base >= hj) return;
     const int s_first = seg_begin + grp * group;
-    const int s_last = min(s_first + group, seg_end);
+    int s_last = min(s_first + group, seg_end);
+    if (r.counts) s_last = min(s_last, seg_begin + r.counts[kCntGather]);   // device-built routing
+    if (s_first >= s_last) return;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;

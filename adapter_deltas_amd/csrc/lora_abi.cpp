@@ -125,13 +125,18 @@ PoolDev pool_dev(const lora_pool *p)
 
 RoutingDev routing_dev(const lora_routing *r)
 {
-    return RoutingDev{r->dev + r->off_seg, r->dev + r->off_tok, r->dev + r->off_row};
+    return RoutingDev{r->dev + r->off_seg, r->dev + r->off_tok, r->dev + r->off_row,
+                      r->device_built ? r->dev + r->off_counts : nullptr};
 }
 
 // Largest rank over the routing's distinct slots and the lane's slices.
 int batch_max_rank(const lora_pool *p, const lora_routing *r)
 {
     int m = 0;
+    if (r->device_built) {   // the slots are only known on the device
+        for (int32_t rk : p->h_rank) m = std::max(m, rk);
+        return m;
+    }
     for (int32_t s : r->distinct_slots)
         for (int j = 0; j < p->desc.n_slices; ++j)
             m = std::max(m, p->h_rank[(size_t)s * kMetaStride + j]);
@@ -607,7 +612,18 @@ int32_t lora_pool_unload(lora_pool *p, int32_t adapter_id)
     auto it = p->id_to_slot.find(adapter_id);
     if (it == p->id_to_slot.end())
         return fail(LORA_ERR_UNKNOWN_ADAPTER, "adapter %d is not resident", adapter_id);
-    p->slot_to_id[it->second] = 0;
+    const int32_t slot = it->second;
+    // The slot's ranks go to zero on the device too, so that a routing built
+    // on the device sees it as holding no adapter.
+    const int32_t zero[kMetaStride] = {};
+    hipError_t e = hipMemcpy(p->rank_tab + (size_t)slot * kMetaStride, zero,
+                             sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "clearing the slot's ranks");
+    for (int j = 0; j < kMetaStride; ++j) {
+        p->h_rank[(size_t)slot * kMetaStride + j] = 0;
+        p->h_scale[(size_t)slot * kMetaStride + j] = 0.f;
+    }
+    p->slot_to_id[slot] = 0;
     p->id_to_slot.erase(it);
     return LORA_OK;
 }
@@ -629,8 +645,10 @@ int32_t lora_routing_bytes(int32_t max_tokens, int64_t *bytes_out)
     if (max_tokens < 1 || max_tokens > (1 << 26))
         return fail(LORA_ERR_SHAPE, "max_tokens=%d outside 1..2^26", max_tokens);
     if (!bytes_out) return fail(LORA_ERR_ARG, "bytes_out is null");
-    // segments (kSegWords each, at most one per active row) + row list + token slots
-    *bytes_out = round_up((int64_t)max_tokens * (kSegWords + 2) * 4 + 64, 256);
+    // segments (kSegWords each: at most one per active row on the host, a
+    // decode and a gather bound of at most max_tokens each on the device)
+    // + row list + token slots + device counts
+    *bytes_out = round_up((int64_t)max_tokens * (2 * kSegWords + 2) * 4 + 256, 256);
     return LORA_OK;
 }
 
@@ -668,6 +686,8 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
     std::memset(&r->info, 0, sizeof r->info);
     r->off_seg = r->off_row = r->off_tok = 0;
     r->pool_max_slots = 0;
+    r->device_built = false;
+    r->off_counts = 0;
     *routing_out = r;
     return LORA_OK;
 }
@@ -724,6 +744,7 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
     r->off_seg = 0;
     r->off_row = (int32_t)pl.off_row();
     r->off_tok = (int32_t)pl.off_tok();
+    r->device_built = false;
     r->info = pl.info;
     r->pool_max_slots = p->desc.max_slots;
     r->distinct_slots = pl.distinct_slots;
@@ -782,6 +803,77 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
     *info_out = pl.info;
     if (admitted_out)
         for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
+    return LORA_OK;
+}
+
+int32_t lora_build_routing_device(const lora_pool *p, const int32_t *tok_slot,
+                                  int32_t n_tokens, lora_routing *r, void *stream)
+{
+    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
+    if (n_tokens < 0) return fail(LORA_ERR_SHAPE, "n_tokens < 0");
+    if (n_tokens > r->max_tokens || n_tokens > LORA_DEVICE_ROUTING_MAX_TOKENS)
+        return fail(LORA_ERR_CAPACITY, "n_tokens=%d > max_tokens=%d or > %d", n_tokens,
+                    r->max_tokens, LORA_DEVICE_ROUTING_MAX_TOKENS);
+    if (n_tokens > 0 && !tok_slot) return fail(LORA_ERR_ARG, "tok_slot is null");
+    // Bounds: a slot's decode rows make ceil(n / 8) decode or ceil(n / 64)
+    // gather segments, so either kind has at most n_tokens / size + slots.
+    // A kind no resident adapter takes gets no room (and no launch).
+    bool any_dec = false, any_gather = false;
+    for (int32_t s = 1; s <= p->desc.max_slots; ++s) {
+        if (p->slot_to_id[s] == 0) continue;
+        int rmax = 0;
+        for (int j = 0; j < kMetaStride; ++j)
+            rmax = std::max(rmax, p->h_rank[(size_t)s * kMetaStride + j]);
+        (rmax >= kGatherMinRank ? any_gather : any_dec) = true;
+    }
+    const int64_t slots = std::min<int64_t>(n_tokens, p->desc.max_slots);
+    const int32_t max_dec = !any_dec ? 0 : (int32_t)std::min<int64_t>(
+        n_tokens, (n_tokens + kDecodeSegRows - 1) / kDecodeSegRows + slots);
+    const int32_t max_gather = !any_gather ? 0 : (int32_t)std::min<int64_t>(
+        n_tokens, (n_tokens + kPrefillSegRows - 1) / kPrefillSegRows + slots);
+    const int64_t off_row = (int64_t)(max_dec + max_gather) * kSegWords;
+    const int64_t off_tok = round_up(off_row + n_tokens, 4);
+    const int64_t off_counts = round_up(off_tok + n_tokens, 4);
+    if (off_counts + kCntWords > r->dev_words)
+        return fail(LORA_ERR_CAPACITY, "routing memory too small for %d tokens", n_tokens);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_route_decode(tok_slot, n_tokens, p->rank_tab, p->desc.max_slots, max_dec,
+                                       max_gather, r->dev, r->dev + off_row, r->dev + off_tok,
+                                       r->dev + off_counts, st);
+    if (e != hipSuccess) return hip_fail(e, "routing kernel launch");
+    r->off_seg = 0;
+    r->off_row = (int32_t)off_row;
+    r->off_tok = (int32_t)off_tok;
+    r->off_counts = (int32_t)off_counts;
+    r->device_built = true;
+    r->pool_max_slots = p->desc.max_slots;
+    // Every resident slot may appear in the tables: a pool used with this
+    // routing must hold all of them with the same ranks.
+    r->distinct_slots.clear();
+    r->slot_ranks.clear();
+    for (int32_t s = 1; s <= p->desc.max_slots; ++s) {
+        if (p->slot_to_id[s] == 0) continue;
+        r->distinct_slots.push_back(s);
+        for (int j = 0; j < kMetaStride; ++j)
+            r->slot_ranks.push_back(p->h_rank[(size_t)s * kMetaStride + j]);
+    }
+    lora_routing_info &I = r->info;
+    std::memset(&I, 0, sizeof I);
+    I.n_tokens = n_tokens;
+    I.n_active = n_tokens;                  // bounds: the exact counts are on the device
+    I.n_decode_segments = max_dec;
+    I.n_prefill_segments = 0;
+    I.n_gather_segments = max_gather;
+    I.n_segments = max_dec + max_gather;
+    I.n_seqs = I.n_admitted_seqs = n_tokens;
+    return LORA_OK;
+}
+
+int32_t lora_routing_device_counts(const lora_routing *r, const int32_t **dev_ptr_out)
+{
+    if (!r || !dev_ptr_out) return fail(LORA_ERR_ARG, "routing or dev_ptr_out is null");
+    if (!r->device_built) return fail(LORA_ERR_ARG, "the routing was built on the host");
+    *dev_ptr_out = r->dev + r->off_counts;
     return LORA_OK;
 }
 

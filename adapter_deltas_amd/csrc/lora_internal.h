@@ -73,7 +73,11 @@ struct RoutingDev {
     const int32_t *seg;       // kSegWords words per segment
     const int32_t *tok_slot;  // slot per token row
     const int32_t *rows;      // token row of each active row
+    const int32_t *counts;    // device-built routing: exact counts (else null)
 };
+// Entries of a device-built routing's counts.
+enum DeviceCount : int { kCntActive = 0, kCntDecode = 1, kCntPrefill = 2, kCntGather = 3,
+                         kCntInvalid = 4, kCntWords = 8 };
 
 // ---- launchers (kernels_*.hip) ----
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
@@ -92,6 +96,9 @@ hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               bool gather, int seg_begin, int n_seg, int group,
                               int tiles_per_slice, int max_rank, const float *v, float *y,
                               int64_t ldy, hipStream_t s);
+hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const int32_t *rank_tab,
+                               int max_slots, int max_dec, int max_gather, int32_t *seg,
+                               int32_t *rows, int32_t *tok, int32_t *counts, hipStream_t s);
 hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
                          int rank, int rank_pad, int h_in, hipStream_t s);
 hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,
@@ -156,6 +163,8 @@ struct lora_routing {
     int32_t off_seg, off_row, off_tok;
     lora_routing_info info;
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
+    bool device_built;                // counts on the device, info holds bounds
+    int32_t off_counts;
     std::vector<int32_t> distinct_slots;
     std::vector<int32_t> slot_ranks;  // kMetaStride per distinct slot
     lora::Plan plan;                  // host tables, reused between builds

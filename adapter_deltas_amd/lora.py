@@ -17,6 +17,7 @@ from . import _lib as L
 
 DEFAULT_PREFILL_MIN_LEN = 64
 NO_PREFILL = 2**31 - 1
+DEVICE_ROUTING_MAX_TOKENS = L.DEVICE_ROUTING_MAX_TOKENS
 
 
 class LoraError(RuntimeError):
@@ -201,6 +202,18 @@ def lora_routing_token_slots(routing) -> int:
     return p.value or 0
 
 
+def lora_build_routing_device(pool, tok_slot, n_tokens, routing, stream=None) -> None:
+    """tok_slot: device int32 tensor (or address) of the slot of each row."""
+    _check(_lib().lora_build_routing_device(pool, _ptr(tok_slot), n_tokens, routing,
+                                            _stream(stream)))
+
+
+def lora_routing_device_counts(routing) -> int:
+    p = ctypes.c_void_p()
+    _check(_lib().lora_routing_device_counts(routing, ctypes.byref(p)))
+    return p.value or 0
+
+
 def lora_shrink(pool, routing, x, ldx, v, stream=None) -> None:
     _check(_lib().lora_shrink(pool, routing, _ptr(x), ldx, _ptr(v), _stream(stream)))
 
@@ -285,6 +298,19 @@ class Routing:
               prefill_min_len=DEFAULT_PREFILL_MIN_LEN, stream=None):
         return lora_build_routing(pool.handle, seq_adapter_id, seq_len, max_loras,
                                   prefill_min_len, self.handle, stream)
+
+    def build_device(self, pool: Pool, tok_slot, stream=None):
+        """Routing of a decode batch built on the device from an int32 device
+        tensor of per-row slots (0 = base)."""
+        lora_build_routing_device(pool.handle, tok_slot, int(tok_slot.numel()), self.handle,
+                                  stream)
+
+    def device_counts(self):
+        """The int32 [8] device counts of a device-built routing, as a tensor
+        viewing the routing's memory."""
+        import torch
+        off = (lora_routing_device_counts(self.handle) - self.mem.data_ptr()) // 4
+        return self.mem.view(torch.int32)[off:off + 8]
 
     def info(self) -> dict:
         return lora_routing_get_info(self.handle)

@@ -355,6 +355,10 @@ def main():
                 for ln in lanes:
                     pool, x, y = per[ln]
                     call(ln, pool, x, y)
+        return replay_us(body) / (args.layers * len(lanes))
+
+    def replay_us(body):
+        """Microseconds per replay of one graph of body's launches."""
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             body()
@@ -372,12 +376,42 @@ def main():
             g.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        return g0.elapsed_time(g1) * 1e3 / (args.graph_reps * args.layers * len(lanes))
+        return g0.elapsed_time(g1) * 1e3 / args.graph_reps
 
     log("graph replay timing")
     per_apply_us = graph_us(lambda ln, pool, x, y: m.delta_apply(pool, routing, x, y, ws[ln]))
     shrink_us = graph_us(lambda ln, pool, x, y: m.shrink(pool, routing, x, vbuf[ln]))
     expand_us = graph_us(lambda ln, pool, x, y: m.expand(pool, routing, vbuf[ln], y))
+
+    # A decode-only batch can also be routed on the device: one graph then
+    # holds the routing kernel and every layer's delta, with no host work.
+    device_routing = None
+    if np.all(w.seq_len == 1) and T <= m.DEVICE_ROUTING_MAX_TOKENS:
+        log("device routing timing")
+        tok = routing.token_slots().clone()
+        pool0 = layers[0][build_lane][0]
+        droute = m.Routing(T, T, device=dev)
+        droute.build_device(pool0, tok)
+        dws = {ln: m.workspace_for(layers[0][ln][0], droute, dev) for ln in lanes}
+
+        def dstep():
+            droute.build_device(pool0, tok)
+            for per in layers:
+                for ln in lanes:
+                    pool, x, y = per[ln]
+                    m.delta_apply(pool, droute, x, y, dws[ln])
+        def route32():
+            for _ in range(32):
+                droute.build_device(pool0, tok)
+        route_us = replay_us(route32) / 32
+        dstep_us = replay_us(dstep)
+        device_routing = {
+            "route_us": round(route_us, 3),
+            "graph_step_ms": round(dstep_us * 1e-3, 4),
+            "graph_value": round(delta_rows / (dstep_us * 1e-6), 1),
+            "note": "the same step as one graph replay: the routing kernel on the "
+                    "per-row slots, then delta_apply on every lane of every layer",
+        }
 
     alg = {"shrink": [0, 0], "expand": [0, 0]}
     for ln in lanes:
@@ -455,6 +489,7 @@ def main():
             "sample": f"the same oracle on row chunks of the batch over {n_thr} threads, "
                       f"{par_reps} repetitions in {par_dt:.1f} s",
         },
+        "device_routing": device_routing,
         "context": {
             "stream_copy_gbs": round(copy_gbs, 1),
             "stream_copy": "torch copy of 1 GiB, read + write bytes per second",

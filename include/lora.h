@@ -161,7 +161,10 @@ int32_t lora_pool_load(lora_pool *pool, int32_t adapter_id, int32_t slot,
                        const int32_t *rank, const float *scale,
                        int32_t src_on_device, void *stream, int32_t *slot_out);
 
-/* Forgets an adapter id; its slot becomes free.  UNKNOWN_ADAPTER if absent. */
+/* Forgets an adapter id; its slot becomes free and the slot's ranks on the
+ * device are zeroed with a blocking copy (so lora_build_routing_device sees it
+ * as holding no adapter); work still reading the slot must have finished.
+ * Errors: ARG, UNKNOWN_ADAPTER (not resident), HIP. */
 int32_t lora_pool_unload(lora_pool *pool, int32_t adapter_id);
 
 /* Slot of a resident id (UNKNOWN_ADAPTER if absent). */
@@ -266,6 +269,44 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
 /* Device pointer to the routing's per-token slot array (int32 [n_tokens]),
  * valid after the copy enqueued by lora_build_routing has run. */
 int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **dev_ptr_out);
+
+#define LORA_DEVICE_ROUTING_MAX_TOKENS 4096
+
+/*
+ * Routing of a decode batch built on the device, with no host planning and
+ * no host-device copy, so that one captured graph of this call and the
+ * compute calls serves any mix of adapters: the slot of each row is read from
+ * device memory when the graph runs (TensorFold PR #47, third commit message).
+ * A batch padded to a captured size gives each padded row its original's slot
+ * and x row; the padded row's y row then gets exactly its original's result
+ * (or the caller writes slot 0 there and the row is skipped).
+ *
+ *   tok_slot  device int32 [n_tokens]: the pool slot of each token row, 0 =
+ *             base; every row is a decode row.  Admission and id -> slot
+ *             resolution are the caller's (as lora_plan_routing does them).
+ *   n_tokens  0..min(max_tokens, LORA_DEVICE_ROUTING_MAX_TOKENS)
+ *
+ * One kernel on `stream` writes the same kinds of segment lora_build_routing
+ * writes for decode rows (decode segments, and gather segments for adapters
+ * with a slice rank >= LORA_GATHER_MIN_RANK), so every row's delta is
+ * bit-identical to the one a host-built routing gives.  A row whose slot is
+ * out of range or holds no adapter is never treated as base silently: it is
+ * left untouched and counted as invalid in the device counts.  The host only
+ * knows upper bounds afterwards: lora_routing_get_info reports n_active =
+ * n_tokens and segment counts that are bounds (the workspace is sized for
+ * them); the kernels read the exact counts from the device.  The routing can
+ * be used with any pool that holds adapters in every slot the building pool
+ * held them in, with the same ranks (MISMATCH otherwise, as with
+ * lora_build_routing).  Errors: ARG, CAPACITY (n_tokens too large), HIP.
+ */
+int32_t lora_build_routing_device(const lora_pool *pool, const int32_t *tok_slot,
+                                  int32_t n_tokens, lora_routing *routing, void *stream);
+
+/* Device pointer to int32 [8] counts of a device-built routing, written by its
+ * kernel: [0] active rows, [1] decode segments, [2] prefill segments (0),
+ * [3] gather segments, [4] rows whose slot held no adapter.  ARG if the
+ * routing was built on the host. */
+int32_t lora_routing_device_counts(const lora_routing *routing, const int32_t **dev_ptr_out);
 
 /* --------------------------------------------------------------- compute --
  * x:  [n_tokens][ldx] bf16 or fp16 (the lane's x_dtype), this GPU's input
