@@ -19,6 +19,14 @@ What it follows:
     added to the fp32 partial sum of the projection; a row of slot 0 is not
     read or written.
 
+  * expert LoRA of a mixture-of-experts layer -- xLLM PR #2014, "Not in this
+    PR" (the fused MoE expert LoRA delta, injected as a grouped GEMM): each
+    dispatched (token, expert) row of an expert projection takes the factors
+    of its token's adapter for that expert; the reading taken is that an
+    adapter carries one LoRA pair per expert it edits, and a row whose token
+    runs the base model, or whose adapter does not edit that expert, gets no
+    delta.
+
 Rows of deferred sequences are outside this batch: the oracle leaves them
 exactly as they were, like base-model rows.
 """
@@ -186,3 +194,31 @@ def workload_lane_delta(workload, lane_name, max_loras=None, rows=None):
     d = lane_delta(lane.x, lane.spec.x_dtype, tok, factors, lane.spec.h_out,
                    lane.spec.a_col0, lane.spec.h_in, rows)
     return d, tok, admitted
+
+
+def moe_lane_delta(workload, lane_name, rows=None):
+    """fp64 delta of one expert projection of a MoE layer.
+
+    Dispatched row p is token row_token[p] sent to expert row_expert[p]; it
+    takes the factors of (that token's adapter, that expert) when the adapter
+    edits the expert, and no delta otherwise.
+
+    Returns (delta float64 [len(rows), H_out], row_pair) where row_pair[p] is
+    the (adapter id, expert) whose factors row p takes, or None.
+    """
+    lane = workload.lanes[lane_name]
+    n = len(workload.row_token)
+    pair_key = {}
+    row_key = np.zeros(n, dtype=np.int64)
+    row_pair = [None] * n
+    for p in range(n):
+        aid = int(workload.tok_adapter[workload.row_token[p]])
+        pair = (aid, int(workload.row_expert[p]))
+        if aid != 0 and pair in workload.factors:
+            row_key[p] = pair_key.setdefault(pair, len(pair_key) + 1)
+            row_pair[p] = pair
+    factors = {key: [(sf.A, sf.B, sf.rank, sf.scale) for sf in workload.factors[pair][lane_name]]
+               for pair, key in pair_key.items()}
+    d = lane_delta(lane.x, lane.spec.x_dtype, row_key, factors, lane.spec.h_out,
+                   lane.spec.a_col0, lane.spec.h_in, rows)
+    return d, row_pair

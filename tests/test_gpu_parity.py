@@ -147,6 +147,26 @@ def test_one_launch_decode_delta_matches_split(lib, lane, mode):
     check_full(w, lane, ya, adm)
 
 
+# Fused QKV with an attention output gate (xLLM #2014, LoRAQKVParallelLinear,
+# q_has_gate): the q lane holds query and gate rows of 16 heads x 256, so the q
+# slice is 8192 wide next to 512-wide k and v slices (2 kv heads x 256).
+GATED_QKV = WorkloadSpec(
+    name="gated_qkv", seed=24,
+    lanes=(LaneSpec("qkv_gate", 2048, (8192, 512, 512)),),
+    n_adapters=4, ranks=(8, 16, 64, 5), rank_mode="list",
+    scale_mode="alpha", alpha=32.0, max_rank=64,
+    decode_rows=40, base_prob=0.25, prefill_seqs=2, prefill_len=(65, 140))
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("path", ["apply", "split"])
+def test_gated_q_lane_full_parity(lib, mode, path):
+    w = generate(GATED_QKV, mode=mode)
+    y, adm, info = run_lane(lib, w, "qkv_gate", path=path)
+    assert info["n_decode_segments"] > 0 and info["n_prefill_segments"] > 0
+    check_full(w, "qkv_gate", y, adm)
+
+
 # ------------------------------------------- full-size configs, sampled rows
 
 @pytest.mark.slow

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from workloads import (CONFIGS, WorkloadSpec, LaneSpec, generate, config_by_name,
-                       f32_to_bf16_bits, bf16_bits_to_f32)
+                       f32_to_bf16_bits, bf16_bits_to_f32, MoeSpec, generate_moe)
 from workloads.gen import f32_to_fp16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -234,3 +234,79 @@ def test_deferred_rows_untouched():
         if not ok:
             assert np.all(d[starts[s]:starts[s] + lens[s]] == 0.0)
     assert len(set(tok.tolist()) - {0}) == 8
+
+
+# ----------------------------------------------------- mixture-of-experts
+
+SMALL_MOE = MoeSpec(
+    name="small_moe", seed=31,
+    lanes=(LaneSpec("gate_up", 64, (48, 40)), LaneSpec("down", 48, (64,))),
+    n_experts=6, top_k=2, n_tokens=30, n_adapters=3, ranks=(4, 8, 3), max_rank=8,
+    token_input=("gate_up",), scale_mode="uniform", scale_range=(0.5, 3.0),
+    base_prob=0.2, expert_coverage=0.7)
+
+
+def _dense_row(w, lane, p, pair):
+    """scale * (B @ A) @ x of one dispatched row, as a dense product."""
+    L = w.lanes[lane]
+    x = bf16_bits_to_f32(L.x[p]).astype(np.float64)
+    out = []
+    for sf in w.factors[pair][lane]:
+        A = bf16_bits_to_f32(sf.A).astype(np.float64)[:sf.rank]
+        B = bf16_bits_to_f32(sf.B).astype(np.float64)[:, :sf.rank]
+        out.append(sf.scale * (np.matmul(B, A) @ x))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["gate_up", "down"])
+def test_moe_rows_match_dense_expert_product(lane, mode):
+    """Every dispatched row equals the dense product of its (adapter, expert)
+    factors, found here from the dispatch table directly; rows of base tokens
+    and of experts the adapter does not edit are exactly zero."""
+    w = generate_moe(SMALL_MOE, mode=mode)
+    d, row_pair = oracle.moe_lane_delta(w, lane)
+    n_edit = n_base = n_unedited = 0
+    for p in range(w.n_rows):
+        aid = int(w.tok_adapter[w.row_token[p]])
+        e = int(w.row_expert[p])
+        if aid == 0 or (aid, e) not in w.factors:
+            assert row_pair[p] is None and not d[p].any()
+            n_base += aid == 0
+            n_unedited += aid != 0
+            continue
+        assert row_pair[p] == (aid, e)
+        ref = _dense_row(w, lane, p, (aid, e))
+        if mode == "int":
+            assert np.array_equal(d[p], ref)
+        else:
+            assert np.allclose(d[p], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+        n_edit += 1
+    assert n_edit > 0 and n_base > 0 and n_unedited > 0
+
+
+def test_moe_dispatch_structure():
+    """top_k distinct experts per token, rows grouped by expert then token,
+    and the gate_up input of every row of a token is that token's row."""
+    w = generate_moe(SMALL_MOE)
+    k = SMALL_MOE.top_k
+    assert w.n_rows == SMALL_MOE.n_tokens * k
+    key = w.row_expert.astype(np.int64) * SMALL_MOE.n_tokens + w.row_token
+    assert np.all(np.diff(key) > 0)
+    for t in range(SMALL_MOE.n_tokens):
+        rows = np.nonzero(w.row_token == t)[0]
+        assert len(rows) == k and len(set(w.row_expert[rows].tolist())) == k
+        x = w.lanes["gate_up"].x
+        assert all(np.array_equal(x[rows[0]], x[r]) for r in rows)
+
+
+def test_moe_row_order_does_not_matter():
+    """Permuting the dispatched rows permutes the oracle's delta exactly."""
+    w = generate_moe(SMALL_MOE)
+    d, _ = oracle.moe_lane_delta(w, "down")
+    perm = np.random.default_rng(3).permutation(w.n_rows)
+    w.row_token, w.row_expert = w.row_token[perm], w.row_expert[perm]
+    L = w.lanes["down"]
+    L.x, L.y0 = L.x[perm], L.y0[perm]
+    dp, _ = oracle.moe_lane_delta(w, "down")
+    assert np.array_equal(dp, d[perm])

@@ -10,9 +10,11 @@ from .gen import (
     Workload, Lane, SliceFactors, Adapter,
     generate, f32_to_bf16_bits, bf16_bits_to_f32,
 )
+from .moe import MoeSpec, MoeWorkload, generate_moe, MOE_CONFIGS, moe_config_by_name
 
 __all__ = [
     "CONFIGS", "config_by_name", "LaneSpec", "WorkloadSpec",
     "Workload", "Lane", "SliceFactors", "Adapter",
     "generate", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "MoeSpec", "MoeWorkload", "generate_moe", "MOE_CONFIGS", "moe_config_by_name",
 ]
