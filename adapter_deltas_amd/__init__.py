@@ -9,7 +9,8 @@ from .lora import (
     lora_pool_load, lora_pool_unload, lora_pool_slot_of, lora_routing_bytes,
     lora_routing_create, lora_routing_destroy, lora_build_routing, lora_routing_get_info,
     lora_plan_routing,
-    lora_routing_token_slots, lora_build_routing_device, lora_routing_device_counts,
+    lora_routing_token_slots, lora_build_routing_device, lora_build_routing_moe,
+    lora_routing_device_counts, moe_slot,
     lora_shrink, lora_expand, lora_workspace_bytes,
     lora_delta_apply,
 )
@@ -18,4 +19,4 @@ _lib.load()
 
 __all__ = [n for n in dir() if n.startswith(("lora_", "Lora")) or n in (
     "Pool", "Routing", "make_desc", "workspace_for", "shrink", "expand", "delta_apply",
-    "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS")]
+    "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS", "moe_slot")]

@@ -30,7 +30,8 @@ EXPORTS = (
     "lora_pool_unload", "lora_pool_slot_of",
     "lora_routing_bytes", "lora_routing_create", "lora_routing_destroy",
     "lora_build_routing", "lora_routing_get_info", "lora_plan_routing",
-    "lora_routing_token_slots", "lora_build_routing_device", "lora_routing_device_counts",
+    "lora_routing_token_slots", "lora_build_routing_device", "lora_build_routing_moe",
+    "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
 )
 
@@ -92,6 +93,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_uint8)]),
         "lora_routing_token_slots": (I32, [P, PP]),
         "lora_build_routing_device": (I32, [P, P, I32, P, P]),
+        "lora_build_routing_moe": (I32, [P, P, I32, P, P, I32, I32, P, P]),
         "lora_routing_device_counts": (I32, [P, PP]),
         "lora_shrink": (I32, [P, P, P, I64, P, P]),
         "lora_expand": (I32, [P, P, P, P, I64, P]),

@@ -190,12 +190,16 @@ __device__ __forceinline__ void bitonic_sort(uint32_t (&k)[4], int n_sort, int t
 }
 
 // THREADS threads route up to 4 * THREADS rows.  Thread t holds the keys of
-// sorted positions 4t .. 4t + 3 in registers.
-template <int THREADS>
+// sorted positions 4t .. 4t + 3 in registers.  With MOE the rows are the
+// dispatched (token, expert) rows of an expert projection and `tok_slot`
+// holds each token's adapter slot; a row's slot is its (adapter, expert)
+// pool slot.
+template <int THREADS, bool MOE>
 __global__ __launch_bounds__(THREADS) void k_route_decode(
-    const int32_t *__restrict__ tok_slot, int n_tok, const int4 *__restrict__ rank_rows,
-    int max_slots, int max_dec, int max_gather, int32_t *__restrict__ seg,
-    int32_t *__restrict__ rows, int32_t *__restrict__ tok, int32_t *__restrict__ counts)
+    const int32_t *__restrict__ tok_slot, int n_tok, MoeDispatch moe,
+    const int4 *__restrict__ rank_rows, int max_slots, int max_dec, int max_gather,
+    int32_t *__restrict__ seg, int32_t *__restrict__ rows, int32_t *__restrict__ tok,
+    int32_t *__restrict__ counts)
 {
     constexpr int E = kRouteRowsPerThread;
     constexpr int ROWS = THREADS * E;
@@ -214,33 +218,60 @@ __global__ __launch_bounds__(THREADS) void k_route_decode(
 
     // Keys path << 28 | slot << 12 | row, one per row; base and invalid rows
     // get kNoKey and sort last.  All slot loads, then all rank loads (rank
-    // row 0 is zero), so the two dependent global reads are paid once.
+    // row 0 is zero), so the dependent global reads are paid once each.
+    // sl = -1 marks a row that names no valid slot.
     int sl[E];
-    int4 rk[E];
+    if constexpr (MOE) {
+        int t[E], x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) sl[e] = p0 + e < n_tok ? tok_slot[p0 + e] : 0;
+        for (int e = 0; e < E; ++e) {
+            const bool row = p0 + e < n_tok;
+            t[e] = row ? moe.row_token[p0 + e] : 0;
+            x[e] = row ? moe.row_expert[p0 + e] : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool row = p0 + e < n_tok;
+            const bool t_ok = t[e] >= 0 && t[e] < moe.n_tokens;
+            const int a = row && t_ok ? tok_slot[t[e]] : 0;
+            const bool ok = t_ok && x[e] >= 0 && x[e] < moe.n_experts && a >= 0 &&
+                            a <= moe.n_adapter_slots;
+            sl[e] = !row ? 0 : !ok ? -1 : a == 0 ? 0 : (a - 1) * moe.n_experts + x[e] + 1;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) sl[e] = p0 + e < n_tok ? tok_slot[p0 + e] : 0;
+    }
+    int4 rk[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) rk[e] = rank_rows[sl[e] >= 1 && sl[e] <= max_slots ? sl[e] : 0];
     uint32_t k[E];
-    int n_ok = 0, n_ok_decode = 0, n_nonzero = 0;
+    int n_ok = 0, n_ok_decode = 0, n_bad = 0, n_unedited = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int i = p0 + e, s = sl[e];
         const int4 r = rk[e];
-        // a slot holds an adapter iff its slice-0 rank is set
+        // a slot holds factors iff its slice-0 rank is set
         const bool g = max(max(r.x, r.y), max(r.z, r.w)) >= kGatherMinRank;
-        const bool ok = s >= 1 && s <= max_slots && r.x > 0 && (g ? max_gather : max_dec) > 0;
+        const bool in_range = s >= 1 && s <= max_slots;
+        const bool ok = in_range && r.x > 0 && (g ? max_gather : max_dec) > 0;
         if (i < n_tok) tok[i] = ok ? s : 0;
         k[e] = ok ? (g ? gather_key : 0u) | (uint32_t)s << kRowBits | (uint32_t)i : kNoKey;
         n_ok += ok;
         n_ok_decode += ok && !g;
-        n_nonzero += s != 0;
+        // an (adapter, expert) slot without factors: the adapter leaves that
+        // expert alone; any other slot that is not 0 and not usable is invalid
+        const bool unedited = MOE && in_range && r.x == 0;
+        n_unedited += unedited;
+        n_bad += s != 0 && !ok && !unedited;
     }
     int2 cnt;
-    block_exclusive_sum2<NW>(make_int2(n_ok | n_ok_decode << 16, n_nonzero), lane, wave, part2, cnt);
+    block_exclusive_sum2<NW>(make_int2(n_ok | n_ok_decode << 16, n_bad | n_unedited << 16), lane,
+                             wave, part2, cnt);
     const int na = cnt.x & 0xffff;          // active rows
     const int fg = cnt.x >> 16;             // decode rows, sorted before the gathered ones
-    const int n_invalid = cnt.y - na;
+    const int n_invalid = cnt.y & 0xffff;
+    const int n_unedited_rows = cnt.y >> 16;
 
     bitonic_sort<ROWS>(k, n_sort, tid, lane, key);
     __syncthreads();
@@ -344,14 +375,16 @@ __global__ __launch_bounds__(THREADS) void k_route_decode(
         counts[kCntPrefill] = 0;
         counts[kCntGather] = total - n_dec;
         counts[kCntInvalid] = n_invalid;
+        counts[kCntUnedited] = n_unedited_rows;
     }
 }
 
 }  // namespace
 
-hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const int32_t *rank_tab,
-                               int max_slots, int max_dec, int max_gather, int32_t *seg,
-                               int32_t *rows, int32_t *tok, int32_t *counts, hipStream_t s)
+hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDispatch *moe,
+                               const int32_t *rank_tab, int max_slots, int max_dec,
+                               int max_gather, int32_t *seg, int32_t *rows, int32_t *tok,
+                               int32_t *counts, hipStream_t s)
 {
     static_assert(kMetaStride == 4, "one int4 of ranks per slot");
     static_assert(kSegWords == 16, "a descriptor is four int4 values");
@@ -359,15 +392,17 @@ hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const int32_t
     if (reinterpret_cast<uintptr_t>(rank_tab) % 16 || reinterpret_cast<uintptr_t>(seg) % 16)
         return hipErrorInvalidValue;
     const int4 *rr = reinterpret_cast<const int4 *>(rank_tab);
+    const MoeDispatch d = moe ? *moe : MoeDispatch{nullptr, nullptr, 0, 1, 0};
+    auto launch = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), 0, s, tok_slot, n_tok, d, rr,
+                           max_slots, max_dec, max_gather, seg, rows, tok, counts);
+    };
     if (n_tok <= 64 * kRouteRowsPerThread)
-        hipLaunchKernelGGL(k_route_decode<64>, dim3(1), dim3(64), 0, s, tok_slot, n_tok, rr,
-                           max_slots, max_dec, max_gather, seg, rows, tok, counts);
+        moe ? launch(k_route_decode<64, true>, 64) : launch(k_route_decode<64, false>, 64);
     else if (n_tok <= 256 * kRouteRowsPerThread)
-        hipLaunchKernelGGL(k_route_decode<256>, dim3(1), dim3(256), 0, s, tok_slot, n_tok, rr,
-                           max_slots, max_dec, max_gather, seg, rows, tok, counts);
+        moe ? launch(k_route_decode<256, true>, 256) : launch(k_route_decode<256, false>, 256);
     else
-        hipLaunchKernelGGL(k_route_decode<1024>, dim3(1), dim3(1024), 0, s, tok_slot, n_tok, rr,
-                           max_slots, max_dec, max_gather, seg, rows, tok, counts);
+        moe ? launch(k_route_decode<1024, true>, 1024) : launch(k_route_decode<1024, false>, 1024);
     return hipGetLastError();
 }
 

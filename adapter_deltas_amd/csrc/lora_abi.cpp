@@ -806,15 +806,15 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
     return LORA_OK;
 }
 
-int32_t lora_build_routing_device(const lora_pool *p, const int32_t *tok_slot,
-                                  int32_t n_tokens, lora_routing *r, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Routing of n_tokens decode rows built on the device (rows = tokens, or the
+// dispatched rows of a MoE layer when moe is set).
+int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_t n_tokens,
+                             const MoeDispatch *moe, lora_routing *r, void *stream)
 {
-    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
-    if (n_tokens < 0) return fail(LORA_ERR_SHAPE, "n_tokens < 0");
-    if (n_tokens > r->max_tokens || n_tokens > LORA_DEVICE_ROUTING_MAX_TOKENS)
-        return fail(LORA_ERR_CAPACITY, "n_tokens=%d > max_tokens=%d or > %d", n_tokens,
-                    r->max_tokens, LORA_DEVICE_ROUTING_MAX_TOKENS);
-    if (n_tokens > 0 && !tok_slot) return fail(LORA_ERR_ARG, "tok_slot is null");
     // Bounds: a slot's decode rows make ceil(n / 8) decode or ceil(n / 64)
     // gather segments, so either kind has at most n_tokens / size + slots.
     // A kind no resident adapter takes gets no room (and no launch).
@@ -837,9 +837,9 @@ int32_t lora_build_routing_device(const lora_pool *p, const int32_t *tok_slot,
     if (off_counts + kCntWords > r->dev_words)
         return fail(LORA_ERR_CAPACITY, "routing memory too small for %d tokens", n_tokens);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_route_decode(tok_slot, n_tokens, p->rank_tab, p->desc.max_slots, max_dec,
-                                       max_gather, r->dev, r->dev + off_row, r->dev + off_tok,
-                                       r->dev + off_counts, st);
+    hipError_t e = launch_route_decode(tok_slot, n_tokens, moe, p->rank_tab, p->desc.max_slots,
+                                       max_dec, max_gather, r->dev, r->dev + off_row,
+                                       r->dev + off_tok, r->dev + off_counts, st);
     if (e != hipSuccess) return hip_fail(e, "routing kernel launch");
     r->off_seg = 0;
     r->off_row = (int32_t)off_row;
@@ -867,6 +867,45 @@ int32_t lora_build_routing_device(const lora_pool *p, const int32_t *tok_slot,
     I.n_segments = max_dec + max_gather;
     I.n_seqs = I.n_admitted_seqs = n_tokens;
     return LORA_OK;
+}
+
+int32_t check_device_rows(const lora_pool *p, lora_routing *r, int32_t n_rows)
+{
+    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
+    if (n_rows < 0) return fail(LORA_ERR_SHAPE, "row count < 0");
+    if (n_rows > r->max_tokens || n_rows > LORA_DEVICE_ROUTING_MAX_TOKENS)
+        return fail(LORA_ERR_CAPACITY, "%d rows > max_tokens=%d or > %d", n_rows,
+                    r->max_tokens, LORA_DEVICE_ROUTING_MAX_TOKENS);
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_build_routing_device(const lora_pool *p, const int32_t *tok_slot,
+                                  int32_t n_tokens, lora_routing *r, void *stream)
+{
+    if (int32_t rc = check_device_rows(p, r, n_tokens)) return rc;
+    if (n_tokens > 0 && !tok_slot) return fail(LORA_ERR_ARG, "tok_slot is null");
+    return build_routing_device(p, tok_slot, n_tokens, nullptr, r, stream);
+}
+
+int32_t lora_build_routing_moe(const lora_pool *p, const int32_t *tok_slot, int32_t n_tokens,
+                               const int32_t *row_token, const int32_t *row_expert,
+                               int32_t n_rows, int32_t n_experts, lora_routing *r,
+                               void *stream)
+{
+    if (int32_t rc = check_device_rows(p, r, n_rows)) return rc;
+    if (n_tokens < 0) return fail(LORA_ERR_SHAPE, "n_tokens < 0");
+    if (n_experts < 1 || p->desc.max_slots % n_experts)
+        return fail(LORA_ERR_SHAPE, "n_experts=%d must be >= 1 and divide max_slots=%d",
+                    n_experts, p->desc.max_slots);
+    if (n_rows > 0 && (!row_token || !row_expert || (n_tokens > 0 && !tok_slot)))
+        return fail(LORA_ERR_ARG, "tok_slot, row_token or row_expert is null");
+    const MoeDispatch moe{row_token, row_expert, n_tokens, n_experts,
+                          p->desc.max_slots / n_experts};
+    return build_routing_device(p, tok_slot, n_rows, &moe, r, stream);
 }
 
 int32_t lora_routing_device_counts(const lora_routing *r, const int32_t **dev_ptr_out)

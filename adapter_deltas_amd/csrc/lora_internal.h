@@ -77,7 +77,18 @@ struct RoutingDev {
 };
 // Entries of a device-built routing's counts.
 enum DeviceCount : int { kCntActive = 0, kCntDecode = 1, kCntPrefill = 2, kCntGather = 3,
-                         kCntInvalid = 4, kCntWords = 8 };
+                         kCntInvalid = 4, kCntUnedited = 5, kCntWords = 8 };
+
+// Dispatch table of a MoE layer's expert rows, for device routing: row p is
+// token row_token[p] sent to expert row_expert[p]; its pool slot is that of
+// (the token's adapter slot a, the expert e): (a - 1) * n_experts + e + 1.
+struct MoeDispatch {
+    const int32_t *row_token;
+    const int32_t *row_expert;
+    int n_tokens;
+    int n_experts;
+    int n_adapter_slots;   // max_slots / n_experts
+};
 
 // ---- launchers (kernels_*.hip) ----
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
@@ -96,9 +107,10 @@ hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               bool gather, int seg_begin, int n_seg, int group,
                               int tiles_per_slice, int max_rank, const float *v, float *y,
                               int64_t ldy, hipStream_t s);
-hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const int32_t *rank_tab,
-                               int max_slots, int max_dec, int max_gather, int32_t *seg,
-                               int32_t *rows, int32_t *tok, int32_t *counts, hipStream_t s);
+hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDispatch *moe,
+                               const int32_t *rank_tab, int max_slots, int max_dec,
+                               int max_gather, int32_t *seg, int32_t *rows, int32_t *tok,
+                               int32_t *counts, hipStream_t s);
 hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
                          int rank, int rank_pad, int h_in, hipStream_t s);
 hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,

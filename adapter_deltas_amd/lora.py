@@ -208,6 +208,21 @@ def lora_build_routing_device(pool, tok_slot, n_tokens, routing, stream=None) ->
                                             _stream(stream)))
 
 
+def lora_build_routing_moe(pool, tok_slot, n_tokens, row_token, row_expert, n_rows, n_experts,
+                           routing, stream=None) -> None:
+    """Device int32 tensors (or addresses): adapter slot per token, and the
+    token and expert of each dispatched row."""
+    _check(_lib().lora_build_routing_moe(pool, _ptr(tok_slot), n_tokens, _ptr(row_token),
+                                         _ptr(row_expert), n_rows, n_experts, routing,
+                                         _stream(stream)))
+
+
+def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:
+    """Pool slot of (adapter slot, expert) in an expert projection's pool
+    (LORA_MOE_SLOT)."""
+    return (adapter_slot - 1) * n_experts + expert + 1
+
+
 def lora_routing_device_counts(routing) -> int:
     p = ctypes.c_void_p()
     _check(_lib().lora_routing_device_counts(routing, ctypes.byref(p)))
@@ -304,6 +319,13 @@ class Routing:
         tensor of per-row slots (0 = base)."""
         lora_build_routing_device(pool.handle, tok_slot, int(tok_slot.numel()), self.handle,
                                   stream)
+
+    def build_moe(self, pool: Pool, tok_slot, row_token, row_expert, n_experts, stream=None):
+        """Routing of a MoE layer's dispatched rows built on the device from
+        int32 device tensors: adapter slot per token, token and expert per row."""
+        lora_build_routing_moe(pool.handle, tok_slot, int(tok_slot.numel()), row_token,
+                               row_expert, int(row_token.numel()), n_experts, self.handle,
+                               stream)
 
     def device_counts(self):
         """The int32 [8] device counts of a device-built routing, as a tensor

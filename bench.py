@@ -221,6 +221,228 @@ def stream_copy_gbs(dev, nbytes=1 << 30, reps=10):
     return gbs
 
 
+def moe_algorithmic(w, lane_name):
+    """algorithmic() for one expert projection of a MoE workload: the rows are
+    the dispatched (token, expert) rows, the factors those of each distinct
+    (adapter, expert) pair the batch uses."""
+    L = w.lanes[lane_name].spec
+    aid = w.tok_adapter[w.row_token]
+    pairs = {}
+    for a, e in zip(aid.tolist(), w.row_expert.tolist()):
+        if a and (a, e) in w.factors:
+            pairs[(a, e)] = pairs.get((a, e), 0) + 1
+    act = sum(pairs.values())
+    sb = act * L.h_in * 2 + 4 * w.n_rows
+    eb = act * 8 * L.h_out_total
+    sf_ = ef = 0
+    for pair, n in pairs.items():
+        for sf, hj in zip(w.factors[pair][lane_name], L.h_out):
+            sb += 2 * sf.rank * L.h_in
+            eb += 2 * sf.rank * hj
+            sf_ += n * 2 * sf.rank * L.h_in
+            ef += n * 2 * sf.rank * hj
+    return {"shrink": (sb, sf_), "expand": (eb, ef), "active": act, "pairs": len(pairs)}
+
+
+def main_moe(args, spec):
+    """The expert LoRA delta of MoE layers: per layer, the dispatched rows are
+    routed on the device to their (adapter, expert) pool slots, then the delta
+    is applied on every expert projection of the layer."""
+    import torch
+    import adapter_deltas_amd as m
+    from workloads import generate_moe
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import to_device_x, to_device_y
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {spec.name}")
+    w = generate_moe(spec)
+    lanes = [l.name for l in spec.lanes]
+    E = spec.n_experts
+    aslot = {aid: i + 1 for i, aid in enumerate(w.adapter_ids)}
+    fac = {ln: [(aid * E + e + 1, m.moe_slot(aslot[aid], e, E),
+                 [torch.from_numpy(sf.A.view(np.int16)).to(dev) for sf in per[ln]],
+                 [torch.from_numpy(sf.B.view(np.int16)).to(dev) for sf in per[ln]],
+                 [sf.rank for sf in per[ln]], [sf.scale for sf in per[ln]])
+                for (aid, e), per in w.factors.items()] for ln in lanes}
+
+    def make_layer():
+        per = {}
+        for ln in lanes:
+            L = w.lanes[ln].spec
+            pool = m.Pool(L.h_in, L.h_out, spec.n_adapters * E, spec.max_rank, L.x_dtype,
+                          device=dev)
+            for pid, slot, A, B, rk, sc in fac[ln]:
+                pool.load(pid, A, B, rk, sc, a_col0=L.a_col0, slot=slot)
+            per[ln] = (pool, to_device_x(w.lanes[ln].x, dev), to_device_y(w.lanes[ln].y0, dev))
+        return per
+    layers = [make_layer()]
+    layer_bytes = sum(p.nbytes + x.numel() * 2 + y.numel() * 4
+                      for (p, x, y) in layers[0].values())
+    if args.layers <= 0:
+        args.layers = max(4, -(-(1 << 30) // layer_bytes))
+    log(f"building {args.layers} layers x {len(lanes)} lanes, {layer_bytes} bytes each")
+    while len(layers) < args.layers:
+        layers.append(make_layer())
+    del fac
+    d32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    tok_slot = d32([aslot[int(a)] if a else 0 for a in w.tok_adapter])
+    row_token, row_expert = d32(w.row_token), d32(w.row_expert)
+    R = w.n_rows
+    first = lanes[0]
+    routing = m.Routing(R, R, device=dev)
+    routing.build_moe(layers[0][first][0], tok_slot, row_token, row_expert, E)
+    ws = {ln: m.workspace_for(layers[0][ln][0], routing, dev) for ln in lanes}
+    torch.cuda.synchronize()
+    counts = routing.device_counts().cpu().numpy()
+    act_rows = int(counts[0])
+
+    def step():
+        for per in layers:
+            routing.build_moe(per[first][0], tok_slot, row_token, row_expert, E)
+            for ln in lanes:
+                pool, x, y = per[ln]
+                m.delta_apply(pool, routing, x, y, ws[ln])
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = wall * 1e3 / args.steps
+    delta_rows = act_rows * len(lanes) * args.layers
+    value = delta_rows / (ms_per_step * 1e-3)
+
+    side = torch.cuda.Stream()
+
+    def replay_us(body):
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            body()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.graph_reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) * 1e3 / args.graph_reps
+
+    vbuf = {ln: torch.empty(R * layers[0][ln][0].v_stride, dtype=torch.float32, device=dev)
+            for ln in lanes}
+
+    def per_call_us(call):
+        def body():
+            for per in layers:
+                for ln in lanes:
+                    pool, x, y = per[ln]
+                    call(ln, pool, x, y)
+        return replay_us(body) / (args.layers * len(lanes))
+
+    log("graph replay timing")
+    routing.build_moe(layers[0][first][0], tok_slot, row_token, row_expert, E)
+    apply_us = per_call_us(lambda ln, pool, x, y: m.delta_apply(pool, routing, x, y, ws[ln]))
+    shrink_us = per_call_us(lambda ln, pool, x, y: m.shrink(pool, routing, x, vbuf[ln]))
+    expand_us = per_call_us(lambda ln, pool, x, y: m.expand(pool, routing, vbuf[ln], y))
+    step_us = replay_us(step)
+
+    alg = {"shrink": [0, 0], "expand": [0, 0]}
+    pairs = 0
+    for ln in lanes:
+        a = moe_algorithmic(w, ln)
+        pairs = a["pairs"]
+        for k in ("shrink", "expand"):
+            alg[k][0] += a[k][0] / len(lanes)
+            alg[k][1] += a[k][1] / len(lanes)
+    dominant = "expand" if expand_us >= shrink_us else "shrink"
+    dom_us = expand_us if dominant == "expand" else shrink_us
+    dom_bytes = alg[dominant][0]
+    achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
+    total_bytes = alg["shrink"][0] + alg["expand"][0]
+    info = routing.info()
+
+    log(f"cpu baseline ~{args.cpu_seconds}s")
+    import oracle
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for ln in lanes:
+            oracle.moe_lane_delta(w, ln)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    cpu_dt = time.perf_counter() - t0
+    cpu_rate = act_rows * len(lanes) * reps / cpu_dt
+
+    out = {
+        "metric": "LoRA-delta tokens/s + achieved HBM GB/s fraction of peak, mixed-adapter decode",
+        "value": round(value, 1),
+        "unit": "delta tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x/A/B, fp32 sums",
+        "data": "synthetic (seeded numpy PCG64, values and dispatch structure of the workload)",
+        "config": {
+            "workload": f"{spec.name}: {spec.description}",
+            "lanes": {ln: [w.lanes[ln].spec.h_in, list(w.lanes[ln].spec.h_out)] for ln in lanes},
+            "tokens": spec.n_tokens, "dispatched_rows": R, "active_rows": act_rows,
+            "distinct_adapter_expert_pairs": pairs,
+            "layers_per_step": args.layers, "layer_buffer_bytes": layer_bytes,
+            "step": "per layer: MoE routing on the device, then delta_apply on each "
+                    "expert projection",
+        },
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "graph_step_ms": round(step_us * 1e-3, 4),
+        "roofline": {
+            "kernel": call_kernels(dominant, info),
+            "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(spec.name, dominant),
+            "algorithmic_bytes_per_launch": int(dom_bytes),
+            "us_per_launch": round(dom_us, 3),
+        },
+        "per_lane_layer": {
+            "delta_apply_us": round(apply_us, 3),
+            "shrink_us": round(shrink_us, 3), "expand_us": round(expand_us, 3),
+            "algorithmic_bytes": int(total_bytes),
+            "delta_apply_gbs": round(total_bytes / (apply_us * 1e-6) / 1e9, 1),
+            "shrink_gbs": round(alg["shrink"][0] / (shrink_us * 1e-6) / 1e9, 1),
+            "expand_gbs": round(alg["expand"][0] / (expand_us * 1e-6) / 1e9, 1),
+            "flops": int(alg["shrink"][1] + alg["expand"][1]),
+        },
+        "cpu_baseline": {
+            "value": round(cpu_rate, 1), "unit": "delta tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 oracle over the whole batch ({act_rows} active dispatched rows "
+                      f"x {len(lanes)} lanes), {reps} repetitions in {cpu_dt:.1f} s",
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +482,12 @@ def main():
               "(each GPU applies the delta to its own rows or its own column share "
               "independently); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    from workloads import MOE_CONFIGS
+    moe = {c.name: c for c in MOE_CONFIGS}
+    if args.config in moe:
+        main_moe(args, moe[args.config])
+        return
 
     import torch
     import adapter_deltas_amd as m

@@ -302,10 +302,47 @@ int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **de
 int32_t lora_build_routing_device(const lora_pool *pool, const int32_t *tok_slot,
                                   int32_t n_tokens, lora_routing *routing, void *stream);
 
+/*
+ * Expert LoRA of a mixture-of-experts layer (xLLM PR #2014, "Not in this PR":
+ * the fused MoE expert LoRA delta, a grouped GEMM over experts and adapters).
+ * An adapter that edits the experts holds one LoRA pair per expert.  A pool
+ * of an expert projection holds the pair of (adapter slot a, expert e) in
+ * slot LORA_MOE_SLOT(a, e, n_experts); its max_slots is a multiple of
+ * n_experts (n_experts times the adapter slots).
+ */
+#define LORA_MOE_SLOT(adapter_slot, expert, n_experts) \
+    (((adapter_slot) - 1) * (n_experts) + (expert) + 1)
+
+/*
+ * Routing of the dispatched rows of a MoE layer's expert projection, built on
+ * the device like lora_build_routing_device (same limits, same segments, same
+ * bit-exactness), for decode batches.
+ *
+ *   tok_slot    device int32 [n_tokens]: adapter slot of each token (0 = base)
+ *   row_token   device int32 [n_rows]: token of each dispatched row
+ *   row_expert  device int32 [n_rows]: expert of each dispatched row
+ *   n_rows      0..min(max_tokens, LORA_DEVICE_ROUTING_MAX_TOKENS)
+ *   n_experts   >= 1, divides the pool's max_slots
+ *
+ * Row p takes the pair in slot LORA_MOE_SLOT(tok_slot[row_token[p]],
+ * row_expert[p], n_experts).  x and y of the compute calls are indexed by
+ * dispatched row (the caller's gathered expert inputs and the expert outputs
+ * before the weighted combine).  A row of a base token is skipped; a row
+ * whose adapter holds no pair for its expert is skipped and counted as
+ * unedited (the adapter leaves that expert alone); a row naming a token,
+ * expert or adapter slot out of range is skipped and counted as invalid.
+ * Errors: ARG, SHAPE (n_experts), CAPACITY, HIP.
+ */
+int32_t lora_build_routing_moe(const lora_pool *pool, const int32_t *tok_slot,
+                               int32_t n_tokens, const int32_t *row_token,
+                               const int32_t *row_expert, int32_t n_rows, int32_t n_experts,
+                               lora_routing *routing, void *stream);
+
 /* Device pointer to int32 [8] counts of a device-built routing, written by its
  * kernel: [0] active rows, [1] decode segments, [2] prefill segments (0),
- * [3] gather segments, [4] rows whose slot held no adapter.  ARG if the
- * routing was built on the host. */
+ * [3] gather segments, [4] rows whose slot held no adapter (invalid), [5] MoE
+ * rows whose adapter does not edit their expert.  ARG if the routing was
+ * built on the host. */
 int32_t lora_routing_device_counts(const lora_routing *routing, const int32_t **dev_ptr_out);
 
 /* --------------------------------------------------------------- compute --

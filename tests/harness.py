@@ -85,3 +85,28 @@ def to_device_x(x_bits, device="cuda"):
 def to_device_y(y, device="cuda"):
     import torch
     return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(device)
+
+
+def load_moe_pool(Pool, workload, lane_name, adapter_slot=None, device="cuda"):
+    """Pool of one expert projection of a MoE workload: the pair of (adapter,
+    expert) in slot moe_slot(adapter slot, expert, n_experts).
+
+    adapter_slot: registry id -> adapter slot (default: 1 + adapter index).
+    Returns (pool, tok_slot int32 [n_tokens] of adapter slots, 0 = base)."""
+    from adapter_deltas_amd import moe_slot
+    spec = workload.spec
+    E = spec.n_experts
+    ids = workload.adapter_ids
+    if adapter_slot is None:
+        adapter_slot = {aid: i + 1 for i, aid in enumerate(ids)}
+    n_slots = max(adapter_slot.values())
+    lane = workload.lanes[lane_name].spec
+    pool = Pool(lane.h_in, lane.h_out, n_slots * E, spec.max_rank, lane.x_dtype, device=device)
+    for (aid, e), per_lane in workload.factors.items():
+        sl = per_lane[lane_name]
+        pool.load(aid * E + e + 1, [s.A for s in sl], [s.B for s in sl], [s.rank for s in sl],
+                  [s.scale for s in sl], a_col0=lane.a_col0,
+                  slot=moe_slot(adapter_slot[aid], e, E))
+    tok_slot = np.array([adapter_slot[int(a)] if a else 0 for a in workload.tok_adapter],
+                        dtype=np.int32)
+    return pool, tok_slot
