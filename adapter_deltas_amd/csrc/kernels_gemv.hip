@@ -116,17 +116,18 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
 }
 
 // Shrink and expand of decode segments in one launch, for ranks up to
-// kFusedMaxRank and slices of at most kFusedMaxTiles column tiles.  A task is the expand's (segment, slice, 512 columns); its
+// kFusedMaxRank.  A task is the expand's (segment, slice, 512 columns); its
 // eight waves first compute the segment's v for the slice exactly as
 // k_shrink_gemv does (wave w sums part w with shrink_part, the parts are
 // combined in the same order, v = fp32(scale * u)) into LDS, while the
 // task's y rows and first B blocks are already loading, and then expand one
 // segment row each with expand_rows.  Every value is the one the two kernels
 // produce, so the result is bit-identical to lora_shrink then lora_expand.
-// The column tiles of a slice recompute the same v: cheap next to a second
-// launch while the rank and the number of tiles are small (8 rows x 64
+// The column tiles of a slice recompute the same v and re-read the slice's
+// A: cheap next to a second launch while those bytes are few (8 rows x 64
 // columns: 6.2 -> 5.0 us per call), too costly for a 4096-wide slice (8
-// tiles: 12 -> 21 us).
+// tiles: 12 -> 21 us) or for many segments over a wide h_in (a MoE gate_up
+// with 768-wide slices: 35 -> 163 us).
 template <bool FP16X>
 __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev p, RoutingDev r,
                                                             int tiles_per_slice,

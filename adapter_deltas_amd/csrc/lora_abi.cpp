@@ -977,15 +977,23 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
                     (long long)workspace_bytes, (long long)need);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *v = static_cast<float *>(workspace);
-    // Decode segments of small ranks and narrow slices: shrink and expand in
-    // one launch, with the same arithmetic as the two kernels (bit-identical
-    // results).  Each column tile of a slice recomputes the segment's v, so
-    // wide slices keep the two launches.
+    // Decode segments of small ranks: shrink and expand in one launch, with
+    // the same arithmetic as the two kernels (bit-identical results).  Each
+    // column tile of a slice recomputes the segment's v, re-reading the
+    // slice's A; the one launch is taken while those extra bytes stay below
+    // about a microsecond of HBM time, the cost of the launch it saves.
     int hmax = 0;
-    for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
+    int64_t extra_tiles = 0;
+    for (int j = 0; j < p->desc.n_slices; ++j) {
+        hmax = std::max(hmax, p->desc.h_out[j]);
+        extra_tiles += (p->desc.h_out[j] + kExpandTile - 1) / kExpandTile - 1;
+    }
     const int tiles = (hmax + kExpandTile - 1) / kExpandTile;
-    const bool fused = r->info.n_decode_segments > 0 && tiles <= kFusedMaxTiles &&
-                       batch_max_rank(p, r) <= kFusedMaxRank;
+    const int kmax = batch_max_rank(p, r);
+    const int64_t extra_bytes = extra_tiles * kmax * (int64_t)p->desc.h_in * 2 *
+                                r->info.n_decode_segments;
+    const bool fused = r->info.n_decode_segments > 0 && kmax <= kFusedMaxRank &&
+                       extra_bytes <= kFusedMaxExtraBytes;
     if (fused) {
         hipError_t e = launch_delta_gemv(p->geom, pool_dev(p), routing_dev(r),
                                          r->info.n_decode_segments, tiles, x, ldx, y, ldy, st);

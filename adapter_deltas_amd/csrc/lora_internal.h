@@ -20,7 +20,7 @@ constexpr int kSubChunk = 512;                          // h_in elements per wav
 constexpr int kParts = 8;                               // interleaved h_in parts (one wave each)
 constexpr int kExpandTile = 512;                        // columns per decode expand task
 constexpr int kFusedMaxRank = 16;                       // ranks of the one-launch decode delta
-constexpr int kFusedMaxTiles = 2;                       // and its column tiles per slice
+constexpr int64_t kFusedMaxExtraBytes = 4 << 20;        // and the A bytes its tiles re-read
 constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
 #ifndef LORA_EXPAND_BLOCKS
 #define LORA_EXPAND_BLOCKS 8192
