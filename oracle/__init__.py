@@ -27,6 +27,13 @@ What it follows:
     runs the base model, or whose adapter does not edit that expert, gets no
     delta.
 
+  * A folded onto a transformed input -- TensorFold PR #47, first and third
+    commit messages: the packed shared expert's down projection reads a
+    rotated, scaled fp16 hidden state x' = M x, and its adapter's A is
+    rewritten once at load to read it.  The reading taken: the stored factor
+    is A' = A M^-1 (the loader is given fold = M^-1), computed exactly and
+    rounded to bf16, the factors' type, to nearest with ties to even.
+
 Rows of deferred sequences are outside this batch: the oracle leaves them
 exactly as they were, like base-model rows.
 """
@@ -222,3 +229,27 @@ def moe_lane_delta(workload, lane_name, rows=None):
     d = lane_delta(lane.x, lane.spec.x_dtype, row_key, factors, lane.spec.h_out,
                    lane.spec.a_col0, lane.spec.h_in, rows)
     return d, row_pair
+
+
+def bf16_nearest_bits(v):
+    """bf16 bits of the nearest bf16 value to each float64 in v, ties to
+    even (finite inputs): the significand is cut to 8 bits with rint, which
+    rounds halves to even; below the smallest normal the spacing is 2^-133."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    tiny = np.abs(v) < 2.0 ** -126
+    r = np.where(tiny, np.ldexp(np.rint(np.ldexp(v, 133)), -133), r)
+    # r is a bf16 value, so its binary32 form is exact; keep its upper half
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def fold_a(A_bits, a_col0, h_in, fold, rank, rounded=True):
+    """A' = A[:rank, a_col0:a_col0 + h_in] @ fold in fp64 (fold [h_in, >= h_in]
+    is read as [h_in, h_in]); returned as bf16 bits [rank, h_in] when
+    `rounded`, else the exact float64 product."""
+    A = (np.asarray(A_bits, dtype=np.uint16)[:rank, a_col0:a_col0 + h_in]
+         .astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    F = np.asarray(fold, dtype=np.float64)[:h_in, :h_in]
+    P = np.matmul(A, F)
+    return bf16_nearest_bits(P) if rounded else P

@@ -310,3 +310,60 @@ def test_moe_row_order_does_not_matter():
     L.x, L.y0 = L.x[perm], L.y0[perm]
     dp, _ = oracle.moe_lane_delta(w, "down")
     assert np.array_equal(dp, d[perm])
+
+
+# ------------------------------------------------------------ folded A
+
+from workloads import hadamard, draw_fold
+
+
+def test_bf16_nearest_matches_torch_on_binary32_values():
+    """For values that are exact in binary32, rounding to bf16 must agree
+    with torch's binary32 -> bfloat16 conversion (nearest, ties to even)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(41)
+    hi = np.arange(0, 1 << 16, dtype=np.uint32)
+    hi = hi[(hi & 0x7f80) != 0x7f80]                     # finite patterns only
+    lo = np.concatenate([[0, 0x8000, 0x7fff, 0x8001, 0xffff],
+                         rng.integers(0, 1 << 16, 11)]).astype(np.uint32)
+    u = (hi[:, None] << 16 | lo[None, :]).reshape(-1)
+    f = u.view(np.float32)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_nearest_bits(f.astype(np.float64)), ref)
+
+
+def test_fold_identity_and_signed_permutation_are_exact():
+    rng = np.random.default_rng(42)
+    r, n, c0 = 5, 64, 32
+    A = _bits(rng.standard_normal((r, c0 + n)) * 0.02)
+    assert np.array_equal(oracle.fold_a(A, c0, n, np.eye(n, dtype=np.float32), r), A[:, c0:])
+    perm = rng.permutation(n)
+    sign = rng.choice([-1.0, 1.0], n)
+    P = np.zeros((n, n), np.float32)
+    P[perm, np.arange(n)] = sign                          # column c takes column perm[c]
+    ref = bf16_bits_to_f32(A[:, c0:])[:, perm] * sign
+    assert np.array_equal(oracle.fold_a(A, c0, n, P, r), _bits(ref))
+
+
+def test_fold_reads_the_transformed_input():
+    """With fold = M^-1 the exact folded factor applied to M x gives A x;
+    M = diag(d) H / 8 with d powers of two, so every product is exact."""
+    rng = np.random.default_rng(43)
+    r, n = 6, 64
+    A = _bits(rng.standard_normal((r, n)) * 0.02)
+    d = 2.0 ** rng.integers(-2, 3, n)
+    H = hadamard(n) / 8.0
+    M = d[:, None] * H
+    fold = (H.T / d[None, :]).astype(np.float32)
+    x = bf16_bits_to_f32(_bits(rng.standard_normal((n, 3)))).astype(np.float64)
+    Af = oracle.fold_a(A, 0, n, fold, r, rounded=False)
+    ref = bf16_bits_to_f32(A).astype(np.float64) @ x
+    assert np.allclose(Af @ (M @ x), ref, rtol=1e-12, atol=1e-15)
+    # the stored factor is within half a bf16 unit of the exact one
+    Ab = bf16_bits_to_f32(oracle.fold_a(A, 0, n, fold, r)).astype(np.float64)
+    assert np.all(np.abs(Ab - Af) <= 2.0 ** -8 * np.abs(Af) + 2.0 ** -134)
+
+
+def test_draw_fold_is_an_inverse():
+    M, fold = draw_fold(7, 256)
+    assert np.allclose(M @ fold.astype(np.float64), np.eye(256), atol=1e-6)

@@ -8,13 +8,13 @@ the fp64 oracle and the HIP path can take their inputs from it.
 from .configs import CONFIGS, config_by_name, LaneSpec, WorkloadSpec
 from .gen import (
     Workload, Lane, SliceFactors, Adapter,
-    generate, f32_to_bf16_bits, bf16_bits_to_f32,
+    generate, f32_to_bf16_bits, bf16_bits_to_f32, hadamard, draw_fold,
 )
 from .moe import MoeSpec, MoeWorkload, generate_moe, MOE_CONFIGS, moe_config_by_name
 
 __all__ = [
     "CONFIGS", "config_by_name", "LaneSpec", "WorkloadSpec",
     "Workload", "Lane", "SliceFactors", "Adapter",
-    "generate", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "generate", "f32_to_bf16_bits", "bf16_bits_to_f32", "hadamard", "draw_fold",
     "MoeSpec", "MoeWorkload", "generate_moe", "MOE_CONFIGS", "moe_config_by_name",
 ]

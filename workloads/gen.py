@@ -229,3 +229,28 @@ def generate(spec: WorkloadSpec, mode: str = "real", y0: str = "normal",
             y = np.zeros((0, l.h_out_total), np.float32)
         lane_objs[l.name] = Lane(l, x, y)
     return Workload(spec, mode, seq_ids, seq_len, adapters, lane_objs)
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def draw_fold(seed: int, n: int):
+    """An input transform of n features and its inverse, as a projection that
+    reads a rotated, scaled hidden state would see it: M = diag(d) H / sqrt(n)
+    with H the Hadamard matrix and d ~ U[0.5, 2] per feature.
+
+    Returns (M float64 [n, n], fold float32 [n, n]) with fold = M^-1 =
+    H^T diag(1/d) / sqrt(n), rounded to binary32 (the fold a loader is given)."""
+    rng = _stream(seed, 20, n)
+    d = rng.uniform(0.5, 2.0, size=n)
+    h = hadamard(n) / np.sqrt(n)
+    M = d[:, None] * h
+    fold = (h.T / d[None, :]).astype(np.float32)
+    return M, fold
