@@ -6,7 +6,7 @@ from .lora import (
     LoraError, Pool, Routing, make_desc, workspace_for, shrink, expand, delta_apply,
     DEFAULT_PREFILL_MIN_LEN, NO_PREFILL, DEVICE_ROUTING_MAX_TOKENS,
     lora_last_error, lora_version, lora_pool_bytes, lora_pool_create, lora_pool_destroy,
-    lora_pool_load, lora_pool_unload, lora_pool_slot_of, lora_routing_bytes,
+    lora_pool_load, lora_pool_load_folded, lora_pool_unload, lora_pool_slot_of, lora_routing_bytes,
     lora_routing_create, lora_routing_destroy, lora_build_routing, lora_routing_get_info,
     lora_plan_routing,
     lora_routing_token_slots, lora_build_routing_device, lora_build_routing_moe,

@@ -30,6 +30,7 @@ EXPORTS = (
     "lora_pool_unload", "lora_pool_slot_of",
     "lora_routing_bytes", "lora_routing_create", "lora_routing_destroy",
     "lora_build_routing", "lora_routing_get_info", "lora_plan_routing",
+    "lora_pool_load_folded",
     "lora_routing_token_slots", "lora_build_routing_device", "lora_build_routing_moe",
     "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lora_pool_destroy": (I32, [P]),
         "lora_pool_load": (I32, [P, I32, I32, PP, PI64, I64, PP, PI64, PI32,
                                  ctypes.POINTER(ctypes.c_float), I32, P, PI32]),
+        "lora_pool_load_folded": (I32, [P, I32, I32, PP, PI64, I64, PP, PI64, PI32,
+                                        ctypes.POINTER(ctypes.c_float), P, I64, P, PI32]),
         "lora_pool_unload": (I32, [P, I32]),
         "lora_pool_slot_of": (I32, [P, I32, PI32]),
         "lora_routing_bytes": (I32, [I32, PI64]),

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora.so")
 
-SOURCES = ["lora_abi.cpp", "kernels_gemv.hip", "kernels_mfma.hip", "kernels_route.hip"]
+SOURCES = ["lora_abi.cpp", "kernels_gemv.hip", "kernels_mfma.hip", "kernels_route.hip",
+           "kernels_fold.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 ALU instructions are switched off for every device compile.

@@ -606,6 +606,31 @@ int32_t lora_pool_load(lora_pool *p, int32_t adapter_id, int32_t slot, const voi
     return LORA_OK;
 }
 
+int32_t lora_pool_load_folded(lora_pool *p, int32_t adapter_id, int32_t slot,
+                              const void *const *A, const int64_t *lda, int64_t a_col0,
+                              const void *const *B, const int64_t *ldb, const int32_t *rank,
+                              const float *scale, const float *fold, int64_t ld_fold,
+                              void *stream, int32_t *slot_out)
+{
+    if (!p || !A || !lda || !rank) return fail(LORA_ERR_ARG, "null argument");
+    if (!fold) return fail(LORA_ERR_ARG, "fold is null");
+    if (ld_fold < p->desc.h_in)
+        return fail(LORA_ERR_SHAPE, "ld_fold=%lld < h_in=%d", (long long)ld_fold, p->desc.h_in);
+    if (reinterpret_cast<uintptr_t>(fold) % 4) return fail(LORA_ERR_SHAPE, "fold is not 4-byte aligned");
+    int32_t target = 0;
+    if (int32_t rc = lora_pool_load(p, adapter_id, slot, A, lda, a_col0, B, ldb, rank, scale, 1,
+                                    stream, &target))
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int j = 0; j < p->desc.n_slices; ++j) {
+        hipError_t e = launch_fold_a(slot_a(p, target, j), static_cast<const uint16_t *>(A[j]),
+                                     lda[j], a_col0, rank[j], p->desc.h_in, fold, ld_fold, st);
+        if (e != hipSuccess) return hip_fail(e, "folding A");
+    }
+    if (slot_out) *slot_out = target;
+    return LORA_OK;
+}
+
 int32_t lora_pool_unload(lora_pool *p, int32_t adapter_id)
 {
     if (!p) return fail(LORA_ERR_ARG, "pool is null");

@@ -111,6 +111,8 @@ hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDisp
                                const int32_t *rank_tab, int max_slots, int max_dec,
                                int max_gather, int32_t *seg, int32_t *rows, int32_t *tok,
                                int32_t *counts, hipStream_t s);
+hipError_t launch_fold_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
+                         int rank, int h_in, const float *F, int64_t ldf, hipStream_t s);
 hipError_t launch_pack_a(uint16_t *dst, const uint16_t *src, int64_t lda, int64_t a_col0,
                          int rank, int rank_pad, int h_in, hipStream_t s);
 hipError_t launch_pack_bt(uint16_t *dst, const uint16_t *src, int64_t ldb, int rank,

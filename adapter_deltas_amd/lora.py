@@ -110,6 +110,22 @@ def lora_pool_load(pool, adapter_id, slot, A, lda, a_col0, B, ldb, rank, scale,
     return out.value
 
 
+def lora_pool_load_folded(pool, adapter_id, slot, A, lda, a_col0, B, ldb, rank, scale, fold,
+                          ld_fold, stream=None) -> int:
+    """Device A, B and fold (fp32 [h_in][ld_fold]): A is stored as A @ fold."""
+    n = len(A)
+    Ap = (ctypes.c_void_p * n)(*[_ptr(a) for a in A])
+    Bp = (ctypes.c_void_p * n)(*[_ptr(b) for b in B])
+    la = (ctypes.c_int64 * n)(*lda)
+    lb = (ctypes.c_int64 * n)(*ldb)
+    rk = (ctypes.c_int32 * n)(*rank)
+    sc = (ctypes.c_float * n)(*scale)
+    out = ctypes.c_int32(0)
+    _check(_lib().lora_pool_load_folded(pool, adapter_id, slot, Ap, la, a_col0, Bp, lb, rk, sc,
+                                        _ptr(fold), ld_fold, _stream(stream), ctypes.byref(out)))
+    return out.value
+
+
 def lora_pool_unload(pool, adapter_id) -> None:
     _check(_lib().lora_pool_unload(pool, adapter_id))
 
@@ -280,6 +296,18 @@ class Pool:
         ldb = [b.shape[1] for b in B]
         return lora_pool_load(self.handle, adapter_id, slot, A, lda, a_col0, B, ldb,
                               list(ranks), list(scales), on_dev, stream)
+
+    def load_folded(self, adapter_id, A, B, ranks, scales, fold, a_col0=0, slot=-1,
+                    stream=None):
+        """Like load, for a lane whose input arrives as M x: device factors and
+        fold = M^-1 (fp32 cuda tensor [h_in, >= h_in]); A is stored as A @ fold."""
+        A = [a.contiguous() for a in A]
+        B = [b.contiguous() for b in B]
+        if fold.stride(1) != 1:
+            fold = fold.contiguous()
+        return lora_pool_load_folded(self.handle, adapter_id, slot, A, [a.shape[1] for a in A],
+                                     a_col0, B, [b.shape[1] for b in B], list(ranks),
+                                     list(scales), fold, fold.stride(0), stream)
 
     def unload(self, adapter_id):
         lora_pool_unload(self.handle, adapter_id)

@@ -161,6 +161,31 @@ int32_t lora_pool_load(lora_pool *pool, int32_t adapter_id, int32_t slot,
                        const int32_t *rank, const float *scale,
                        int32_t src_on_device, void *stream, int32_t *slot_out);
 
+/*
+ * lora_pool_load for a lane whose input arrives transformed, x' = M x (the
+ * packed shared expert's down projection reads the rotated, scaled fp16
+ * hidden state its expert kernels leave; TensorFold PR #47, first and third
+ * commit messages: the shared expert's A is folded once at load).  Slice j is
+ * stored with A'[k][c] = bf16(sum_i A[j][k][a_col0 + i] * fold[i][c]), an fp32
+ * fma chain over i ascending rounded to nearest even, so that A' x' = A x
+ * up to that rounding when fold = M^-1.  B, ranks and scales as in
+ * lora_pool_load.
+ *
+ *   A, B    device pointers (as lora_pool_load with src_on_device = 1)
+ *   fold    device fp32 [h_in][ld_fold], row-major; fold[i][c] multiplies
+ *           column a_col0 + i of A into column c of A'
+ *   ld_fold >= h_in
+ *
+ * Work is enqueued on `stream`; the source buffers and fold must stay valid
+ * until it has run.  Errors: as lora_pool_load; ARG (null fold), SHAPE
+ * (ld_fold < h_in or fold not 4-byte aligned).
+ */
+int32_t lora_pool_load_folded(lora_pool *pool, int32_t adapter_id, int32_t slot,
+                              const void *const *A, const int64_t *lda, int64_t a_col0,
+                              const void *const *B, const int64_t *ldb, const int32_t *rank,
+                              const float *scale, const float *fold, int64_t ld_fold,
+                              void *stream, int32_t *slot_out);
+
 /* Forgets an adapter id; its slot becomes free and the slot's ranks on the
  * device are zeroed with a blocking copy (so lora_build_routing_device sees it
  * as holding no adapter); work still reading the slot must have finished.

@@ -252,5 +252,5 @@ def draw_fold(seed: int, n: int):
     d = rng.uniform(0.5, 2.0, size=n)
     h = hadamard(n) / np.sqrt(n)
     M = d[:, None] * h
-    fold = (h.T / d[None, :]).astype(np.float32)
+    fold = np.ascontiguousarray((h.T / d[None, :]).astype(np.float32))
     return M, fold
