@@ -75,6 +75,24 @@ def test_validation_errors_without_device(m):
         m.lora_pool_create(m.make_desc(64, [64], 4, 8), 256, 16, stream=0)
     assert e.value.status == "LORA_ERR_CAPACITY"
     assert "needed" in m.lora_last_error()
+    # null handles are refused before any device work
+    for call in (lambda: m.lora_build_routing_device(None, 0, 0, None, stream=0),
+                 lambda: m.lora_build_routing_moe(None, 0, 0, 0, 0, 0, 1, None, stream=0),
+                 lambda: m.lora_routing_device_counts(None),
+                 lambda: m.lora_pool_load_folded(None, 1, -1, [0], [64], 0, [0], [8], [4],
+                                                 [1.0], 0, 64, stream=0)):
+        with pytest.raises(m.LoraError) as e:
+            call()
+        assert e.value.status == "LORA_ERR_ARG"
+
+
+def test_moe_slot_layout(m):
+    """The pair of (adapter slot a, expert e) sits in slot (a - 1) * E + e + 1:
+    an adapter's experts are consecutive slots and the map is one to one."""
+    E, A = 6, 4
+    slots = [m.moe_slot(a, e, E) for a in range(1, A + 1) for e in range(E)]
+    assert slots == list(range(1, A * E + 1))
+    assert m.moe_slot(1, 0, E) == 1 and m.moe_slot(A, E - 1, E) == A * E
 
 
 def test_pool_bytes_layout(m):
