@@ -438,6 +438,82 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     return LORA_OK;
 }
 
+
+// Segments of a batch given one slot per row (0 = skip), on the host: the
+// dispatched rows of a MoE layer, whose (adapter, expert) slots the caller
+// resolved.  A decode row of a slot whose largest slice rank is below
+// kGatherMinRank takes the GEMV path (decode segments of up to
+// kDecodeSegRows rows); a prefill row, or a row of a higher-rank slot, takes
+// the matrix-core path (gather segments of up to kPrefillSegRows rows of one
+// slot).  A row's path so depends only on its own kind and slot.  Rows of a
+// slot are in row order; v holds the GEMV rows, then the gathered rows.
+template <class Ranks>
+void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefill,
+               int32_t max_slots, Ranks ranks, Plan &pl)
+{
+    auto high_rank = [&](int32_t s) {
+        int32_t m = 0;
+        for (int j = 0; j < kMetaStride; ++j) m = std::max(m, ranks(s, j));
+        return m >= kGatherMinRank;
+    };
+    // rows per (slot, path) in first-appearance order of the slots
+    std::vector<std::vector<int32_t>> gemv((size_t)max_slots + 1), gath((size_t)max_slots + 1);
+    std::vector<int32_t> order;
+    std::vector<uint8_t> seen((size_t)max_slots + 1, 0);
+    pl.tok.assign((size_t)n_rows, 0);
+    for (int32_t i = 0; i < n_rows; ++i) {
+        const int32_t s = row_slot[i];
+        if (s == 0) continue;
+        pl.tok[(size_t)i] = s;
+        if (!seen[s]) {
+            seen[s] = 1;
+            order.push_back(s);
+        }
+        const bool prefill = row_prefill && row_prefill[i];
+        (prefill || high_rank(s) ? gath[s] : gemv[s]).push_back(i);
+    }
+    pl.rows.clear();
+    pl.seg.clear();
+    for (int32_t s : order) {
+        const std::vector<int32_t> &rs = gemv[s];
+        const int32_t n_s = (int32_t)rs.size();
+        for (int32_t b = 0; b < n_s; b += kDecodeSegRows) {
+            const int32_t n = std::min(kDecodeSegRows, n_s - b);
+            push_seg(pl.seg, s, (int32_t)pl.rows.size() + b, n, kSegDecode, ranks);
+            for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(rs[(size_t)(b + std::min(c, n - 1))]);
+        }
+        pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
+    }
+    const int32_t n_dec_seg = (int32_t)(pl.seg.size() / kSegWords);
+    for (int32_t s : order) {
+        const std::vector<int32_t> &rs = gath[s];
+        const int32_t n_s = (int32_t)rs.size();
+        for (int32_t b = 0; b < n_s; b += kPrefillSegRows) {
+            const int32_t n = std::min(kPrefillSegRows, n_s - b);
+            push_seg(pl.seg, s, (int32_t)pl.rows.size() + b, n, kSegGather, ranks);
+            for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
+        }
+        pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
+    }
+    const int32_t n_seg = (int32_t)(pl.seg.size() / kSegWords);
+    pl.info = lora_routing_info{};
+    pl.info.n_tokens = n_rows;
+    pl.info.n_active = (int32_t)pl.rows.size();
+    pl.info.n_segments = n_seg;
+    pl.info.n_decode_segments = n_dec_seg;
+    pl.info.n_prefill_segments = 0;
+    pl.info.n_gather_segments = n_seg - n_dec_seg;
+    pl.info.n_distinct = (int32_t)order.size();
+    pl.info.n_seqs = pl.info.n_admitted_seqs = n_rows;
+    pl.adm.clear();
+    pl.distinct_slots = order;
+    pl.slot_ranks.clear();
+    for (int32_t s : order)
+        for (int j = 0; j < kMetaStride; ++j) pl.slot_ranks.push_back(ranks(s, j));
+}
+
+int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -750,7 +826,42 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
     if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
                                   r->max_tokens, p->desc.max_slots, resolve, ranks, pl))
         return rc;
+    if (int32_t rc = upload_plan(p, r, stream)) return rc;
+    if (admitted_out)
+        for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
+    if (n_distinct_out) *n_distinct_out = pl.info.n_distinct;
+    return LORA_OK;
+}
 
+int32_t lora_build_routing_rows(const lora_pool *p, int32_t n_rows, const int32_t *row_slot,
+                                const uint8_t *row_prefill, lora_routing *r, void *stream)
+{
+    if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
+    if (n_rows < 0) return fail(LORA_ERR_SHAPE, "n_rows < 0");
+    if (n_rows > 0 && !row_slot) return fail(LORA_ERR_ARG, "row_slot is null");
+    if (n_rows > r->max_tokens)
+        return fail(LORA_ERR_CAPACITY, "n_rows=%d > max_tokens=%d", n_rows, r->max_tokens);
+    auto ranks = [p](int32_t slot, int j) -> int32_t {
+        return p->h_rank[(size_t)slot * kMetaStride + j];
+    };
+    for (int32_t i = 0; i < n_rows; ++i) {
+        const int32_t s = row_slot[i];
+        if (s != 0 && (s < 1 || s > p->desc.max_slots || p->slot_to_id[s] == 0))
+            return fail(LORA_ERR_SLOT, "row %d names slot %d, which holds no adapter", i, s);
+    }
+    plan_rows(n_rows, row_slot, row_prefill, p->desc.max_slots, ranks, r->plan);
+    return upload_plan(p, r, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Copies r->plan to the routing's device memory (through pinned staging, on
+// `stream`) and makes it the routing's current batch.
+int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
+{
+    const Plan &pl = r->plan;
     const int64_t words = pl.words();
     if (words > r->dev_words)
         return fail(LORA_ERR_CAPACITY, "routing needs %lld words > %lld", (long long)words,
@@ -774,11 +885,12 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
     r->pool_max_slots = p->desc.max_slots;
     r->distinct_slots = pl.distinct_slots;
     r->slot_ranks = pl.slot_ranks;
-    if (admitted_out)
-        for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
-    if (n_distinct_out) *n_distinct_out = pl.info.n_distinct;
     return LORA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
                           int32_t max_loras, int32_t prefill_min_len, int32_t n_resident,

@@ -233,6 +233,18 @@ def lora_build_routing_moe(pool, tok_slot, n_tokens, row_token, row_expert, n_ro
                                          _stream(stream)))
 
 
+def lora_build_routing_rows(pool, row_slot, row_prefill, routing, stream=None) -> None:
+    """Host arrays: int32 slot per row (0 = skip) and optional uint8 prefill flags."""
+    slots = np.ascontiguousarray(row_slot, dtype=np.int32)
+    pre = None if row_prefill is None else np.ascontiguousarray(row_prefill, dtype=np.uint8)
+    if pre is not None and len(pre) != len(slots):
+        raise ValueError("row_slot and row_prefill differ in length")
+    _check(_lib().lora_build_routing_rows(
+        pool, len(slots), slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        None if pre is None else pre.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+        routing, _stream(stream)))
+
+
 def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:
     """Pool slot of (adapter slot, expert) in an expert projection's pool
     (LORA_MOE_SLOT)."""
@@ -354,6 +366,11 @@ class Routing:
         lora_build_routing_moe(pool.handle, tok_slot, int(tok_slot.numel()), row_token,
                                row_expert, int(row_token.numel()), n_experts, self.handle,
                                stream)
+
+    def build_rows(self, pool: Pool, row_slot, row_prefill=None, stream=None):
+        """Routing planned on the host from the slot of every row (0 = skip)
+        and, optionally, which rows belong to prefill tokens."""
+        lora_build_routing_rows(pool.handle, row_slot, row_prefill, self.handle, stream)
 
     def device_counts(self):
         """The int32 [8] device counts of a device-built routing, as a tensor

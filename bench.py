@@ -252,13 +252,16 @@ def main_moe(args, spec):
     import adapter_deltas_amd as m
     from workloads import generate_moe
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import to_device_x, to_device_y
+    from harness import to_device_x, to_device_y, moe_row_slots
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"generating {spec.name}")
     w = generate_moe(spec)
+    # decode batches that fit are routed on the device; prefill chunks are
+    # planned on the host from each row's (adapter, expert) slot
+    on_device = not w.row_prefill.any() and w.n_rows <= m.DEVICE_ROUTING_MAX_TOKENS
     lanes = [l.name for l in spec.lanes]
     E = spec.n_experts
     aslot = {aid: i + 1 for i, aid in enumerate(w.adapter_ids)}
@@ -293,15 +296,23 @@ def main_moe(args, spec):
     R = w.n_rows
     first = lanes[0]
     routing = m.Routing(R, R, device=dev)
-    routing.build_moe(layers[0][first][0], tok_slot, row_token, row_expert, E)
+    row_slot = moe_row_slots(w, [aslot[int(a)] if a else 0 for a in w.tok_adapter])
+    row_prefill = w.row_prefill.astype(np.uint8)
+
+    def route(pool):
+        if on_device:
+            routing.build_moe(pool, tok_slot, row_token, row_expert, E)
+        else:
+            routing.build_rows(pool, row_slot, row_prefill)
+    route(layers[0][first][0])
     ws = {ln: m.workspace_for(layers[0][ln][0], routing, dev) for ln in lanes}
     torch.cuda.synchronize()
-    counts = routing.device_counts().cpu().numpy()
-    act_rows = int(counts[0])
+    act_rows = int(routing.device_counts().cpu().numpy()[0]) if on_device else \
+        routing.info()["n_active"]
 
     def step():
         for per in layers:
-            routing.build_moe(per[first][0], tok_slot, row_token, row_expert, E)
+            route(per[first][0])
             for ln in lanes:
                 pool, x, y = per[ln]
                 m.delta_apply(pool, routing, x, y, ws[ln])
@@ -358,11 +369,12 @@ def main_moe(args, spec):
         return replay_us(body) / (args.layers * len(lanes))
 
     log("graph replay timing")
-    routing.build_moe(layers[0][first][0], tok_slot, row_token, row_expert, E)
+    route(layers[0][first][0])
     apply_us = per_call_us(lambda ln, pool, x, y: m.delta_apply(pool, routing, x, y, ws[ln]))
     shrink_us = per_call_us(lambda ln, pool, x, y: m.shrink(pool, routing, x, vbuf[ln]))
     expand_us = per_call_us(lambda ln, pool, x, y: m.expand(pool, routing, vbuf[ln], y))
-    step_us = replay_us(step)
+    # a host-planned routing is copied from pinned staging: no graph of the step
+    step_us = replay_us(step) if on_device else None
 
     alg = {"shrink": [0, 0], "expand": [0, 0]}
     pairs = 0
@@ -411,11 +423,15 @@ def main_moe(args, spec):
             "tokens": spec.n_tokens, "dispatched_rows": R, "active_rows": act_rows,
             "distinct_adapter_expert_pairs": pairs,
             "layers_per_step": args.layers, "layer_buffer_bytes": layer_bytes,
-            "step": "per layer: MoE routing on the device, then delta_apply on each "
-                    "expert projection",
+            "step": ("per layer: MoE routing on the device" if on_device else
+                     "per layer: MoE routing planned on the host from the rows' "
+                     "(adapter, expert) slots, copied") +
+                    ", then delta_apply on each expert projection",
+            "decode_segments": routing.info()["n_decode_segments"] if not on_device else None,
+            "gather_segments": routing.info()["n_gather_segments"] if not on_device else None,
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
-        "graph_step_ms": round(step_us * 1e-3, 4),
+        "graph_step_ms": round(step_us * 1e-3, 4) if step_us is not None else None,
         "roofline": {
             "kernel": call_kernels(dominant, info),
             "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,

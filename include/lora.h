@@ -363,6 +363,29 @@ int32_t lora_build_routing_moe(const lora_pool *pool, const int32_t *tok_slot,
                                const int32_t *row_expert, int32_t n_rows, int32_t n_experts,
                                lora_routing *routing, void *stream);
 
+/*
+ * Routing of a batch given the pool slot of every row, planned on the host
+ * (like lora_build_routing, copied on `stream`): for MoE batches of any size,
+ * prefill chunks included, whose dispatched rows the caller has resolved to
+ * (adapter, expert) slots with LORA_MOE_SLOT.
+ *
+ *   row_slot     host int32 [n_rows]: slot of each row, 0 = skip the row;
+ *                every other value must be a slot that holds an adapter
+ *   row_prefill  host uint8 [n_rows] or NULL (all rows decode): 1 for a row
+ *                of a prefill token
+ *
+ * A decode row of a slot whose largest slice rank is below
+ * LORA_GATHER_MIN_RANK takes the GEMV path (decode segments); a prefill row,
+ * or a row of a higher-rank slot, takes the matrix-core path in gather
+ * segments of up to LORA_PREFILL_SEG_ROWS rows of one slot (the grouped GEMM
+ * over (adapter, expert) pairs).  A row's bits depend only on its own x row,
+ * its slot's factors and its kind.  Errors: ARG, SHAPE, CAPACITY (n_rows >
+ * max_tokens), SLOT (a row names a slot that holds no adapter), HIP.
+ */
+int32_t lora_build_routing_rows(const lora_pool *pool, int32_t n_rows, const int32_t *row_slot,
+                                const uint8_t *row_prefill, lora_routing *routing,
+                                void *stream);
+
 /* Device pointer to int32 [8] counts of a device-built routing, written by its
  * kernel: [0] active rows, [1] decode segments, [2] prefill segments (0),
  * [3] gather segments, [4] rows whose slot held no adapter (invalid), [5] MoE

@@ -110,3 +110,18 @@ def load_moe_pool(Pool, workload, lane_name, adapter_slot=None, device="cuda"):
     tok_slot = np.array([adapter_slot[int(a)] if a else 0 for a in workload.tok_adapter],
                         dtype=np.int32)
     return pool, tok_slot
+
+
+def moe_row_slots(workload, tok_slot):
+    """Pool slot of every dispatched row of a MoE workload (0 for rows of base
+    tokens and of experts the token's adapter does not edit), for
+    lora_build_routing_rows."""
+    from adapter_deltas_amd import moe_slot
+    E = workload.spec.n_experts
+    ids = workload.tok_adapter[workload.row_token]
+    out = np.zeros(workload.n_rows, dtype=np.int32)
+    for p in range(workload.n_rows):
+        a = int(tok_slot[workload.row_token[p]])
+        if a and (int(ids[p]), int(workload.row_expert[p])) in workload.factors:
+            out[p] = moe_slot(a, int(workload.row_expert[p]), E)
+    return out

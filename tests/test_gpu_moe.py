@@ -7,7 +7,7 @@ import pytest
 import oracle
 from workloads import LaneSpec, MoeSpec, generate_moe, moe_config_by_name
 
-from harness import compare, load_moe_pool, to_device_x, to_device_y
+from harness import compare, load_moe_pool, moe_row_slots, to_device_x, to_device_y
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,109 @@ def test_moe_graph_replays_any_dispatch(lib):
         torch.cuda.synchronize()
         ye, _ = run_moe(lib, w, lane, pool, ts, row_expert=re)
         assert np.array_equal(y.cpu().numpy().view(np.uint32), ye.view(np.uint32)), i
+
+
+
+# ------------------------------------------- host routing from per-row slots
+
+import dataclasses
+
+# The small layer with half of its tokens in prefill chunks.
+SMALL_MOE_MIXED = dataclasses.replace(SMALL_MOE, name="small_moe_mixed", prefill_frac=0.5)
+
+
+def run_rows(m, w, lane, pool, row_slot, row_prefill, path="apply", rows=None):
+    import torch
+    L = w.lanes[lane]
+    sel = np.arange(w.n_rows) if rows is None else rows
+    n = len(sel)
+    r = m.Routing(max(n, 1), max(n, 1))
+    r.build_rows(pool, row_slot[sel], None if row_prefill is None else row_prefill[sel])
+    xd, yd = to_device_x(L.x[sel]), to_device_y(L.y0[sel])
+    if path == "apply":
+        m.delta_apply(pool, r, xd, yd)
+    else:
+        v = torch.zeros(max(n, 1) * pool.v_stride, dtype=torch.float32, device="cuda")
+        m.shrink(pool, r, xd, v)
+        m.expand(pool, r, v, yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy(), r.info()
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["gate_up", "down"])
+@pytest.mark.parametrize("path", ["apply", "split"])
+def test_host_rows_mixed_prefill_parity(lib, lane, mode, path):
+    """Prefill rows grouped per (adapter, expert) on the matrix cores, decode
+    rows on the GEMV path (the rank-130 adapter's on the matrix cores)."""
+    w = generate_moe(SMALL_MOE_MIXED, mode=mode)
+    pool, tok_slot = load_moe_pool(lib.Pool, w, lane)
+    rs = moe_row_slots(w, tok_slot)
+    y, info = run_rows(lib, w, lane, pool, rs, w.row_prefill, path)
+    assert info["n_decode_segments"] > 0 and info["n_gather_segments"] > 0
+    assert info["n_active"] == int((rs != 0).sum())
+    L = w.lanes[lane]
+    d_ref, row_pair = oracle.moe_lane_delta(w, lane)
+    on = np.array([p is not None for p in row_pair])
+    assert np.array_equal(on, rs != 0)
+    assert np.array_equal(y[~on].view(np.uint32), L.y0[~on].view(np.uint32))
+    if mode == "int":
+        assert np.array_equal(y[on].astype(np.float64), L.y0[on].astype(np.float64) + d_ref[on])
+    else:
+        st = compare(y, L.y0, d_ref[on], L.spec.h_out, rows=np.nonzero(on)[0])
+        assert st["ok"], st
+
+
+def test_host_rows_decode_equal_device_routing(lib):
+    """All rows decode: the host plan and the device routing give the same
+    bits; prefill rows keep their bits when dispatched alone."""
+    w = generate_moe(SMALL_MOE_MIXED)
+    lane = "gate_up"
+    pool, tok_slot = load_moe_pool(lib.Pool, w, lane)
+    rs = moe_row_slots(w, tok_slot)
+    yh, _ = run_rows(lib, w, lane, pool, rs, None)
+    yd, _ = run_moe(lib, w, lane, pool, tok_slot)
+    assert np.array_equal(yh.view(np.uint32), yd.view(np.uint32))
+    ym, _ = run_rows(lib, w, lane, pool, rs, w.row_prefill)
+    sub = np.sort(np.random.default_rng(9).permutation(w.n_rows)[: w.n_rows // 3])
+    ys, _ = run_rows(lib, w, lane, pool, rs, w.row_prefill, rows=sub)
+    assert np.array_equal(ys.view(np.uint32), ym[sub].view(np.uint32))
+
+
+def test_host_rows_errors(lib):
+    """A row naming a slot that holds no pair, or a slot out of range, is an
+    error before anything is copied; so is a batch past max_tokens."""
+    w = generate_moe(SMALL_MOE)
+    E = SMALL_MOE.n_experts
+    pool, tok_slot = load_moe_pool(lib.Pool, w, "down")
+    rs = moe_row_slots(w, tok_slot)
+    ids = w.adapter_ids
+    held = {lib.moe_slot(ids.index(aid) + 1, e, E) for (aid, e) in w.factors}
+    empty = next(s for s in range(1, pool.max_slots + 1) if s not in held)
+    r = lib.Routing(w.n_rows, w.n_rows)
+    for s_bad in (empty, pool.max_slots + 1, -2):
+        bad = rs.copy()
+        bad[5] = s_bad
+        with pytest.raises(lib.LoraError) as e:
+            r.build_rows(pool, bad)
+        assert e.value.status == "LORA_ERR_SLOT"
+    with pytest.raises(lib.LoraError) as e:
+        lib.Routing(8, 8).build_rows(pool, rs)
+    assert e.value.status == "LORA_ERR_CAPACITY"
+
+
+def test_moe_prefill_layer_parity(lib):
+    """The Qwen3-30B-A3B-sized layer on a 2048-token prefill chunk (16384
+    dispatched rows), expert down projection."""
+    w = generate_moe(moe_config_by_name("moe_prefill"))
+    lane = "expert_down"
+    pool, tok_slot = load_moe_pool(lib.Pool, w, lane)
+    rs = moe_row_slots(w, tok_slot)
+    y, info = run_rows(lib, w, lane, pool, rs, w.row_prefill)
+    assert info["n_decode_segments"] == 0 and info["n_gather_segments"] > 0
+    L = w.lanes[lane]
+    d_ref, row_pair = oracle.moe_lane_delta(w, lane)
+    on = rs != 0
+    assert np.array_equal(y[~on].view(np.uint32), L.y0[~on].view(np.uint32))
+    st = compare(y, L.y0, d_ref[on], L.spec.h_out, rows=np.nonzero(on)[0])
+    assert st["ok"], st

@@ -39,6 +39,7 @@ class MoeSpec:
     scale_range: tuple = (0.5, 4.0)
     base_prob: float = 0.25
     expert_coverage: float = 1.0
+    prefill_frac: float = 0.0      # fraction of tokens that are prefill tokens
     description: str = ""
 
 
@@ -51,6 +52,7 @@ class MoeWorkload:
     row_expert: np.ndarray     # int32 [R], expert of each dispatched row
     factors: dict              # (registry id, expert) -> {lane name: [SliceFactors]}
     lanes: dict                # lane name -> Lane (x [R, h_in], y0 [R, H_out])
+    tok_prefill: np.ndarray    # bool [T], the token belongs to a prefill chunk
 
     @property
     def adapter_ids(self) -> list:
@@ -59,6 +61,10 @@ class MoeWorkload:
     @property
     def n_rows(self) -> int:
         return len(self.row_token)
+
+    @property
+    def row_prefill(self) -> np.ndarray:
+        return self.tok_prefill[self.row_token]
 
 
 def draw_dispatch(spec: MoeSpec):
@@ -153,7 +159,14 @@ def generate_moe(spec: MoeSpec, mode: str = "real", y0: str = "normal") -> MoeWo
             x = _activations(_stream(spec.seed, 16, li), l, R, mode)
         y = _partial_sums(_stream(spec.seed, 17, li), l, R, mode, y0)
         lanes[l.name] = Lane(l, np.ascontiguousarray(x), y)
-    return MoeWorkload(spec, mode, tok_adapter, row_token, row_expert, factors, lanes)
+    if spec.prefill_frac >= 1.0:
+        tok_prefill = np.ones(spec.n_tokens, dtype=bool)
+    elif spec.prefill_frac <= 0.0:
+        tok_prefill = np.zeros(spec.n_tokens, dtype=bool)
+    else:
+        tok_prefill = _stream(spec.seed, 18).random(spec.n_tokens) < spec.prefill_frac
+    return MoeWorkload(spec, mode, tok_adapter, row_token, row_expert, factors, lanes,
+                       tok_prefill)
 
 
 # Expert projections of a Qwen3-30B-A3B-sized MoE layer (hidden 2048, 128
@@ -169,7 +182,19 @@ MOE_DECODE = MoeSpec(
                 "expert gate_up 2048->768|768 and down 768->2048; 8 adapters r=16 "
                 "alpha=32 on every expert, 25% base")
 
-MOE_CONFIGS = (MOE_DECODE,)
+# The same layer on a 2048-token prefill chunk: 16384 dispatched rows, about
+# 12 per (adapter, expert) pair.
+MOE_PREFILL = MoeSpec(
+    name="moe_prefill", seed=7,
+    lanes=(LaneSpec("expert_gate_up", 2048, (768, 768)),
+           LaneSpec("expert_down", 768, (2048,))),
+    n_experts=128, top_k=8, n_tokens=2048, n_adapters=8, ranks=(16,) * 8, max_rank=16,
+    token_input=("expert_gate_up",), base_prob=0.25, prefill_frac=1.0,
+    description="T=2048 prefill tokens x top-8 of 128 experts = 16384 dispatched rows; "
+                "expert gate_up 2048->768|768 and down 768->2048; 8 adapters r=16 "
+                "alpha=32 on every expert, 25% base")
+
+MOE_CONFIGS = (MOE_DECODE, MOE_PREFILL)
 
 
 def moe_config_by_name(name: str) -> MoeSpec:
