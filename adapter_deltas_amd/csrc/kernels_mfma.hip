@@ -256,9 +256,12 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
 // prefill segments.  The tile's B rows (128 outputs x 32*NK ranks, zero past
 // the slot's rank) are staged in LDS once and kept while the slot stays the
 // same, so a group that covers one prompt reads its B tile from HBM once.
-// Wave w multiplies rows 16w .. 16w + 15 of each segment.
-template <int NK, bool GATHER>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
+// Wave w multiplies rows 16w .. 16w + 15 of each segment; with WAVES = 1 a
+// workgroup is one wave and every segment has at most 16 rows (gather
+// segments cut that small for batches of small (adapter, expert) groups, so
+// no wave of a workgroup idles on an empty row block).
+template <int NK, bool GATHER, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
 void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
                                                       int seg_begin, int seg_end, int group,
                                                       int tiles_per_slice,
@@ -294,7 +297,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     const bool yc_ok = yc < hj;
 
     __shared__ __align__(16) uint16_t bs[COLS][LDB];
-    __shared__ __align__(16) float dt[4][16][LDT];
+    __shared__ __align__(16) float dt[WAVES][16][LDT];
 
     // y of this wave's 16 rows of a segment, two whole 128-column rows per
     // instruction: lane l takes row 2q + l/32, columns 4 * (l % 32) .. + 3.
@@ -348,7 +351,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
         __syncthreads();
         const int rank = sd.rank(j);
         const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j];
-        for (int c = threadIdx.x; c < COLS * CPR; c += 256) {
+        for (int c = threadIdx.x; c < COLS * CPR; c += 64 * WAVES) {
             const int ol = c / CPR, kc = (c - ol * CPR) * 8;
             const int o = o_base + ol;
             // kc < rank <= rank_pad (a multiple of 16): the chunk lies in the
@@ -516,43 +519,50 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
 }
 
 template <int NK>
-static void launch_expand_nk(bool gather, dim3 grid, hipStream_t s, const LaneGeom &g,
-                             const PoolDev &p, const RoutingDev &r, int seg_begin, int seg_end,
-                             int group, int tiles_per_slice, const float *v, float *y, int64_t ldy)
+static void launch_expand_nk(bool gather, bool one_wave, dim3 grid, hipStream_t s,
+                             const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
+                             int seg_begin, int seg_end, int group, int tiles_per_slice,
+                             const float *v, float *y, int64_t ldy)
 {
-    if (gather)
-        hipLaunchKernelGGL((k_expand_mfma<NK, true>), grid, dim3(256), 0, s, g, p, r, seg_begin,
-                           seg_end, group, tiles_per_slice, v, y, ldy);
+    if (gather && one_wave)
+        hipLaunchKernelGGL((k_expand_mfma<NK, true, 1>), grid, dim3(64), 0, s, g, p, r,
+                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+    else if (gather)
+        hipLaunchKernelGGL((k_expand_mfma<NK, true, 4>), grid, dim3(256), 0, s, g, p, r,
+                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
     else
-        hipLaunchKernelGGL((k_expand_mfma<NK, false>), grid, dim3(256), 0, s, g, p, r, seg_begin,
-                           seg_end, group, tiles_per_slice, v, y, ldy);
+        hipLaunchKernelGGL((k_expand_mfma<NK, false, 4>), grid, dim3(256), 0, s, g, p, r,
+                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
 }
 
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int group,
-                              int tiles_per_slice, int max_rank, const float *v, float *y,
-                              int64_t ldy, hipStream_t s)
+                              int tiles_per_slice, int max_rank, int max_seg_rows,
+                              const float *v, float *y, int64_t ldy, hipStream_t s)
 {
     if (n_seg <= 0) return hipSuccess;
     if (group < 1 || max_rank < 1 || max_rank > 256) return hipErrorInvalidValue;
+    if (max_seg_rows < 1 || max_seg_rows > kPrefillSegRows) return hipErrorInvalidValue;
     const int64_t groups = (n_seg + group - 1) / group;
     const int64_t blocks = groups * g.n_slices * tiles_per_slice;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const int seg_end = seg_begin + n_seg;
     const int nk = (max_rank + 31) / 32;
+    // one wave per workgroup when no gather segment has more than 16 rows
+    const bool one_wave = gather && max_seg_rows <= 16;
     if (nk <= 1)
-        launch_expand_nk<1>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
-                            v, y, ldy);
+        launch_expand_nk<1>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
+                            tiles_per_slice, v, y, ldy);
     else if (nk <= 2)
-        launch_expand_nk<2>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
-                            v, y, ldy);
+        launch_expand_nk<2>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
+                            tiles_per_slice, v, y, ldy);
     else if (nk <= 4)
-        launch_expand_nk<4>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
-                            v, y, ldy);
+        launch_expand_nk<4>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
+                            tiles_per_slice, v, y, ldy);
     else
-        launch_expand_nk<8>(gather, grid, s, g, p, r, seg_begin, seg_end, group, tiles_per_slice,
-                            v, y, ldy);
+        launch_expand_nk<8>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
+                            tiles_per_slice, v, y, ldy);
     return hipGetLastError();
 }
 

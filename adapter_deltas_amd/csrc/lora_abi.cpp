@@ -246,14 +246,15 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     if (I.n_prefill_segments > 0) {
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, false, I.n_decode_segments,
                                           I.n_prefill_segments, group_for(I.n_prefill_segments),
-                                          tiles, kmax, v, y, ldy, s);
+                                          tiles, kmax, kPrefillSegRows, v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (prefill) launch");
     }
     if (I.n_gather_segments > 0) {
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, true,
                                           I.n_decode_segments + I.n_prefill_segments,
                                           I.n_gather_segments, group_for(I.n_gather_segments),
-                                          tiles, kmax, v, y, ldy, s);
+                                          tiles, kmax, std::max(1, r->max_gather_rows), v, y,
+                                          ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (gather) launch");
     }
     return LORA_OK;
@@ -409,12 +410,14 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     }
     const int32_t n_pre_seg = (int32_t)(pl.seg.size() / kSegWords) - n_dec_seg;
     // gathered decode rows: chunks of kPrefillSegRows rows of one slot
+    pl.max_gather_rows = 0;
     for (int32_t s : slot_order)
         if (gathered(s))
             for (int32_t b = 0; b < count[s]; b += kPrefillSegRows) {
                 const int32_t n = std::min(kPrefillSegRows, count[s] - b);
                 push_seg(pl.seg, s, start[s] + b, n, kSegGather, ranks);
                 for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
+                pl.max_gather_rows = std::max(pl.max_gather_rows, n);
             }
     const int32_t n_seg = (int32_t)(pl.seg.size() / kSegWords);
     pl.info.n_tokens = (int32_t)T;
@@ -485,13 +488,28 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
         pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
     }
     const int32_t n_dec_seg = (int32_t)(pl.seg.size() / kSegWords);
+    // Groups of a few rows each (the usual MoE case: many (adapter, expert)
+    // pairs) are cut into segments of kSmallGatherRows, so that the expand
+    // runs one wave per segment; larger groups keep kPrefillSegRows rows and
+    // read their factors fewer times.  Gathered rows' bits do not depend on
+    // how they are cut.
+    int64_t g_rows = 0, g_slots = 0;
+    for (int32_t s : order)
+        if (!gath[s].empty()) {
+            g_rows += (int64_t)gath[s].size();
+            ++g_slots;
+        }
+    const int32_t g_size = g_rows <= (int64_t)kSmallGatherRows * g_slots ? kSmallGatherRows
+                                                                         : kPrefillSegRows;
+    pl.max_gather_rows = 0;
     for (int32_t s : order) {
         const std::vector<int32_t> &rs = gath[s];
         const int32_t n_s = (int32_t)rs.size();
-        for (int32_t b = 0; b < n_s; b += kPrefillSegRows) {
-            const int32_t n = std::min(kPrefillSegRows, n_s - b);
+        for (int32_t b = 0; b < n_s; b += g_size) {
+            const int32_t n = std::min(g_size, n_s - b);
             push_seg(pl.seg, s, (int32_t)pl.rows.size() + b, n, kSegGather, ranks);
             for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
+            pl.max_gather_rows = std::max(pl.max_gather_rows, n);
         }
         pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
     }
@@ -789,6 +807,7 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
     r->pool_max_slots = 0;
     r->device_built = false;
     r->off_counts = 0;
+    r->max_gather_rows = 0;
     *routing_out = r;
     return LORA_OK;
 }
@@ -885,6 +904,7 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->pool_max_slots = p->desc.max_slots;
     r->distinct_slots = pl.distinct_slots;
     r->slot_ranks = pl.slot_ranks;
+    r->max_gather_rows = pl.max_gather_rows;
     return LORA_OK;
 }
 
@@ -983,6 +1003,7 @@ int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_
     r->off_tok = (int32_t)off_tok;
     r->off_counts = (int32_t)off_counts;
     r->device_built = true;
+    r->max_gather_rows = kPrefillSegRows;   // segment sizes are known on the device only
     r->pool_max_slots = p->desc.max_slots;
     // Every resident slot may appear in the tables: a pool used with this
     // routing must hold all of them with the same ranks.

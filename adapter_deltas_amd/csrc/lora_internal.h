@@ -14,6 +14,7 @@ namespace lora {
 
 constexpr int kDecodeSegRows = LORA_DECODE_SEG_ROWS;    // rows per decode segment
 constexpr int kPrefillSegRows = LORA_PREFILL_SEG_ROWS;  // rows per prefill segment
+constexpr int kSmallGatherRows = 16;                    // gather segments of small groups
 constexpr int kRankAlign = 16;                          // rank padding of the pool
 constexpr int kKBlock = 8;                              // ranks per decode shrink task
 constexpr int kSubChunk = 512;                          // h_in elements per wave pass
@@ -105,8 +106,8 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               const void *x, int64_t ldx, float *v, hipStream_t s);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int group,
-                              int tiles_per_slice, int max_rank, const float *v, float *y,
-                              int64_t ldy, hipStream_t s);
+                              int tiles_per_slice, int max_rank, int max_seg_rows,
+                              const float *v, float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDispatch *moe,
                                const int32_t *rank_tab, int max_slots, int max_dec,
                                int max_gather, int32_t *seg, int32_t *rows, int32_t *tok,
@@ -149,6 +150,7 @@ struct Plan {
     std::vector<int32_t> slot_ranks;   // per distinct slot: kMetaStride ranks
     std::vector<uint8_t> adm;
     std::vector<int32_t> distinct_slots;
+    int32_t max_gather_rows = 0;        // rows of the largest gather segment
     lora_routing_info info{};
     int64_t off_row() const { return (int64_t)seg.size(); }  // multiple of 4
     int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
@@ -179,6 +181,7 @@ struct lora_routing {
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
     bool device_built;                // counts on the device, info holds bounds
     int32_t off_counts;
+    int32_t max_gather_rows;          // rows of the largest gather segment (bound)
     std::vector<int32_t> distinct_slots;
     std::vector<int32_t> slot_ranks;  // kMetaStride per distinct slot
     lora::Plan plan;                  // host tables, reused between builds
