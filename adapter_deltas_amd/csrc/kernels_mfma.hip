@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
 // segments cut that small for batches of small (adapter, expert) groups, so
 // no wave of a workgroup idles on an empty row block).
 template <int NK, bool GATHER, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 1 ? 2 : NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
 void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
                                                       int seg_begin, int seg_end, int group,
                                                       int tiles_per_slice,
@@ -363,15 +363,54 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
         __syncthreads();
         staged = slot;
     };
+    // The one-wave form with up to 32 ranks also loads the next segment's B
+    // tile into registers while the current segment is worked on (its
+    // segments are mostly of different slots; LDS allows 2 waves per SIMD,
+    // so the registers are there): CHL chunks of 16 bytes per lane.
+    constexpr bool kPrefetchB = WAVES == 1 && NK == 1;
+    constexpr int CHL = kPrefetchB ? COLS * CPR / 64 : 1;
+    auto load_b_regs = [&](Seg sd, uint4 (&bq)[CHL]) {
+        const int rank = sd.rank(j);
+        const uint16_t *Bn =
+            p.Bn + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+#pragma unroll
+        for (int i = 0; i < CHL; ++i) {
+            const int c = lane + 64 * i;
+            const int ol = c / CPR, kc = (c - ol * CPR) * 8;
+            const int o = o_base + ol;
+            bq[i] = (o < hj && kc < rank) ? ld16(Bn + (int64_t)o * g.rank_pad + kc)
+                                          : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_b = [&](Seg sd, const uint4 (&bq)[CHL]) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < CHL; ++i) {
+            const int c = lane + 64 * i;
+            const int ol = c / CPR, kc = (c - ol * CPR) * 8;
+            *reinterpret_cast<uint4 *>(&bs[ol][kc]) = bq[i];
+        }
+        __syncthreads();
+        staged = sd.slot();
+    };
+
+    // One set of B registers suffices: a segment's prefetched tile goes to
+    // LDS at the start of its step, before the next one is loaded.
+    uint4 bq[CHL];
 
     // One segment: multiply with the rows loaded into (yv, vf) while the rows
-    // of the next segment of the group load into (yn, vn).
+    // of the next segment of the group load into (yn, vn) (and, with
+    // kPrefetchB, its B tile into bq when its slot differs).
     auto step = [&](int si, Seg sd, float4 (&yv)[8], float4 (&vr)[2 * NK],
                     float4 (&yn)[8], float4 (&vn)[2 * NK]) {
         const bool act = r0 < sd.n_rows();
         if constexpr (!kPrefetchV)
             if (act) load_v(sd, vr);
-        stage_b(sd);
+        if constexpr (kPrefetchB) {
+            if (sd.slot() != staged) store_b(sd, bq);
+        } else {
+            stage_b(sd);
+        }
         f32x4_t acc[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -402,6 +441,8 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
         if (si + 1 < s_last) {
             const Seg nx = load_seg(r.seg, si + 1);
             if (r0 < nx.n_rows()) load_rows(nx, yn, vn);
+            if constexpr (kPrefetchB)
+                if (nx.slot() != sd.slot()) load_b_regs(nx, bq);
         }
         if (act) {
             // d of (row li, columns 16 s + 4 lg ..) -> LDS -> the y layout.
@@ -444,6 +485,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     {
         const Seg sd = load_seg(r.seg, s_first);
         if (r0 < sd.n_rows()) load_rows(sd, ya, va);
+        if constexpr (kPrefetchB) load_b_regs(sd, bq);
     }
     for (int si = s_first; si < s_last; si += 2) {
         step(si, load_seg(r.seg, si), ya, va, yb, vb);

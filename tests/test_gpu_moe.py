@@ -283,3 +283,32 @@ def test_moe_prefill_layer_parity(lib):
     assert np.array_equal(y[~on].view(np.uint32), L.y0[~on].view(np.uint32))
     st = compare(y, L.y0, d_ref[on], L.spec.h_out, rows=np.nonzero(on)[0])
     assert st["ok"], st
+
+
+# Prefill rows only and ranks up to 32: the one-wave gather expand with its
+# B tiles prefetched across segments of different (adapter, expert) pairs.
+SMALL_MOE_PREFILL = dataclasses.replace(SMALL_MOE, name="small_moe_prefill", ranks=(4, 16, 32),
+                                        max_rank=32, prefill_frac=1.0)
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["gate_up", "down"])
+def test_host_rows_small_groups_parity(lib, lane, mode):
+    w = generate_moe(SMALL_MOE_PREFILL, mode=mode)
+    pool, tok_slot = load_moe_pool(lib.Pool, w, lane)
+    rs = moe_row_slots(w, tok_slot)
+    y, info = run_rows(lib, w, lane, pool, rs, w.row_prefill)
+    assert info["n_decode_segments"] == 0 and info["n_gather_segments"] > 0
+    L = w.lanes[lane]
+    d_ref, row_pair = oracle.moe_lane_delta(w, lane)
+    on = rs != 0
+    assert np.array_equal(y[~on].view(np.uint32), L.y0[~on].view(np.uint32))
+    if mode == "int":
+        assert np.array_equal(y[on].astype(np.float64), L.y0[on].astype(np.float64) + d_ref[on])
+    else:
+        st = compare(y, L.y0, d_ref[on], L.spec.h_out, rows=np.nonzero(on)[0])
+        assert st["ok"], st
+    # every third row alone: other segments, other neighbours, same bits
+    sub = np.arange(0, w.n_rows, 3)
+    ys, _ = run_rows(lib, w, lane, pool, rs, w.row_prefill, rows=sub)
+    assert np.array_equal(ys.view(np.uint32), y[sub].view(np.uint32))
