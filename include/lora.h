@@ -291,8 +291,9 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
                           int64_t words_capacity, int32_t *offsets_out,
                           lora_routing_info *info_out, uint8_t *admitted_out);
 
-/* Device pointer to the routing's per-token slot array (int32 [n_tokens]),
- * valid after the copy enqueued by lora_build_routing has run. */
+/* Device pointer to the routing's per-token slot array (int32 [n_tokens], 0
+ * for rows outside the batch), valid once the work a build call enqueued (the
+ * copy of a host plan, or the routing kernel) has run on its stream. */
 int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **dev_ptr_out);
 
 #define LORA_DEVICE_ROUTING_MAX_TOKENS 4096
