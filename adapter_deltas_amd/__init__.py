@@ -10,7 +10,7 @@ from .lora import (
     lora_routing_create, lora_routing_destroy, lora_build_routing, lora_routing_get_info,
     lora_plan_routing,
     lora_routing_token_slots, lora_build_routing_device, lora_build_routing_moe,
-    lora_build_routing_rows,
+    lora_build_routing_rows, lora_plan_rows,
     lora_routing_device_counts, moe_slot,
     lora_shrink, lora_expand, lora_workspace_bytes,
     lora_delta_apply,

@@ -31,7 +31,7 @@ EXPORTS = (
     "lora_routing_bytes", "lora_routing_create", "lora_routing_destroy",
     "lora_build_routing", "lora_routing_get_info", "lora_plan_routing",
     "lora_pool_load_folded",
-    "lora_build_routing_rows",
+    "lora_build_routing_rows", "lora_plan_rows",
     "lora_routing_token_slots", "lora_build_routing_device", "lora_build_routing_moe",
     "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lora_build_routing_device": (I32, [P, P, I32, P, P]),
         "lora_build_routing_moe": (I32, [P, P, I32, P, P, I32, I32, P, P]),
         "lora_build_routing_rows": (I32, [P, I32, PI32, ctypes.POINTER(ctypes.c_uint8), P, P]),
+        "lora_plan_rows": (I32, [I32, PI32, ctypes.POINTER(ctypes.c_uint8), I32, PI32, PI32, I64,
+                                 PI32, ctypes.POINTER(RoutingInfo)]),
         "lora_routing_device_counts": (I32, [P, PP]),
         "lora_shrink": (I32, [P, P, P, I64, P, P]),
         "lora_expand": (I32, [P, P, P, P, I64, P]),

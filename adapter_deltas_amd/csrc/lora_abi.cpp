@@ -963,6 +963,37 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
     return LORA_OK;
 }
 
+int32_t lora_plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefill,
+                       int32_t max_slots, const int32_t *slot_rank, int32_t *words_out,
+                       int64_t words_capacity, int32_t *offsets_out,
+                       lora_routing_info *info_out)
+{
+    if (max_slots < 1 || max_slots > 65535)
+        return fail(LORA_ERR_SHAPE, "max_slots=%d outside 1..65535", max_slots);
+    if (n_rows < 0) return fail(LORA_ERR_SHAPE, "n_rows < 0");
+    if ((n_rows > 0 && !row_slot) || !slot_rank || !words_out || !offsets_out || !info_out)
+        return fail(LORA_ERR_ARG, "null argument");
+    auto ranks = [slot_rank](int32_t slot, int j) -> int32_t {
+        return slot_rank[(size_t)slot * kMetaStride + j];
+    };
+    for (int32_t i = 0; i < n_rows; ++i) {
+        const int32_t s = row_slot[i];
+        if (s != 0 && (s < 1 || s > max_slots || ranks(s, 0) < 1))
+            return fail(LORA_ERR_SLOT, "row %d names slot %d, which holds no adapter", i, s);
+    }
+    Plan pl;
+    plan_rows(n_rows, row_slot, row_prefill, max_slots, ranks, pl);
+    if (pl.words() > words_capacity)
+        return fail(LORA_ERR_CAPACITY, "plan needs %lld words > %lld", (long long)pl.words(),
+                    (long long)words_capacity);
+    pl.pack(words_out);
+    offsets_out[0] = 0;
+    offsets_out[1] = (int32_t)pl.off_row();
+    offsets_out[2] = (int32_t)pl.off_tok();
+    *info_out = pl.info;
+    return LORA_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -245,6 +245,34 @@ def lora_build_routing_rows(pool, row_slot, row_prefill, routing, stream=None) -
         routing, _stream(stream)))
 
 
+def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
+    """Host-only plan from per-row slots.  slot_rank: int32 [max_slots + 1, 4].
+
+    Returns a dict with info counts and the tables seg (int32 [n_seg, 16]),
+    rows (int32 [n_active]) and tok_slot (int32 [n_rows])."""
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    slots = np.ascontiguousarray(row_slot, dtype=np.int32)
+    pre = None if row_prefill is None else np.ascontiguousarray(row_prefill, dtype=np.uint8)
+    rk = np.ascontiguousarray(slot_rank, dtype=np.int32)
+    if rk.shape != (max_slots + 1, 4):
+        raise ValueError("slot_rank must be [max_slots + 1, 4]")
+    cap = lora_routing_bytes(max_tokens) // 4
+    words = np.zeros(cap, dtype=np.int32)
+    offs = np.zeros(3, dtype=np.int32)
+    info = L.RoutingInfo()
+    _check(_lib().lora_plan_rows(
+        len(slots), slots.ctypes.data_as(i32p),
+        None if pre is None else pre.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+        max_slots, rk.ctypes.data_as(i32p), words.ctypes.data_as(i32p), cap,
+        offs.ctypes.data_as(i32p), ctypes.byref(info)))
+    d = info.as_dict()
+    return dict(
+        info=d,
+        seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
+        rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
+        tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy())
+
+
 def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:
     """Pool slot of (adapter slot, expert) in an expert projection's pool
     (LORA_MOE_SLOT)."""

@@ -387,6 +387,24 @@ int32_t lora_build_routing_rows(const lora_pool *pool, int32_t n_rows, const int
                                 const uint8_t *row_prefill, lora_routing *routing,
                                 void *stream);
 
+/*
+ * The host half of lora_build_routing_rows with no device involved: the same
+ * segments from per-row slots, against an explicit rank table, written to
+ * host memory in lora_plan_routing's packed layout (gather segments of up to
+ * 16 rows when the gathered rows average at most 16 per slot, else up to
+ * LORA_PREFILL_SEG_ROWS).
+ *
+ *   slot_rank  host int32 [max_slots + 1][4]: rank of each slice of each slot;
+ *              a slot holds an adapter iff its slice-0 rank is >= 1
+ *   the rest   as lora_build_routing_rows and lora_plan_routing
+ *
+ * Errors: ARG, SHAPE, SLOT (a row names a slot with no adapter), CAPACITY.
+ */
+int32_t lora_plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefill,
+                       int32_t max_slots, const int32_t *slot_rank, int32_t *words_out,
+                       int64_t words_capacity, int32_t *offsets_out,
+                       lora_routing_info *info_out);
+
 /* Device pointer to int32 [8] counts of a device-built routing, written by its
  * kernel: [0] active rows, [1] decode segments, [2] prefill segments (0),
  * [3] gather segments, [4] rows whose slot held no adapter (invalid), [5] MoE

@@ -209,3 +209,89 @@ def test_plan_errors(m):
     # an unknown id that the cap defers is never looked up
     p = m.lora_plan_routing([5, 6], [1, 1], 1, 64, {5: 1}, 4, 4)
     assert list(p["admitted"]) == [True, False]
+
+
+# ------------------------------------------------ plans from per-row slots
+
+def _check_rows_plan(p, row_slot, row_prefill, slot_rank):
+    """Structure of a plan from per-row slots (MoE dispatched rows)."""
+    info, seg, rows = p["info"], p["seg"], p["rows"]
+    slots = np.asarray(row_slot)
+    pre = np.zeros(len(slots), bool) if row_prefill is None else np.asarray(row_prefill, bool)
+    assert np.array_equal(p["tok_slot"], slots)
+    assert info["n_tokens"] == len(slots) and info["n_prefill_segments"] == 0
+    assert info["n_active"] == int((slots != 0).sum()) == len(rows)
+    assert sorted(rows.tolist()) == np.nonzero(slots)[0].tolist()
+    big = slot_rank.max(axis=1) >= GATHER_MIN_RANK
+    gathered = (slots != 0) & (pre | big[slots])
+    n_dec = info["n_decode_segments"]
+    assert info["n_segments"] == n_dec + info["n_gather_segments"] == len(seg)
+    # gather segments: 16 rows when gathered rows average at most 16 per slot
+    g_slots = set(slots[gathered].tolist())
+    size = 16 if gathered.sum() <= 16 * len(g_slots) else 64
+    covered = 0
+    for k, d in enumerate(seg):
+        s, b, n, kind = d[:4]
+        assert b == covered and n >= 1
+        covered += n
+        r = rows[b:b + n]
+        assert np.all(slots[r] == s) and np.all(np.diff(r) > 0)
+        assert list(d[4:8]) == list(slot_rank[s])
+        if kind == 0:
+            assert k < n_dec and n <= 8 and not np.any(gathered[r])
+            assert list(d[8:8 + n]) == list(r) and np.all(d[8 + n:] == r[-1])
+        else:
+            assert kind == 2 and k >= n_dec and n <= size and np.all(gathered[r])
+            assert np.all(d[8:] == 0)
+    assert covered == len(rows)
+    # a slot's rows of one path sit in consecutive segments, full but the last
+    for part, full in ((seg[:n_dec], 8), (seg[n_dec:], size)):
+        for s in set(part[:, 0].tolist()):
+            ks = np.nonzero(part[:, 0] == s)[0]
+            assert np.all(np.diff(ks) == 1)
+            assert np.all(part[ks][:-1, 2] == full)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_plan_rows_random(m, seed):
+    rng = np.random.default_rng(100 + seed)
+    max_slots = int(rng.integers(1, 40))
+    slot_rank = np.zeros((max_slots + 1, 4), np.int32)
+    held = rng.random(max_slots + 1) < 0.8
+    held[0] = False
+    for s in np.nonzero(held)[0]:
+        slot_rank[s, :int(rng.integers(1, 5))] = rng.choice([1, 4, 16, 64, 128, 130])
+    live = np.nonzero(held)[0]
+    n = int(rng.integers(0, 3000)) if seed else 0
+    row_slot = np.where(rng.random(n) < 0.2, 0, rng.choice(live, n) if len(live) else 0)
+    row_slot = row_slot.astype(np.int32)
+    row_prefill = (rng.random(n) < [0.0, 0.5, 1.0][seed % 3]) if seed % 4 else None
+    p = m.lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max(n, 1))
+    _check_rows_plan(p, row_slot, row_prefill, slot_rank)
+
+
+def test_plan_rows_cuts_small_groups_at_16(m):
+    """Many small groups: 16-row gather segments; one big group: 64."""
+    slot_rank = np.zeros((9, 4), np.int32)
+    slot_rank[1:, 0] = 16
+    small = np.repeat(np.arange(1, 9), 12).astype(np.int32)          # 12 rows per slot
+    p = m.lora_plan_rows(small, np.ones(len(small), np.uint8), 8, slot_rank, len(small))
+    assert p["info"]["n_gather_segments"] == 8 and p["seg"][:, 2].max() == 12
+    big = np.full(100, 3, np.int32)
+    p = m.lora_plan_rows(big, np.ones(100, np.uint8), 8, slot_rank, 100)
+    assert list(p["seg"][:, 2]) == [64, 36]
+    mixed = np.concatenate([np.full(40, 2), np.full(8, 5)]).astype(np.int32)   # 24 per slot
+    p = m.lora_plan_rows(mixed, np.ones(len(mixed), np.uint8), 8, slot_rank, len(mixed))
+    assert list(p["seg"][:, 2]) == [40, 8]
+
+
+def test_plan_rows_errors(m):
+    slot_rank = np.zeros((5, 4), np.int32)
+    slot_rank[1:3, 0] = 8
+    for bad in (3, 5, -1):                       # empty, out of range, negative
+        with pytest.raises(m.LoraError) as e:
+            m.lora_plan_rows(np.array([1, bad], np.int32), None, 4, slot_rank, 4)
+        assert e.value.status == "LORA_ERR_SLOT"
+    with pytest.raises(m.LoraError) as e:
+        m.lora_plan_rows(np.array([1, 2], np.int32), None, 0, np.zeros((1, 4), np.int32), 4)
+    assert e.value.status == "LORA_ERR_SHAPE"
