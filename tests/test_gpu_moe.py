@@ -312,3 +312,15 @@ def test_host_rows_small_groups_parity(lib, lane, mode):
     sub = np.arange(0, w.n_rows, 3)
     ys, _ = run_rows(lib, w, lane, pool, rs, w.row_prefill, rows=sub)
     assert np.array_equal(ys.view(np.uint32), y[sub].view(np.uint32))
+
+
+def test_moe_device_routing_at_the_row_limit(lib):
+    """512 tokens x top 8 = 4096 dispatched rows, the most the device routing
+    takes (its 1024-thread form), against the oracle."""
+    spec = dataclasses.replace(SMALL_MOE, name="moe_4096", n_tokens=512, top_k=8,
+                               lanes=(LaneSpec("down", 136, (264,)),), token_input=())
+    w = generate_moe(spec)
+    assert w.n_rows == lib.DEVICE_ROUTING_MAX_TOKENS
+    pool, tok_slot = load_moe_pool(lib.Pool, w, "down")
+    y, c = run_moe(lib, w, "down", pool, tok_slot)
+    check_moe(w, "down", y, c)
