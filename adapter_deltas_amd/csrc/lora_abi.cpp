@@ -459,60 +459,65 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
         for (int j = 0; j < kMetaStride; ++j) m = std::max(m, ranks(s, j));
         return m >= kGatherMinRank;
     };
-    // rows per (slot, path) in first-appearance order of the slots
-    std::vector<std::vector<int32_t>> gemv((size_t)max_slots + 1), gath((size_t)max_slots + 1);
+    // rows per (slot, path), counted, then placed in row order: GEMV rows
+    // of the slots in first-appearance order, then gathered rows likewise
+    std::vector<int32_t> n_gemv((size_t)max_slots + 1, 0), n_gath((size_t)max_slots + 1, 0);
+    std::vector<uint8_t> is_gath((size_t)n_rows, 0);
     std::vector<int32_t> order;
-    std::vector<uint8_t> seen((size_t)max_slots + 1, 0);
     pl.tok.assign((size_t)n_rows, 0);
     for (int32_t i = 0; i < n_rows; ++i) {
         const int32_t s = row_slot[i];
         if (s == 0) continue;
         pl.tok[(size_t)i] = s;
-        if (!seen[s]) {
-            seen[s] = 1;
-            order.push_back(s);
-        }
-        const bool prefill = row_prefill && row_prefill[i];
-        (prefill || high_rank(s) ? gath[s] : gemv[s]).push_back(i);
+        if (n_gemv[s] == 0 && n_gath[s] == 0) order.push_back(s);
+        const bool g = (row_prefill && row_prefill[i]) || high_rank(s);
+        is_gath[(size_t)i] = g;
+        ++(g ? n_gath : n_gemv)[s];
     }
-    pl.rows.clear();
-    pl.seg.clear();
+    std::vector<int32_t> at_gemv((size_t)max_slots + 1, 0), at_gath((size_t)max_slots + 1, 0);
+    int64_t n_gemv_rows = 0, g_rows = 0, g_slots = 0;
     for (int32_t s : order) {
-        const std::vector<int32_t> &rs = gemv[s];
-        const int32_t n_s = (int32_t)rs.size();
-        for (int32_t b = 0; b < n_s; b += kDecodeSegRows) {
-            const int32_t n = std::min(kDecodeSegRows, n_s - b);
-            push_seg(pl.seg, s, (int32_t)pl.rows.size() + b, n, kSegDecode, ranks);
-            for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(rs[(size_t)(b + std::min(c, n - 1))]);
-        }
-        pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
+        at_gemv[s] = (int32_t)n_gemv_rows;
+        n_gemv_rows += n_gemv[s];
     }
+    for (int32_t s : order) {
+        at_gath[s] = (int32_t)(n_gemv_rows + g_rows);
+        g_rows += n_gath[s];
+        g_slots += n_gath[s] > 0;
+    }
+    pl.rows.assign((size_t)(n_gemv_rows + g_rows), 0);
+    {
+        std::vector<int32_t> fg = at_gemv, fa = at_gath;
+        for (int32_t i = 0; i < n_rows; ++i) {
+            const int32_t s = row_slot[i];
+            if (s == 0) continue;
+            pl.rows[(size_t)(is_gath[(size_t)i] ? fa[s]++ : fg[s]++)] = i;
+        }
+    }
+    pl.seg.clear();
+    for (int32_t s : order)
+        for (int32_t b = 0; b < n_gemv[s]; b += kDecodeSegRows) {
+            const int32_t n = std::min(kDecodeSegRows, n_gemv[s] - b);
+            push_seg(pl.seg, s, at_gemv[s] + b, n, kSegDecode, ranks);
+            for (int32_t c = 0; c < kDecodeSegRows; ++c)
+                pl.seg.push_back(pl.rows[(size_t)(at_gemv[s] + b + std::min(c, n - 1))]);
+        }
     const int32_t n_dec_seg = (int32_t)(pl.seg.size() / kSegWords);
     // Groups of a few rows each (the usual MoE case: many (adapter, expert)
     // pairs) are cut into segments of kSmallGatherRows, so that the expand
     // runs one wave per segment; larger groups keep kPrefillSegRows rows and
     // read their factors fewer times.  Gathered rows' bits do not depend on
     // how they are cut.
-    int64_t g_rows = 0, g_slots = 0;
-    for (int32_t s : order)
-        if (!gath[s].empty()) {
-            g_rows += (int64_t)gath[s].size();
-            ++g_slots;
-        }
     const int32_t g_size = g_rows <= (int64_t)kSmallGatherRows * g_slots ? kSmallGatherRows
                                                                          : kPrefillSegRows;
     pl.max_gather_rows = 0;
-    for (int32_t s : order) {
-        const std::vector<int32_t> &rs = gath[s];
-        const int32_t n_s = (int32_t)rs.size();
-        for (int32_t b = 0; b < n_s; b += g_size) {
-            const int32_t n = std::min(g_size, n_s - b);
-            push_seg(pl.seg, s, (int32_t)pl.rows.size() + b, n, kSegGather, ranks);
+    for (int32_t s : order)
+        for (int32_t b = 0; b < n_gath[s]; b += g_size) {
+            const int32_t n = std::min(g_size, n_gath[s] - b);
+            push_seg(pl.seg, s, at_gath[s] + b, n, kSegGather, ranks);
             for (int32_t c = 0; c < kDecodeSegRows; ++c) pl.seg.push_back(0);
             pl.max_gather_rows = std::max(pl.max_gather_rows, n);
         }
-        pl.rows.insert(pl.rows.end(), rs.begin(), rs.end());
-    }
     const int32_t n_seg = (int32_t)(pl.seg.size() / kSegWords);
     pl.info = lora_routing_info{};
     pl.info.n_tokens = n_rows;
