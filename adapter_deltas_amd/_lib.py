@@ -20,7 +20,7 @@ MAX_RANK = 256
 DECODE_SEG_ROWS = 8
 SEG_WORDS = 16
 GATHER_MIN_RANK = 128         # LORA_GATHER_MIN_RANK
-DEVICE_ROUTING_MAX_TOKENS = 4096   # LORA_DEVICE_ROUTING_MAX_TOKENS
+DEVICE_ROUTING_MAX_TOKENS = 8192   # LORA_DEVICE_ROUTING_MAX_TOKENS
 PREFILL_SEG_ROWS = 64
 
 # every symbol include/lora.h declares

@@ -13,15 +13,17 @@
 //
 // The segment table has room for max_dec decode segments, then max_gather
 // gather segments; the exact counts go to `counts` for the kernels to read.
+#include <utility>
+
 #include "kernels_common.h"
 
 namespace lora {
 namespace {
 
 constexpr uint32_t kNoKey = 0xffffffffu;
-constexpr int kRowBits = 12;                 // row index bits of a sort key
+constexpr int kRowBits = 13;                 // row index bits of a sort key
 constexpr int kSlotBits = 16;                // slot bits above them, then the path bit
-constexpr int kRouteRowsPerThread = 4;
+constexpr int kRouteRowsPerThread = 4;       // sort keys per thread (8 in the largest form)
 static_assert(LORA_DEVICE_ROUTING_MAX_TOKENS <= (1 << kRowBits), "rows fit the key");
 static_assert((kDecodeSegRows & (kDecodeSegRows - 1)) == 0 &&
                   (kPrefillSegRows & (kPrefillSegRows - 1)) == 0,
@@ -139,69 +141,79 @@ __device__ inline void order2(uint32_t &a, uint32_t &b, bool up)
 }
 
 // One compare-exchange stage of a bitonic merge of SIZE positions, then the
-// smaller strides of the same merge.  Thread t holds positions 4t .. 4t + 3;
-// strides below 4 stay in the thread, below 256 in the wave, larger ones go
-// through LDS (`key`, 4 entries per thread).
-template <int SIZE, int STRIDE>
-__device__ __forceinline__ void bitonic_stage(uint32_t (&k)[4], int tid, int lane, uint32_t *key)
+// smaller strides of the same merge.  Thread t holds positions E t .. E t +
+// E - 1; strides below E stay in the thread, below 64 E in the wave, larger
+// ones go through LDS (`key`, E entries per thread).
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(uint32_t (&k)[E], int tid, int lane, uint32_t *key)
 {
-    const int p0 = tid * 4;
-    const bool up = (p0 & SIZE) == 0;       // this thread's direction (SIZE >= 4)
-    if constexpr (STRIDE >= 256) {
+    static_assert(E == 4 || E == 8, "four or eight keys per thread");
+    const int p0 = tid * E;
+    if constexpr (STRIDE >= 64 * E) {
+        const bool up = (p0 & SIZE) == 0;
         __syncthreads();
-        *reinterpret_cast<uint4 *>(&key[p0]) = make_uint4(k[0], k[1], k[2], k[3]);
-        __syncthreads();
-        const uint4 o = *reinterpret_cast<const uint4 *>(&key[p0 ^ STRIDE]);
-        const bool keep_min = ((p0 & STRIDE) == 0) == up;
-        k[0] = keep_min ? min(k[0], o.x) : max(k[0], o.x);
-        k[1] = keep_min ? min(k[1], o.y) : max(k[1], o.y);
-        k[2] = keep_min ? min(k[2], o.z) : max(k[2], o.z);
-        k[3] = keep_min ? min(k[3], o.w) : max(k[3], o.w);
-    } else if constexpr (STRIDE >= 4) {
-        const bool keep_min = ((tid & (STRIDE / 4)) == 0) == up;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t o = lane_xor<STRIDE / 4>(k[e], lane);
+        for (int e = 0; e < E; e += 4)
+            *reinterpret_cast<uint4 *>(&key[p0 + e]) = make_uint4(k[e], k[e + 1], k[e + 2], k[e + 3]);
+        __syncthreads();
+        const bool keep_min = ((p0 & STRIDE) == 0) == up;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            const uint4 o = *reinterpret_cast<const uint4 *>(&key[(p0 ^ STRIDE) + e]);
+            k[e] = keep_min ? min(k[e], o.x) : max(k[e], o.x);
+            k[e + 1] = keep_min ? min(k[e + 1], o.y) : max(k[e + 1], o.y);
+            k[e + 2] = keep_min ? min(k[e + 2], o.z) : max(k[e + 2], o.z);
+            k[e + 3] = keep_min ? min(k[e + 3], o.w) : max(k[e + 3], o.w);
+        }
+    } else if constexpr (STRIDE >= E) {
+        const bool up = (p0 & SIZE) == 0;
+        const bool keep_min = ((tid & (STRIDE / E)) == 0) == up;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t o = lane_xor<STRIDE / E>(k[e], lane);
             k[e] = keep_min ? min(k[e], o) : max(k[e], o);
         }
-    } else if constexpr (STRIDE == 2) {
-        order2(k[0], k[2], up);
-        order2(k[1], k[3], up);
-    } else if constexpr (SIZE == 2) {
-        order2(k[0], k[1], true);
-        order2(k[2], k[3], false);
     } else {
-        order2(k[0], k[1], up);
-        order2(k[2], k[3], up);
+        // partners inside the thread: e and e + STRIDE; the direction of a
+        // pair comes from its position's SIZE bit
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if ((e & STRIDE) == 0) order2(k[e], k[e + STRIDE], ((p0 + e) & SIZE) == 0);
     }
-    if constexpr (STRIDE > 1) bitonic_stage<SIZE, STRIDE / 2>(k, tid, lane, key);
+    if constexpr (STRIDE > 1) bitonic_stage<E, SIZE, STRIDE / 2>(k, tid, lane, key);
 }
 
 // Bitonic sort, ascending, of the first n_sort positions (a power of two,
 // uniform): merges of 2, 4, ... n_sort positions.  Positions past n_sort are
 // sorted among themselves only.
-template <int ROWS, int SIZE = 2>
-__device__ __forceinline__ void bitonic_sort(uint32_t (&k)[4], int n_sort, int tid, int lane,
+template <int E, int ROWS, int SIZE = 2>
+__device__ __forceinline__ void bitonic_sort(uint32_t (&k)[E], int n_sort, int tid, int lane,
                                              uint32_t *key)
 {
     if (SIZE > n_sort) return;
-    bitonic_stage<SIZE, SIZE / 2>(k, tid, lane, key);
-    if constexpr (SIZE < ROWS) bitonic_sort<ROWS, SIZE * 2>(k, n_sort, tid, lane, key);
+    bitonic_stage<E, SIZE, SIZE / 2>(k, tid, lane, key);
+    if constexpr (SIZE < ROWS) bitonic_sort<E, ROWS, SIZE * 2>(k, n_sort, tid, lane, key);
 }
 
-// THREADS threads route up to 4 * THREADS rows.  Thread t holds the keys of
-// sorted positions 4t .. 4t + 3 in registers.  With MOE the rows are the
+// f(integral_constant<int, e>) for e = 0 .. E - 1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void for_each_key(F f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// THREADS threads route up to E * THREADS rows.  Thread t holds the keys of
+// sorted positions E t .. E t + E - 1 in registers.  With MOE the rows are the
 // dispatched (token, expert) rows of an expert projection and `tok_slot`
 // holds each token's adapter slot; a row's slot is its (adapter, expert)
 // pool slot.
-template <int THREADS, bool MOE>
+template <int THREADS, int E, bool MOE>
 __global__ __launch_bounds__(THREADS) void k_route_decode(
     const int32_t *__restrict__ tok_slot, int n_tok, MoeDispatch moe,
     const int4 *__restrict__ rank_rows, int max_slots, int max_dec, int max_gather,
     int32_t *__restrict__ seg, int32_t *__restrict__ rows, int32_t *__restrict__ tok,
     int32_t *__restrict__ counts)
 {
-    constexpr int E = kRouteRowsPerThread;
     constexpr int ROWS = THREADS * E;
     constexpr int NW = THREADS / 64;
     constexpr uint32_t kRowMask = (1u << kRowBits) - 1;
@@ -273,9 +285,11 @@ __global__ __launch_bounds__(THREADS) void k_route_decode(
     const int n_invalid = cnt.y & 0xffff;
     const int n_unedited_rows = cnt.y >> 16;
 
-    bitonic_sort<ROWS>(k, n_sort, tid, lane, key);
+    bitonic_sort<E, ROWS>(k, n_sort, tid, lane, key);
     __syncthreads();
-    *reinterpret_cast<uint4 *>(&key[p0]) = make_uint4(k[0], k[1], k[2], k[3]);
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<uint4 *>(&key[p0 + e]) = make_uint4(k[e], k[e + 1], k[e + 2], k[e + 3]);
     __syncthreads();
     // the ranks of each sorted row's slot, needed by the descriptors at the
     // end (loaded after the barrier, which would wait for them)
@@ -364,11 +378,14 @@ __global__ __launch_bounds__(THREADS) void k_route_decode(
         d[2] = make_int4(r[0], r[1], r[2], r[3]);
         d[3] = make_int4(r[4], r[5], r[6], r[7]);
     };
-    static_assert(E == 4, "four positions per thread");
-    emit(p0, k[0], flag[0], srk[0], ord);
-    emit(p0 + 1, k[1], flag[1], srk[1], ord + flag[0]);
-    emit(p0 + 2, k[2], flag[2], srk[2], ord + flag[0] + flag[1]);
-    emit(p0 + 3, k[3], flag[3], srk[3], ord + flag[0] + flag[1] + flag[2]);
+    int ordv[E];                            // segments before position p0 + e
+    ordv[0] = ord;
+#pragma unroll
+    for (int e = 1; e < E; ++e) ordv[e] = ordv[e - 1] + flag[e - 1];
+    for_each_key([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        emit(p0 + e, k[e], flag[e], srk[e], ordv[e]);
+    }, std::make_integer_sequence<int, E>{});
     if (tid == 0) {
         counts[kCntActive] = na;
         counts[kCntDecode] = n_dec;
@@ -397,12 +414,18 @@ hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDisp
         hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), 0, s, tok_slot, n_tok, d, rr,
                            max_slots, max_dec, max_gather, seg, rows, tok, counts);
     };
-    if (n_tok <= 64 * kRouteRowsPerThread)
-        moe ? launch(k_route_decode<64, true>, 64) : launch(k_route_decode<64, false>, 64);
-    else if (n_tok <= 256 * kRouteRowsPerThread)
-        moe ? launch(k_route_decode<256, true>, 256) : launch(k_route_decode<256, false>, 256);
+    constexpr int E = kRouteRowsPerThread;
+    if (n_tok <= 64 * E)
+        moe ? launch(k_route_decode<64, E, true>, 64) : launch(k_route_decode<64, E, false>, 64);
+    else if (n_tok <= 256 * E)
+        moe ? launch(k_route_decode<256, E, true>, 256)
+            : launch(k_route_decode<256, E, false>, 256);
+    else if (n_tok <= 1024 * E)
+        moe ? launch(k_route_decode<1024, E, true>, 1024)
+            : launch(k_route_decode<1024, E, false>, 1024);
     else
-        moe ? launch(k_route_decode<1024, true>, 1024) : launch(k_route_decode<1024, false>, 1024);
+        moe ? launch(k_route_decode<1024, 2 * E, true>, 1024)
+            : launch(k_route_decode<1024, 2 * E, false>, 1024);
     return hipGetLastError();
 }
 

@@ -296,7 +296,7 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
  * copy of a host plan, or the routing kernel) has run on its stream. */
 int32_t lora_routing_token_slots(const lora_routing *routing, const int32_t **dev_ptr_out);
 
-#define LORA_DEVICE_ROUTING_MAX_TOKENS 4096
+#define LORA_DEVICE_ROUTING_MAX_TOKENS 8192
 
 /*
  * Routing of a decode batch built on the device, with no host planning and

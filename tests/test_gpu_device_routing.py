@@ -96,11 +96,11 @@ def test_device_routing_matches_host(lib, cfg, lane, path):
     assert np.array_equal(rd.token_slots().cpu().numpy(), slots_of(pool, ids))
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 64, 65, 256, 257, 1000, 1024, 1025, 4096])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 64, 65, 256, 257, 1000, 1024, 1025, 4096, 4097, 8192])
 def test_device_routing_sizes(lib, n):
     """Empty, single-row, segment-edge and maximum batch sizes, and the edges
-    of the routing kernel's 64-, 256- and 1024-thread forms; adapters of both
-    paths plus base rows."""
+    of the routing kernel's forms (64, 256 and 1024 threads with 4 keys each,
+    1024 threads with 8); adapters of both paths plus base rows."""
     w = generate(DEVICE_MIX)
     pool, x, y0 = lane_setup(lib, w, "qkv_like")
     T = x.shape[0]

@@ -315,9 +315,9 @@ def test_host_rows_small_groups_parity(lib, lane, mode):
 
 
 def test_moe_device_routing_at_the_row_limit(lib):
-    """512 tokens x top 8 = 4096 dispatched rows, the most the device routing
-    takes (its 1024-thread form), against the oracle."""
-    spec = dataclasses.replace(SMALL_MOE, name="moe_4096", n_tokens=512, top_k=8,
+    """1024 tokens x top 8 = 8192 dispatched rows, the most the device
+    routing takes (its 1024-thread, 8-key form), against the oracle."""
+    spec = dataclasses.replace(SMALL_MOE, name="moe_8192", n_tokens=1024, top_k=8,
                                lanes=(LaneSpec("down", 136, (264,)),), token_input=())
     w = generate_moe(spec)
     assert w.n_rows == lib.DEVICE_ROUTING_MAX_TOKENS
