@@ -39,12 +39,15 @@ struct Seg {
 // Descriptors are read-only while kernels run, so they are read through the
 // constant address space: a uniform index then gives scalar loads, which
 // neither take vector registers nor wait behind the vector loads in flight.
+// The 64-byte descriptor is read as one 16-word load, so that no part of it
+// is fetched later than another.
 __device__ __forceinline__ Seg load_seg(const int32_t *seg, int si)
 {
-    typedef const __attribute__((address_space(4))) int32_t cint;
-    cint *p = (cint *)(seg + (int64_t)si * kSegWords);
-    return Seg{make_int4(p[0], p[1], p[2], p[3]), make_int4(p[4], p[5], p[6], p[7]),
-               make_int4(p[8], p[9], p[10], p[11]), make_int4(p[12], p[13], p[14], p[15])};
+    typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+    typedef const __attribute__((address_space(4))) i32x16 cvec;
+    const i32x16 d = *(cvec *)(seg + (int64_t)si * kSegWords);
+    return Seg{make_int4(d[0], d[1], d[2], d[3]), make_int4(d[4], d[5], d[6], d[7]),
+               make_int4(d[8], d[9], d[10], d[11]), make_int4(d[12], d[13], d[14], d[15])};
 }
 
 // Workgroups are handed to the 8 XCDs round-robin by block id, and each XCD
@@ -55,9 +58,39 @@ __device__ __forceinline__ Seg load_seg(const int32_t *seg, int si)
 constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_task(int b, int n)
 {
+    // XCD x < n % 8 has q + 1 tasks, the others q (written without a branch,
+    // so that loads after it are not held behind one)
     const int q = n / kXcds, rem = n % kXcds;
     const int xcd = b % kXcds, local = b / kXcds;
-    return xcd < rem ? xcd * (q + 1) + local : rem * (q + 1) + (xcd - rem) * q + local;
+    return xcd * q + min(xcd, rem) + local;
+}
+
+// Entry j (0..3) of a 4-entry array held in the kernel arguments, taken by
+// selects: indexing the argument segment with a runtime value would make the
+// load of the entry wait for that value, one more dependent scalar load
+// before the kernel's first data load.
+template <class T>
+__device__ __forceinline__ T pick4(const T (&a)[4], int j)
+{
+    const T a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+    return j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
+}
+
+// Descriptor of decode segment si into sd, and whether si is one of the
+// batch's decode segments: with device-built routing the grid covers the
+// bound on the count and the tasks past the count end here.  The count and
+// the descriptor (inside the table for any si of the grid) are both loaded
+// before either is waited for, and the result depends on both, so neither
+// load is moved behind the other's branch.  With host-built routing there is
+// no count and an arbitrary readable word stands in for it.
+__device__ __forceinline__ bool decode_seg(const RoutingDev &r, int si, Seg &sd)
+{
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    const int32_t *cp = r.counts ? r.counts + kCntDecode : r.seg;
+    const int raw = *(cint *)cp;
+    sd = load_seg(r.seg, si);
+    const int n_dec = r.counts ? raw : INT32_MAX;
+    return si < n_dec && sd.n_rows() > 0;
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p)

@@ -14,20 +14,27 @@ namespace {
 
 // W waves per task (1, 2, 4 or 8): wave w sums parts w, w + W, ... of the 8,
 // each reduced on its own, so the bits do not depend on W.
+//
+// The prologue has no branch before the descriptor and count loads are
+// issued, and the scale load follows them, so the first data loads wait for
+// about two scalar round trips rather than a chain of them.
 template <bool FP16X, int W>
 __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                         int kb_per_slice,
+                                                         int n_tasks, int kb_per_slice,
                                                          const uint16_t *__restrict__ x,
                                                          int64_t ldx, float *__restrict__ v)
 {
     const int per_seg = g.n_slices * kb_per_slice;
-    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / kb_per_slice;
     const int kb = rem - j * kb_per_slice;
-    if (r.counts && si >= r.counts[kCntDecode]) return;    // device-built routing
-    const Seg sd = load_seg(r.seg, si);
+    Seg sd;
+    if (!decode_seg(r, si, sd)) return;
+    // past the count a device-built descriptor is stale: its slot is read
+    // only after the check
+    const float scale = p.scale[sd.slot() * kMetaStride + j];
     const int rank = sd.rank(j);
     const int k0 = kb * kKBlock;
     if (k0 >= rank) return;
@@ -51,7 +58,6 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
         const int c = lane / kKBlock;
         const int k = lane % kKBlock;
         if (c < sd.n_rows() && k < kn) {
-            const float scale = p.scale[sd.slot() * kMetaStride + j];
             v[(int64_t)(sd.v_row() + c) * g.v_stride + j * g.rank_pad + k0 + k] = scale * (q0 + q1);
         }
     }
@@ -59,8 +65,10 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
 
 constexpr int kExpandWaves = kDecodeSegRows / kExpandRows;   // waves per expand task
 
+// Prologue as in k_shrink_gemv; the slice's widths and offsets are taken from
+// the arguments by selects.
 __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, PoolDev p,
-                                                                   RoutingDev r,
+                                                                   RoutingDev r, int n_tasks,
                                                                    int tiles_per_slice,
                                                                    const float *__restrict__ v,
                                                                    float *__restrict__ y,
@@ -68,15 +76,17 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
 {
     constexpr int C = kExpandRows;
     const int per_seg = g.n_slices * tiles_per_slice;
-    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / tiles_per_slice;
     const int tile = rem - j * tiles_per_slice;
-    const int hj = g.h_out[j];
-    if (tile * kExpandTile >= hj) return;
-    if (r.counts && si >= r.counts[kCntDecode]) return;    // device-built routing
-    const Seg sd = load_seg(r.seg, si);
+    const int hj = pick4(g.h_out, j);
+    const int col_off = pick4(g.col_off, j);
+    const int64_t bt_off = pick4(g.bt_slice_off, j);
+    Seg sd;
+    const bool live = decode_seg(r, si, sd);
+    if (!live || tile * kExpandTile >= hj) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c0 = wave * C;                    // first segment row of this wave
@@ -96,10 +106,9 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
 #pragma unroll
         for (int w = 1; w < kExpandWaves; ++w)
             if (wave == w) t = all[w * C + c];
-        yp[c] = y + (int64_t)t * ldy + g.col_off[j] + oc;
+        yp[c] = y + (int64_t)t * ldy + col_off + oc;
     }
-    const uint16_t *bt =
-        p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j] + oc;
+    const uint16_t *bt = p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + bt_off + oc;
     // v is read-only here and the same for every lane: constant-space reads
     // become scalar loads.
     typedef const __attribute__((address_space(4))) float cfloat;
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
 // with 768-wide slices: 35 -> 163 us).
 template <bool FP16X>
 __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                            int tiles_per_slice,
+                                                            int n_tasks, int tiles_per_slice,
                                                             const uint16_t *__restrict__ x,
                                                             int64_t ldx, float *__restrict__ y,
                                                             int64_t ldy)
@@ -138,15 +147,18 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
     constexpr int KB = kFusedMaxRank / kKBlock;   // rank blocks at most
     static_assert(kParts == kDecodeSegRows, "one part and one row per wave");
     const int per_seg = g.n_slices * tiles_per_slice;
-    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
     const int rem = task - si * per_seg;
     const int j = rem / tiles_per_slice;
     const int tile = rem - j * tiles_per_slice;
-    const int hj = g.h_out[j];
-    if (tile * kExpandTile >= hj) return;       // the whole workgroup
-    if (r.counts && si >= r.counts[kCntDecode]) return;
-    const Seg sd = load_seg(r.seg, si);
+    const int hj = pick4(g.h_out, j);
+    const int col_off = pick4(g.col_off, j);
+    const int64_t bt_off = pick4(g.bt_slice_off, j);
+    Seg sd;
+    const bool live = decode_seg(r, si, sd);
+    if (!live || tile * kExpandTile >= hj) return;       // the whole workgroup
+    const float scale = p.scale[sd.slot() * kMetaStride + j];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int rank = sd.rank(j);
@@ -162,9 +174,8 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
 #pragma unroll
     for (int w = 1; w < kDecodeSegRows; ++w)
         if (wave == w) trow = all[w];
-    float *const yp[1] = {y + (int64_t)trow * ldy + g.col_off[j] + oc};
-    const uint16_t *bt =
-        p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j] + oc;
+    float *const yp[1] = {y + (int64_t)trow * ldy + col_off + oc};
+    const uint16_t *bt = p.Bt + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + bt_off + oc;
 
     __shared__ float part[KB][kParts][64];
     __shared__ float vl[kDecodeSegRows][KB * kKBlock];
@@ -183,7 +194,6 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
             const int kb = threadIdx.x >> 6, l = threadIdx.x & 63;
             const float q0 = (part[kb][0][l] + part[kb][1][l]) + (part[kb][2][l] + part[kb][3][l]);
             const float q1 = (part[kb][4][l] + part[kb][5][l]) + (part[kb][6][l] + part[kb][7][l]);
-            const float scale = p.scale[sd.slot() * kMetaStride + j];
             vl[l / kKBlock][kb * kKBlock + l % kKBlock] = scale * (q0 + q1);
         }
         __syncthreads();
@@ -258,7 +268,8 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const int w = n_sub >= 8 ? 8 : n_sub >= 4 ? 4 : n_sub >= 2 ? 2 : 1;
     const dim3 grid((unsigned)blocks), block(64 * w);
 #define LAUNCH_SHRINK(F, W) \
-    hipLaunchKernelGGL((k_shrink_gemv<F, W>), grid, block, 0, s, g, p, r, kb_per_slice, xp, ldx, v)
+    hipLaunchKernelGGL((k_shrink_gemv<F, W>), grid, block, 0, s, g, p, r, (int)blocks, \
+                       kb_per_slice, xp, ldx, v)
     if (g.x_fp16) {
         if (w == 8) LAUNCH_SHRINK(true, 8);
         else if (w == 4) LAUNCH_SHRINK(true, 4);
@@ -284,11 +295,11 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
     const uint16_t *xp = static_cast<const uint16_t *>(x);
     const dim3 grid((unsigned)blocks), block(64 * kParts);
     if (g.x_fp16)
-        hipLaunchKernelGGL(k_delta_gemv<true>, grid, block, 0, s, g, p, r, tiles_per_slice, xp, ldx,
-                           y, ldy);
+        hipLaunchKernelGGL(k_delta_gemv<true>, grid, block, 0, s, g, p, r, (int)blocks,
+                           tiles_per_slice, xp, ldx, y, ldy);
     else
-        hipLaunchKernelGGL(k_delta_gemv<false>, grid, block, 0, s, g, p, r, tiles_per_slice, xp,
-                           ldx, y, ldy);
+        hipLaunchKernelGGL(k_delta_gemv<false>, grid, block, 0, s, g, p, r, (int)blocks,
+                           tiles_per_slice, xp, ldx, y, ldy);
     return hipGetLastError();
 }
 
@@ -300,7 +311,7 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_expand_gemv, dim3((unsigned)blocks), dim3(64 * kExpandWaves), 0, s, g,
-                       p, r, tiles_per_slice, v, y, ldy);
+                       p, r, (int)blocks, tiles_per_slice, v, y, ldy);
     return hipGetLastError();
 }
 
