@@ -76,6 +76,21 @@ __device__ __forceinline__ T pick4(const T (&a)[4], int j)
     return j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
 }
 
+// The kernel arguments of the decode kernels (lane geometry, pool and
+// routing views, then the call's own scalars) span four 64-byte lines.  Left
+// to itself the compiler loads each argument at its first use, so a line
+// first needed deep in the prologue costs one more miss in series.  This
+// asks for one argument of each line at entry, so the four lines are fetched
+// together and later argument loads hit the scalar cache.  The task count
+// passes through the same statement, so the task arithmetic (and everything
+// after it) is placed behind the one wait.
+__device__ __forceinline__ void touch_args(int &n_tasks, const LaneGeom &g, const PoolDev &p,
+                                           const RoutingDev &r, int64_t last)
+{
+    asm volatile("" : "+s"(n_tasks) : "s"(g.h_in), "s"(g.bt_slot_stride), "s"(p.scale),
+                 "s"(r.counts), "s"(last));
+}
+
 // Descriptor of decode segment si into sd, and whether si is one of the
 // batch's decode segments: with device-built routing the grid covers the
 // bound on the count and the tasks past the count end here.  The count and

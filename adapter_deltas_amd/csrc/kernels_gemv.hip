@@ -24,6 +24,7 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
                                                          const uint16_t *__restrict__ x,
                                                          int64_t ldx, float *__restrict__ v)
 {
+    touch_args(n_tasks, g, p, r, ldx);
     const int per_seg = g.n_slices * kb_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
                                                                    int64_t ldy)
 {
     constexpr int C = kExpandRows;
+    touch_args(n_tasks, g, p, r, ldy);
     const int per_seg = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
@@ -146,6 +148,7 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
 {
     constexpr int KB = kFusedMaxRank / kKBlock;   // rank blocks at most
     static_assert(kParts == kDecodeSegRows, "one part and one row per wave");
+    touch_args(n_tasks, g, p, r, ldy);
     const int per_seg = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = task / per_seg;
