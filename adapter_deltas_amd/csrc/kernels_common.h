@@ -69,11 +69,17 @@ __device__ __forceinline__ int xcd_task(int b, int n)
 // selects: indexing the argument segment with a runtime value would make the
 // load of the entry wait for that value, one more dependent scalar load
 // before the kernel's first data load.
+// The empty statement makes the four values opaque, so the compiler neither
+// turns the selects back into a load through a selected address nor into
+// branches.
 template <class T>
 __device__ __forceinline__ T pick4(const T (&a)[4], int j)
 {
-    const T a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
-    return j == 0 ? a0 : j == 1 ? a1 : j == 2 ? a2 : a3;
+    T a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+    asm("" : "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3));
+    const T lo = (j & 1) ? a1 : a0;
+    const T hi = (j & 1) ? a3 : a2;
+    return (j & 2) ? hi : lo;
 }
 
 // The kernel arguments of the decode kernels (lane geometry, pool and

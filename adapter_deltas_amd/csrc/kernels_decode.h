@@ -255,12 +255,20 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[C], int n_rows,
         }
     };
     wait();
-    for (int kb = 0; kb < rank; kb += 16) {
-        fma_b(b0, kb);
-        if (kb + 8 >= rank) break;
-        if (kb + 16 < rank) load_b(b0, kb + 16);
-        fma_b(b1, kb + 8);
-        if (kb + 24 < rank) load_b(b1, kb + 24);
+    // ranks 0..15 peeled (constant kb, so a caller's vsrc can serve them from
+    // registers), then blocks of 16
+    fma_b(b0, 0);
+    if (rank > 8) {
+        if (rank > 16) load_b(b0, 16);
+        fma_b(b1, 8);
+        if (rank > 24) load_b(b1, 24);
+        for (int kb = 16; kb < rank; kb += 16) {
+            fma_b(b0, kb);
+            if (kb + 8 >= rank) break;
+            if (kb + 16 < rank) load_b(b0, kb + 16);
+            fma_b(b1, kb + 8);
+            if (kb + 24 < rank) load_b(b1, kb + 24);
+        }
     }
     if (store) {
 #pragma unroll

@@ -115,8 +115,28 @@ __global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, P
     // become scalar loads.
     typedef const __attribute__((address_space(4))) float cfloat;
     const int64_t vrow0 = (int64_t)(sd.v_row() + c0) * g.v_stride + j * g.rank_pad;
+    auto vrow = [&](int c) {
+        return (cfloat *)(v + vrow0 + (int64_t)min(c, n_rows - 1) * g.v_stride);
+    };
+    // v of ranks 0..15 (inside rank_pad) is requested here, ahead of the B and
+    // y loads, so that it is not the last operand to arrive
+    float vp[C][16];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        cfloat *vr = vrow(c);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float t = vr[k];
+            vp[c][k] = k < rank ? t : 0.f;
+        }
+    }
     auto vsrc = [&](int c, int kb, float (&out)[8]) {
-        cfloat *vr = (cfloat *)(v + vrow0 + (int64_t)min(c, n_rows - 1) * g.v_stride);
+        if (kb < 16) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) out[k] = kb == 0 ? vp[c][k] : vp[c][8 + k];
+            return;
+        }
+        cfloat *vr = vrow(c);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float t = vr[kb + k];
