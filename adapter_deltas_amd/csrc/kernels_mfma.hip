@@ -91,15 +91,16 @@ __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1
 // layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
 template <bool FP16X, int NG, int RT, bool GATHER>
 __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
-    LaneGeom g, PoolDev p, RoutingDev r, int seg_begin, int groups_per_slice,
+    LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
     const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v)
 {
+    touch_args(n_tasks, g, p, r, ldx);
     constexpr int D = kShrinkDepth, ROWS = 16 * RT;
     static_assert(kRowTiles % RT == 0, "row chunks tile the segment");
     // task order within a segment: row chunk, slice, rank group
     const int per_chunk = g.n_slices * groups_per_slice;
     const int per_seg = per_chunk * (kRowTiles / RT);
-    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = seg_begin + task / per_seg;
     const int rem = task % per_seg;
     const int rc = rem / per_chunk;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
 // no wave of a workgroup idles on an empty row block).
 template <int NK, bool GATHER, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 1 ? 2 : NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
-void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
+void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
                                                       int seg_begin, int seg_end, int group,
                                                       int tiles_per_slice,
                                                       const float *__restrict__ v,
@@ -275,13 +276,16 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     constexpr int LDB = KR + 8;                   // padded LDS row of B (bf16)
     constexpr int CPR = KR / 8;                   // 16-byte chunks per staged B row
     static_assert(COLS == 128, "two rows of y per wave instruction");
+    touch_args(n_tasks, g, p, r, ldy);
     const int per_grp = g.n_slices * tiles_per_slice;
-    const int task = xcd_task(blockIdx.x, gridDim.x);
+    const int task = xcd_task(blockIdx.x, n_tasks);
     const int grp = task / per_grp;
     const int rem = task - grp * per_grp;
     const int j = rem / tiles_per_slice;
     const int tile = rem - j * tiles_per_slice;
-    const int hj = g.h_out[j];
+    const int hj = pick4(g.h_out, j);
+    const int col_off = pick4(g.col_off, j);
+    const int64_t bt_off = pick4(g.bt_slice_off, j);
     const int o_base = tile * COLS;
     if (o_base >= hj) return;
     const int s_first = seg_begin + grp * group;
@@ -305,7 +309,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     // columns past the slice its last four columns (h_out is a multiple of 8);
     // only the stores are masked.
     auto y_row = [&](int q) { return r0 + 2 * q + (lane >> 5); };
-    const int ycol = g.col_off[j] + min(yc, hj - 4);
+    const int ycol = col_off + min(yc, hj - 4);
     // token row of this lane's y row q of segment sd
     auto y_tok = [&](Seg sd, int q) -> int {
         const int last = sd.n_rows() - 1;
@@ -350,7 +354,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
         if (slot == staged) return;
         __syncthreads();
         const int rank = sd.rank(j);
-        const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+        const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + bt_off;
         for (int c = threadIdx.x; c < COLS * CPR; c += 64 * WAVES) {
             const int ol = c / CPR, kc = (c - ol * CPR) * 8;
             const int o = o_base + ol;
@@ -372,7 +376,7 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r,
     auto load_b_regs = [&](Seg sd, uint4 (&bq)[CHL]) {
         const int rank = sd.rank(j);
         const uint16_t *Bn =
-            p.Bn + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + g.bt_slice_off[j];
+            p.Bn + (int64_t)(sd.slot() - 1) * g.bt_slot_stride + bt_off;
 #pragma unroll
         for (int i = 0; i < CHL; ++i) {
             const int c = lane + 64 * i;
@@ -504,16 +508,16 @@ static void launch_shrink_t(bool fp16, bool gather, dim3 grid, hipStream_t s, co
     const dim3 block(64 * kShrinkParts);
     if (fp16 && gather)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v);
     else if (fp16)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v);
     else if (gather)
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v);
     else
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v);
 }
 
 template <int NG>
@@ -568,13 +572,13 @@ static void launch_expand_nk(bool gather, bool one_wave, dim3 grid, hipStream_t 
 {
     if (gather && one_wave)
         hipLaunchKernelGGL((k_expand_mfma<NK, true, 1>), grid, dim3(64), 0, s, g, p, r,
-                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
     else if (gather)
         hipLaunchKernelGGL((k_expand_mfma<NK, true, 4>), grid, dim3(256), 0, s, g, p, r,
-                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
     else
         hipLaunchKernelGGL((k_expand_mfma<NK, false, 4>), grid, dim3(256), 0, s, g, p, r,
-                           seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
 }
 
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
