@@ -19,7 +19,6 @@
 
 namespace lora {
 
-constexpr int kExpandRows = 2;       // segment rows per expanding wave
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 

@@ -64,18 +64,20 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
     }
 }
 
-constexpr int kExpandWaves = kDecodeSegRows / kExpandRows;   // waves per expand task
 
 // Prologue as in k_shrink_gemv; the slice's widths and offsets are taken from
 // the arguments by selects.
-__global__ __launch_bounds__(64 * kExpandWaves) void k_expand_gemv(LaneGeom g, PoolDev p,
+// A task is (segment, slice, 512 columns); each of its 8 / C waves expands C
+// segment rows.  C changes which wave computes a row, never its sums.
+template <int C>
+__global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneGeom g, PoolDev p,
                                                                    RoutingDev r, int n_tasks,
                                                                    int tiles_per_slice,
                                                                    const float *__restrict__ v,
                                                                    float *__restrict__ y,
                                                                    int64_t ldy)
 {
-    constexpr int C = kExpandRows;
+    constexpr int kExpandWaves = kDecodeSegRows / C;
     touch_args(n_tasks, g, p, r, ldy);
     const int per_seg = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
@@ -327,14 +329,20 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
 }
 
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int n_seg, int tiles_per_slice, const float *v, float *y,
-                              int64_t ldy, hipStream_t s)
+                              int n_seg, int tiles_per_slice, int rows_per_wave, const float *v,
+                              float *y, int64_t ldy, hipStream_t s)
 {
     const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_expand_gemv, dim3((unsigned)blocks), dim3(64 * kExpandWaves), 0, s, g,
-                       p, r, (int)blocks, tiles_per_slice, v, y, ldy);
+    if (rows_per_wave == 4)
+        hipLaunchKernelGGL(k_expand_gemv<4>, dim3((unsigned)blocks), dim3(64 * 2), 0, s, g, p, r,
+                           (int)blocks, tiles_per_slice, v, y, ldy);
+    else if (rows_per_wave == 2)
+        hipLaunchKernelGGL(k_expand_gemv<2>, dim3((unsigned)blocks), dim3(64 * 4), 0, s, g, p, r,
+                           (int)blocks, tiles_per_slice, v, y, ldy);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -231,7 +231,16 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
     if (decode && I.n_decode_segments > 0) {
         int tiles = (hmax + kExpandTile - 1) / kExpandTile;
-        hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, v, y, ldy, s);
+        // Waves of 4 rows (two per task) when the decode segments are close
+        // to full (at least 7 of 8 rows on average): fewer waves load the
+        // task's B tile.  With emptier segments the second half of such a
+        // wave would mostly repeat a row, so waves take 2 rows (measured on
+        // decode_mix, 7.2 rows a segment: 7.08 -> 6.56 us per call; on
+        // moe_decode, 2.3 rows: 20.0 -> 21.0 us).  The choice changes which
+        // wave computes a row, not its sums.
+        const int rpw = r->decode_rows >= 7 * I.n_decode_segments ? 4 : 2;
+        hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, rpw, v, y,
+                                          ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
     }
     // Consecutive segments share a task (and its staged B tile) while the
@@ -910,6 +919,9 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->distinct_slots = pl.distinct_slots;
     r->slot_ranks = pl.slot_ranks;
     r->max_gather_rows = pl.max_gather_rows;
+    r->decode_rows = 0;
+    for (int32_t i = 0; i < pl.info.n_decode_segments; ++i)
+        r->decode_rows += pl.seg[(size_t)i * kSegWords + 2];
     return LORA_OK;
 }
 
@@ -1040,6 +1052,7 @@ int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_
     r->off_counts = (int32_t)off_counts;
     r->device_built = true;
     r->max_gather_rows = kPrefillSegRows;   // segment sizes are known on the device only
+    r->decode_rows = 0;
     r->pool_max_slots = p->desc.max_slots;
     // Every resident slot may appear in the tables: a pool used with this
     // routing must hold all of them with the same ranks.

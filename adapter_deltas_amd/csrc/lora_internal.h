@@ -99,8 +99,8 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
                              int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
                              int64_t ldy, hipStream_t s);
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int n_seg, int tiles_per_slice, const float *v, float *y,
-                              int64_t ldy, hipStream_t s);
+                              int n_seg, int tiles_per_slice, int rows_per_wave, const float *v,
+                              float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
                               const void *x, int64_t ldx, float *v, hipStream_t s);
@@ -182,6 +182,7 @@ struct lora_routing {
     bool device_built;                // counts on the device, info holds bounds
     int32_t off_counts;
     int32_t max_gather_rows;          // rows of the largest gather segment (bound)
+    int32_t decode_rows;              // rows of the decode segments (0: not known on the host)
     std::vector<int32_t> distinct_slots;
     std::vector<int32_t> slot_ranks;  // kMetaStride per distinct slot
     lora::Plan plan;                  // host tables, reused between builds
