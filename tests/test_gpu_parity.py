@@ -234,6 +234,27 @@ def test_permutation_and_solo_bit_exact(lib, cfg, lane):
         assert np.array_equal(ys.view(np.uint32), y[r].view(np.uint32)), i
 
 
+@pytest.mark.parametrize("cfg,lane", [("many_tenants", "down_proj"), ("tp_share", "attn_out")])
+def test_solo_matches_large_batch_bit_exact(lib, cfg, lane):
+    """The launch shape follows the batch (waves per shrink task by grid size,
+    rows per expand wave by how full the decode segments are); a row's bits
+    must not: sequences of a full-size batch, run alone, give the same bits."""
+    w = generate(config_by_name(cfg), lanes=(lane,))
+    L = w.lanes[lane]
+    pool = load_lane_pool(lib.Pool, w, lane)
+    y, adm, info = run_lane(lib, w, lane, pool=pool)
+    kmax = max(s.rank for ad in w.adapters.values() for s in ad.lanes[lane])
+    tasks = info["n_decode_segments"] * len(L.spec.h_out) * -(-kmax // 8)
+    assert tasks >= 512                    # the large-grid shrink form runs for the batch
+    starts = seq_starts(w.seq_len)
+    active = [i for i in range(len(w.seq_len)) if w.seq_adapter[i] != 0 and adm[i]]
+    for i in np.random.default_rng(3).choice(active, 6, replace=False):
+        r = np.arange(starts[i], starts[i] + w.seq_len[i])
+        ys, _, _ = run_lane(lib, w, lane, pool=pool, x=L.x[r], y0=L.y0[r],
+                            seq_ids=w.seq_adapter[i:i + 1], seq_lens=w.seq_len[i:i + 1])
+        assert np.array_equal(ys.view(np.uint32), y[r].view(np.uint32)), i
+
+
 def test_run_to_run_relocation_and_split_bit_exact(lib):
     w = generate(MID)
     lane = "qkv_like"
