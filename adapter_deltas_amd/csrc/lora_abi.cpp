@@ -192,18 +192,53 @@ int32_t check_v(const float *v)
     return LORA_OK;
 }
 
+// Streams of one call.  The decode kernels (GEMV) and the matrix-core
+// kernels of a batch touch disjoint rows of v and y, so for a batch with
+// both kinds the decode kernels run on the routing's second stream, forked
+// from the caller's stream and joined back into it with events (under graph
+// capture: two parallel branches); otherwise everything runs on the caller's
+// stream.
+struct CallStreams {
+    hipStream_t main;   // the caller's stream: matrix-core kernels
+    hipStream_t dec;    // decode kernels
+};
+
+int32_t fork_streams(const lora_routing *r, hipStream_t s, CallStreams &cs)
+{
+    const lora_routing_info &I = r->info;
+    cs.main = cs.dec = s;
+    const bool mixed = I.n_decode_segments > 0 && I.n_prefill_segments + I.n_gather_segments > 0;
+    if (!mixed || !r->side) return LORA_OK;
+    hipError_t e = hipEventRecord(r->fork_ev, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(r->side, r->fork_ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "forking the decode stream");
+    cs.dec = r->side;
+    return LORA_OK;
+}
+
+int32_t join_streams(const lora_routing *r, const CallStreams &cs)
+{
+    if (cs.dec == cs.main) return LORA_OK;
+    hipError_t e = hipEventRecord(r->join_ev, cs.dec);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs.main, r->join_ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "joining the decode stream");
+    return LORA_OK;
+}
+
 // The kernels of each call.  With decode = false the decode segments are left
 // to the caller (the one-launch decode delta of lora_delta_apply).
 int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
-                       float *v, hipStream_t s, bool decode = true)
+                       float *v, const CallStreams &cs, bool decode = true)
 {
+    hipStream_t s = cs.main;
     const lora_routing_info &I = r->info;
     const int kmax = batch_max_rank(p, r);
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
     if (decode && I.n_decode_segments > 0) {
         int kb = (kmax + kKBlock - 1) / kKBlock;
-        hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, s);
+        hipError_t e =
+            launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, cs.dec);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
     const int nt = (kmax + 15) / 16;
@@ -222,8 +257,9 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
 }
 
 int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v, float *y,
-                       int64_t ldy, hipStream_t s, bool decode = true)
+                       int64_t ldy, const CallStreams &cs, bool decode = true)
 {
+    hipStream_t s = cs.main;
     const lora_routing_info &I = r->info;
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
@@ -240,7 +276,7 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         // wave computes a row, not its sums.
         const int rpw = r->decode_rows >= 7 * I.n_decode_segments ? 4 : 2;
         hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, rpw, v, y,
-                                          ldy, s);
+                                          ldy, cs.dec);
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
     }
     // Consecutive segments share a task (and its staged B tile) while the
@@ -816,6 +852,16 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
         }
     }
     r->stage_next = 0;
+    {
+        // the second stream of mixed batches, at the default priority
+        hipError_t e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->fork_ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&r->join_ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            lora_routing_destroy(r);
+            return hip_fail(e, "creating the routing's second stream");
+        }
+    }
     std::memset(&r->info, 0, sizeof r->info);
     r->off_seg = r->off_row = r->off_tok = 0;
     r->pool_max_slots = 0;
@@ -829,6 +875,12 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
 int32_t lora_routing_destroy(lora_routing *r)
 {
     if (!r) return LORA_OK;
+    if (r->side) {
+        (void)hipStreamSynchronize(r->side);
+        (void)hipStreamDestroy(r->side);
+    }
+    if (r->fork_ev) (void)hipEventDestroy(r->fork_ev);
+    if (r->join_ev) (void)hipEventDestroy(r->join_ev);
     for (int i = 0; i < 2; ++i) {
         if (r->stage_done[i]) {
             (void)hipEventSynchronize(r->stage_done[i]);
@@ -1146,7 +1198,11 @@ int32_t lora_shrink(const lora_pool *p, const lora_routing *r, const void *x, in
     if (r->info.n_active == 0) return LORA_OK;
     if (int32_t rc = check_x(p, x, ldx)) return rc;
     if (int32_t rc = check_v(v)) return rc;
-    return enqueue_shrink(p, r, x, ldx, v, static_cast<hipStream_t>(stream));
+    CallStreams cs;
+    if (int32_t rc = fork_streams(r, static_cast<hipStream_t>(stream), cs)) return rc;
+    const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs);
+    const int32_t rj = join_streams(r, cs);
+    return rc ? rc : rj;
 }
 
 int32_t lora_expand(const lora_pool *p, const lora_routing *r, const float *v, float *y,
@@ -1156,7 +1212,11 @@ int32_t lora_expand(const lora_pool *p, const lora_routing *r, const float *v, f
     if (r->info.n_active == 0) return LORA_OK;
     if (int32_t rc = check_v(v)) return rc;
     if (int32_t rc = check_y(p, y, ldy)) return rc;
-    return enqueue_expand(p, r, v, y, ldy, static_cast<hipStream_t>(stream));
+    CallStreams cs;
+    if (int32_t rc = fork_streams(r, static_cast<hipStream_t>(stream), cs)) return rc;
+    const int32_t rc = enqueue_expand(p, r, v, y, ldy, cs);
+    const int32_t rj = join_streams(r, cs);
+    return rc ? rc : rj;
 }
 
 int32_t lora_workspace_bytes(const lora_pool *p, const lora_routing *r, int64_t *bytes_out)
@@ -1201,13 +1261,18 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
                                 r->info.n_decode_segments;
     const bool fused = r->info.n_decode_segments > 0 && kmax <= kFusedMaxRank &&
                        extra_bytes <= kFusedMaxExtraBytes;
+    CallStreams cs;
+    if (int32_t rc = fork_streams(r, st, cs)) return rc;
+    int32_t rc = LORA_OK;
     if (fused) {
         hipError_t e = launch_delta_gemv(p->geom, pool_dev(p), routing_dev(r),
-                                         r->info.n_decode_segments, tiles, x, ldx, y, ldy, st);
-        if (e != hipSuccess) return hip_fail(e, "delta (decode) launch");
+                                         r->info.n_decode_segments, tiles, x, ldx, y, ldy, cs.dec);
+        if (e != hipSuccess) rc = hip_fail(e, "delta (decode) launch");
     }
-    if (int32_t rc = enqueue_shrink(p, r, x, ldx, v, st, !fused)) return rc;
-    return enqueue_expand(p, r, v, y, ldy, st, !fused);
+    if (rc == LORA_OK) rc = enqueue_shrink(p, r, x, ldx, v, cs, !fused);
+    if (rc == LORA_OK) rc = enqueue_expand(p, r, v, y, ldy, cs, !fused);
+    const int32_t rj = join_streams(r, cs);
+    return rc ? rc : rj;
 }
 
 }  // extern "C"

@@ -183,6 +183,8 @@ struct lora_routing {
     int32_t off_counts;
     int32_t max_gather_rows;          // rows of the largest gather segment (bound)
     int32_t decode_rows;              // rows of the decode segments (0: not known on the host)
+    hipStream_t side;                 // decode kernels of a mixed batch (default priority)
+    hipEvent_t fork_ev, join_ev;      // fork from / join into the caller's stream
     std::vector<int32_t> distinct_slots;
     std::vector<int32_t> slot_ranks;  // kMetaStride per distinct slot
     lora::Plan plan;                  // host tables, reused between builds
