@@ -134,6 +134,29 @@ SMALL_RANK = WorkloadSpec(
     decode_rows=150, base_prob=0.2, prefill_seqs=0, prefill_len=(1, 1))
 
 
+# Decode rows over a wide input (parts of h_in holding one or two
+# sub-chunks) with ranks past 16, for bf16 and fp16 x: delta_apply matches
+# the oracle and, bit for bit, lora_shrink then lora_expand.
+WIDE_DECODE = WorkloadSpec(
+    name="wide_decode", seed=31,
+    lanes=(LaneSpec("fp16_wide", 4616, (264, 72), "fp16"),
+           LaneSpec("bf16_wide", 5128, (520,))),
+    n_adapters=4, ranks=(24, 40, 8, 33), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.5, 2.0), max_rank=48,
+    decode_rows=90, base_prob=0.2, prefill_seqs=0, prefill_len=(1, 1))
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("lane", ["fp16_wide", "bf16_wide"])
+def test_wide_decode_apply_matches_two_calls(lib, lane, mode):
+    w = generate(WIDE_DECODE, mode=mode)
+    y, adm, info = run_lane(lib, w, lane)
+    assert info["n_decode_segments"] and not info["n_prefill_segments"]
+    check_full(w, lane, y, adm)
+    ys, _, _ = run_lane(lib, w, lane, path="split")
+    assert np.array_equal(y.view(np.uint32), ys.view(np.uint32))
+
+
 @pytest.mark.parametrize("mode", ["real", "int"])
 @pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
 def test_one_launch_decode_delta_matches_split(lib, lane, mode):
