@@ -24,10 +24,15 @@
  *   - Device buffers (x, y, pool memory, routing memory, workspace) belong to
  *     the caller; the library never allocates or frees device memory.  The
  *     library owns only its opaque host handles and, inside a routing handle,
- *     two small pinned host staging buffers.
+ *     two small pinned host staging buffers and a stream with two events.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued on it asynchronously; nothing synchronises
- *     except where a call says so.
+ *     except where a call says so.  A compute call on a batch with both
+ *     decode and matrix-core segments runs its decode kernels on a second
+ *     stream owned by the routing handle, which waits for `stream`'s earlier
+ *     work and which `stream` waits for before its later work (events; two
+ *     parallel branches under graph capture), so for the caller the call is
+ *     still ordered on `stream` alone.
  *   - A handle must not be used by two threads at once.  Buffers written by
  *     a call must not be read or written on another stream until that
  *     stream's work is ordered after the call.
@@ -206,7 +211,9 @@ int32_t lora_pool_slot_of(const lora_pool *pool, int32_t adapter_id, int32_t *sl
  * Routing memory is one caller-allocated device buffer of
  * lora_routing_bytes(max_tokens) bytes.  The handle also owns two pinned host
  * staging buffers, so building the next batch's routing can overlap the
- * device work of the previous one.
+ * device work of the previous one, and one stream (default priority) with
+ * two events for the decode kernels of mixed batches, on the device current
+ * at lora_routing_create; lora_routing_destroy waits for that stream.
  */
 int32_t lora_routing_bytes(int32_t max_tokens, int64_t *bytes_out);
 
