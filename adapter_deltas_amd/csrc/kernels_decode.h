@@ -200,7 +200,24 @@ __device__ __forceinline__ void widen_bf16x8(uint4 b, float (&f)[8])
     f[7] = __uint_as_float(b.w & 0xffff0000u);
 }
 
-// Expand of C rows of a decode segment over 8 columns per lane.
+// B^T of LC = 8 or 4 adjacent columns of one rank, as one 16- or 8-byte load.
+template <int LC> struct BLoad;
+template <> struct BLoad<8> {
+    typedef uint4 T;
+    __device__ static void widen(T b, float (&f)[8]) { widen_bf16x8(b, f); }
+};
+template <> struct BLoad<4> {
+    typedef uint2 T;
+    __device__ static void widen(T b, float (&f)[4])
+    {
+        f[0] = __uint_as_float(b.x << 16);
+        f[1] = __uint_as_float(b.x & 0xffff0000u);
+        f[2] = __uint_as_float(b.y << 16);
+        f[3] = __uint_as_float(b.y & 0xffff0000u);
+    }
+};
+
+// Expand of C rows of a decode segment over LC (8 or 4) columns per lane.
 //   yp[c]    y of segment row c at this lane's columns (valid for every c)
 //   n_rows   rows of the C that belong to the segment (may exceed C, rows
 //            from C on being another wave's, or be <= 0: nothing is stored)
@@ -210,20 +227,22 @@ __device__ __forceinline__ void widen_bf16x8(uint4 b, float (&f)[8])
 //   vsrc     vsrc(c, kb, out) fills out[0..8) with v of row c, ranks kb..kb+7
 //            (ranks at or past `rank` must come back as zero)
 // y[row c][cols] += sum_k B[k] v[c][k] for c < n_rows, when store is true.
-template <int C, class Wait, class VSrc>
+template <int C, int LC, class Wait, class VSrc>
 __device__ __forceinline__ void expand_rows(float *const (&yp)[C], int n_rows,
                                             const uint16_t *bt, int hj, int rank, bool store,
                                             Wait wait, VSrc vsrc)
 {
+    static_assert(LC == 8 || LC == 4, "8 or 4 columns per lane");
+    typedef typename BLoad<LC>::T BV;
     // Ranks in blocks of 8 (pool rows past the rank are zero and in bounds;
     // v past the rank is zero), the next block's B loads in flight.  Loads
     // complete in issue order, so the first two B blocks (rows 0..15, inside
     // rank_pad) are issued before y: their products then run while y is
     // still on its way from HBM.
-    uint4 b0[8], b1[8];
-    auto load_b = [&](uint4 (&b)[8], int kb) {
+    BV b0[8], b1[8];
+    auto load_b = [&](BV (&b)[8], int kb) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) b[k] = ld16(bt + (int64_t)(kb + k) * hj);
+        for (int k = 0; k < 8; ++k) b[k] = *reinterpret_cast<const BV *>(bt + (int64_t)(kb + k) * hj);
     };
     load_b(b0, 0);
     load_b(b1, 8);
@@ -232,25 +251,25 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[C], int n_rows,
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         ya[c] = reinterpret_cast<const float4 *>(yp[c])[0];
-        yb[c] = reinterpret_cast<const float4 *>(yp[c])[1];
+        if constexpr (LC == 8) yb[c] = reinterpret_cast<const float4 *>(yp[c])[1];
     }
-    float acc[C][8];
+    float acc[C][LC];
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-    auto fma_b = [&](const uint4 (&b)[8], int kb) {
+        for (int e = 0; e < LC; ++e) acc[c][e] = 0.f;
+    auto fma_b = [&](const BV (&b)[8], int kb) {
         float vk[C][8];
 #pragma unroll
         for (int c = 0; c < C; ++c) vsrc(c, kb, vk[c]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            float bf[8];
-            widen_bf16x8(b[k], bf);
+            float bf[LC];
+            BLoad<LC>::widen(b[k], bf);
 #pragma unroll
             for (int c = 0; c < C; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[c][e] = __builtin_fmaf(bf[e], vk[c][k], acc[c][e]);
+                for (int e = 0; e < LC; ++e) acc[c][e] = __builtin_fmaf(bf[e], vk[c][k], acc[c][e]);
         }
     };
     wait();
@@ -273,17 +292,20 @@ __device__ __forceinline__ void expand_rows(float *const (&yp)[C], int n_rows,
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             if (c < n_rows) {
-                float4 a = ya[c], b = yb[c];
+                float4 a = ya[c];
                 a.x += acc[c][0];
                 a.y += acc[c][1];
                 a.z += acc[c][2];
                 a.w += acc[c][3];
-                b.x += acc[c][4];
-                b.y += acc[c][5];
-                b.z += acc[c][6];
-                b.w += acc[c][7];
                 reinterpret_cast<float4 *>(yp[c])[0] = a;
-                reinterpret_cast<float4 *>(yp[c])[1] = b;
+                if constexpr (LC == 8) {
+                    float4 b = yb[c];
+                    b.x += acc[c][4];
+                    b.y += acc[c][5];
+                    b.z += acc[c][6];
+                    b.w += acc[c][7];
+                    reinterpret_cast<float4 *>(yp[c])[1] = b;
+                }
             }
         }
     }

@@ -69,9 +69,10 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
 
 // Prologue as in k_shrink_gemv; the slice's widths and offsets are taken from
 // the arguments by selects.
-// A task is (segment, slice, 512 columns); each of its 8 / C waves expands C
-// segment rows.  C changes which wave computes a row, never its sums.
-template <int C>
+// A task is (segment, slice, 64 LC columns), LC = 8 or 4 columns per lane;
+// each of its 8 / C waves expands C segment rows.  C and LC change which
+// wave computes an output, never its sum.
+template <int C, int LC>
 __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneGeom g, PoolDev p,
                                                                    RoutingDev r, int n_tasks,
                                                                    int tiles_per_slice,
@@ -92,16 +93,17 @@ __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneG
     const int64_t bt_off = pick4(g.bt_slice_off, j);
     Seg sd;
     const bool live = decode_seg(r, si, sd);
-    if (!live || tile * kExpandTile >= hj) return;
+    constexpr int TILE = 64 * LC;
+    if (!live || tile * TILE >= hj) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c0 = wave * C;                    // first segment row of this wave
     const int n_rows = sd.n_rows() - c0;        // rows of this wave (may be <= 0)
     if (n_rows <= 0) return;
     const int rank = sd.rank(j);
-    const int o0 = tile * kExpandTile + lane * 8;
+    const int o0 = tile * TILE + lane * LC;
     const bool col_ok = o0 < hj;
-    const int oc = col_ok ? o0 : hj - 8;
+    const int oc = col_ok ? o0 : hj - LC;
     // token rows c0 .. c0 + C - 1 of the segment (wave-uniform selection)
     const int all[kDecodeSegRows] = {sd.row<0>(), sd.row<1>(), sd.row<2>(), sd.row<3>(),
                                      sd.row<4>(), sd.row<5>(), sd.row<6>(), sd.row<7>()};
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneG
             out[k] = kb + k < rank ? t : 0.f;
         }
     };
-    expand_rows<C>(yp, n_rows, bt, hj, rank, col_ok, [] {}, vsrc);
+    expand_rows<C, LC>(yp, n_rows, bt, hj, rank, col_ok, [] {}, vsrc);
 }
 
 // Shrink and expand of decode segments in one launch, for ranks up to
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
 #pragma unroll
         for (int k = 0; k < 8; ++k) out[k] = kb + k < rank ? vl[wave][kb + k] : 0.f;
     };
-    expand_rows<1>(yp, sd.n_rows() - wave, bt, hj, rank, col_ok, shrink, vsrc);
+    expand_rows<1, 8>(yp, sd.n_rows() - wave, bt, hj, rank, col_ok, shrink, vsrc);
 }
 
 // ---- pool maintenance ----
@@ -338,20 +340,25 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
 }
 
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int n_seg, int tiles_per_slice, int rows_per_wave, const float *v,
+                              int n_seg, int rows_per_wave, int lane_cols, const float *v,
                               float *y, int64_t ldy, hipStream_t s)
 {
+    int hmax = 0;
+    for (int j = 0; j < g.n_slices; ++j) hmax = std::max(hmax, g.h_out[j]);
+    const int tiles_per_slice = (hmax + 64 * lane_cols - 1) / (64 * lane_cols);
     const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    if (rows_per_wave == 4)
-        hipLaunchKernelGGL(k_expand_gemv<4>, dim3((unsigned)blocks), dim3(64 * 2), 0, s, g, p, r,
-                           (int)blocks, tiles_per_slice, v, y, ldy);
-    else if (rows_per_wave == 2)
-        hipLaunchKernelGGL(k_expand_gemv<2>, dim3((unsigned)blocks), dim3(64 * 4), 0, s, g, p, r,
-                           (int)blocks, tiles_per_slice, v, y, ldy);
-    else
-        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks);
+#define LAUNCH_EXPAND(C, LC)                                                                      \
+    hipLaunchKernelGGL((k_expand_gemv<C, LC>), grid, dim3(64 * (kDecodeSegRows / C)), 0, s, g, p, \
+                       r, (int)blocks, tiles_per_slice, v, y, ldy)
+    if (rows_per_wave == 4 && lane_cols == 8) LAUNCH_EXPAND(4, 8);
+    else if (rows_per_wave == 4 && lane_cols == 4) LAUNCH_EXPAND(4, 4);
+    else if (rows_per_wave == 2 && lane_cols == 8) LAUNCH_EXPAND(2, 8);
+    else if (rows_per_wave == 2 && lane_cols == 4) LAUNCH_EXPAND(2, 4);
+    else return hipErrorInvalidValue;
+#undef LAUNCH_EXPAND
     return hipGetLastError();
 }
 

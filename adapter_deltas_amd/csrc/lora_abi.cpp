@@ -266,7 +266,6 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     int hmax = 0;
     for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
     if (decode && I.n_decode_segments > 0) {
-        int tiles = (hmax + kExpandTile - 1) / kExpandTile;
         // Waves of 4 rows (two per task) when the decode segments are close
         // to full (at least 7 of 8 rows on average): fewer waves load the
         // task's B tile.  With emptier segments the second half of such a
@@ -275,7 +274,12 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         // moe_decode, 2.3 rows: 20.0 -> 21.0 us).  The choice changes which
         // wave computes a row, not its sums.
         const int rpw = r->decode_rows >= 7 * I.n_decode_segments ? 4 : 2;
-        hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, tiles, rpw, v, y,
+        // Columns per lane: 4 (256-column tasks, twice the workgroups, half
+        // the fmas per wave) for sparse segments, 8 otherwise (measured per
+        // call with 8 / 4: moe_decode, 2.3 rows a segment, 20.4 / 19.0 us;
+        // decode_mix 6.56 / 6.78; many_tenants 21.3 / 24.4).
+        const int lc = r->expand_lane_cols == 4 ? 4 : 8;
+        hipError_t e = launch_expand_gemv(p->geom, pd, rd, I.n_decode_segments, rpw, lc, v, y,
                                           ldy, cs.dec);
         if (e != hipSuccess) return hip_fail(e, "expand (decode) launch");
     }
@@ -974,6 +978,8 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->decode_rows = 0;
     for (int32_t i = 0; i < pl.info.n_decode_segments; ++i)
         r->decode_rows += pl.seg[(size_t)i * kSegWords + 2];
+    // fewer than 4 rows a decode segment on average: sparse
+    r->expand_lane_cols = r->decode_rows < 4 * pl.info.n_decode_segments ? 4 : 8;
     return LORA_OK;
 }
 
@@ -1105,6 +1111,10 @@ int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_
     r->device_built = true;
     r->max_gather_rows = kPrefillSegRows;   // segment sizes are known on the device only
     r->decode_rows = 0;
+    // A MoE layer's dispatched rows spread over (adapter, expert) pairs, so
+    // its decode segments are sparse; other device-built batches are taken
+    // as dense (segment fill is known on the device only).
+    r->expand_lane_cols = moe ? 4 : 8;
     r->pool_max_slots = p->desc.max_slots;
     // Every resident slot may appear in the tables: a pool used with this
     // routing must hold all of them with the same ranks.

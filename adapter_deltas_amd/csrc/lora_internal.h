@@ -99,7 +99,7 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
                              int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
                              int64_t ldy, hipStream_t s);
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              int n_seg, int tiles_per_slice, int rows_per_wave, const float *v,
+                              int n_seg, int rows_per_wave, int lane_cols, const float *v,
                               float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
@@ -183,6 +183,7 @@ struct lora_routing {
     int32_t off_counts;
     int32_t max_gather_rows;          // rows of the largest gather segment (bound)
     int32_t decode_rows;              // rows of the decode segments (0: not known on the host)
+    int32_t expand_lane_cols;         // columns per lane of the decode expand: 8 or 4 (0: 8)
     hipStream_t side;                 // decode kernels of a mixed batch (default priority)
     hipEvent_t fork_ev, join_ev;      // fork from / join into the caller's stream
     std::vector<int32_t> distinct_slots;
