@@ -106,11 +106,12 @@ struct ShrinkTile {
     uint4 a[kKBlock];
 };
 
-template <bool FP16X>
+// Only the first R rows are loaded and multiplied (the others' sums stay 0).
+template <bool FP16X, int R>
 __device__ __forceinline__ void shrink_tile_fma(const ShrinkTile &t, bool valid,
                                                 float (&acc)[kDecodeSegRows][kKBlock])
 {
-    constexpr int C = kDecodeSegRows;
+    constexpr int C = R;
     uint32_t xw[C][FP16X ? 8 : 4];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -145,8 +146,12 @@ __device__ __forceinline__ void shrink_tile_fma(const ShrinkTile &t, bool valid,
 
 // One wave's part sum for the 8 x 8 (row, rank) block of a shrink task:
 // part `part` of h_in, reduced over the wave; lane L returns the value of
-// (row L / 8, rank k0 + L % 8).
-template <bool FP16X>
+// (row L / 8, rank k0 + L % 8).  With R < 8 only rows 0 .. R-1 are loaded
+// and multiplied and the other rows sum to 0: every (row, rank) value has
+// its own chain of pair-dots and its own path through the butterfly, so the
+// computed rows get the same bits as with R = 8 (for segments of at most R
+// rows, at a fraction of the loads and products).
+template <bool FP16X, int R = kDecodeSegRows>
 __device__ __forceinline__ float shrink_part(const LaneGeom &g, const PoolDev &p, const Seg &sd,
                                              int j, int k0, int kn, int part, int lane,
                                              const uint16_t *__restrict__ x, int64_t ldx)
@@ -175,10 +180,10 @@ __device__ __forceinline__ float shrink_part(const LaneGeom &g, const PoolDev &p
         const int e = min(e_raw, g.h_in - 8);
         ShrinkTile t;
 #pragma unroll
-        for (int c = 0; c < C; ++c) t.x[c] = ld16(xr[c] + e);
+        for (int c = 0; c < R; ++c) t.x[c] = ld16(xr[c] + e);
 #pragma unroll
         for (int k = 0; k < kKBlock; ++k) t.a[k] = ld16(ar[k] + e);
-        shrink_tile_fma<FP16X>(t, e_raw < g.h_in, acc);
+        shrink_tile_fma<FP16X, R>(t, e_raw < g.h_in, acc);
     }
     float val[64];
 #pragma unroll

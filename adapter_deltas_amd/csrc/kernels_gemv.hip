@@ -46,13 +46,20 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
     const int lane = threadIdx.x & 63;
     const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
 
+    // rows past the segment are not multiplied (same bits for the others)
+    const int nr = sd.n_rows();
     __shared__ float part[kParts][64];
 #pragma unroll
     for (int pp = 0; pp < kParts / W; ++pp) {
         const int pt = wave + pp * W;
         // a part with no sub-chunk sums to zero
-        part[pt][lane] =
-            pt < n_sub ? shrink_part<FP16X>(g, p, sd, j, k0, kn, pt, lane, x, ldx) : 0.f;
+        float u = 0.f;
+        if (pt < n_sub) {
+            if (nr <= 2) u = shrink_part<FP16X, 2>(g, p, sd, j, k0, kn, pt, lane, x, ldx);
+            else if (nr <= 4) u = shrink_part<FP16X, 4>(g, p, sd, j, k0, kn, pt, lane, x, ldx);
+            else u = shrink_part<FP16X, 8>(g, p, sd, j, k0, kn, pt, lane, x, ldx);
+        }
+        part[pt][lane] = u;
     }
     __syncthreads();
     if (wave == 0) {
