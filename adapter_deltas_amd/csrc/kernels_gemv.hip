@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
                              : 0.f;
         }
         __syncthreads();
-        if (threadIdx.x < n_kb * 64) {
+        if ((int)threadIdx.x < n_kb * 64) {
             const int kb = threadIdx.x >> 6, l = threadIdx.x & 63;
             const float q0 = (part[kb][0][l] + part[kb][1][l]) + (part[kb][2][l] + part[kb][3][l]);
             const float q1 = (part[kb][4][l] + part[kb][5][l]) + (part[kb][6][l] + part[kb][7][l]);

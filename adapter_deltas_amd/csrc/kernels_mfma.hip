@@ -262,7 +262,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
 // segments cut that small for batches of small (adapter, expert) groups, so
 // no wave of a workgroup idles on an empty row block).
 template <int NK, bool GATHER, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 1 ? 2 : NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 1 ? (NK <= 2 ? 2 : 1) : NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
 void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
                                                       int seg_begin, int seg_end, int group,
                                                       int tiles_per_slice,

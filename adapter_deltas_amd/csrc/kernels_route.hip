@@ -281,7 +281,6 @@ __global__ __launch_bounds__(THREADS) void k_route_decode(
     block_exclusive_sum2<NW>(make_int2(n_ok | n_ok_decode << 16, n_bad | n_unedited << 16), lane,
                              wave, part2, cnt);
     const int na = cnt.x & 0xffff;          // active rows
-    const int fg = cnt.x >> 16;             // decode rows, sorted before the gathered ones
     const int n_invalid = cnt.y & 0xffff;
     const int n_unedited_rows = cnt.y >> 16;
 
