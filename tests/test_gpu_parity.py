@@ -403,3 +403,38 @@ def test_graph_replays_match_eager(lib):
             g.replay()
             torch.cuda.synchronize()
             assert np.array_equal(yg.cpu().numpy().view(np.uint32), ref), (lane, i)
+
+
+def test_graph_replays_of_split_calls_on_a_mixed_batch(lib):
+    """lora_shrink and lora_expand captured separately on a batch with decode,
+    prefill and gather segments (each call forks its decode kernels to the
+    routing's second stream and joins them back): every replay gives the
+    bits of an eager delta_apply."""
+    import torch
+    w = generate(MID)
+    lane = "qkv_like"
+    L = w.lanes[lane]
+    pool = load_lane_pool(lib.Pool, w, lane)
+    routing = lib.Routing(int(np.sum(w.seq_len)), len(w.seq_len))
+    routing.build(pool, w.seq_adapter, w.seq_len, w.spec.max_loras)
+    info = routing.info()
+    assert info["n_decode_segments"] and (info["n_prefill_segments"] or info["n_gather_segments"])
+    xd, y0 = to_device_x(L.x), to_device_y(L.y0)
+    ye = y0.clone()
+    lib.delta_apply(pool, routing, xd, ye)
+    torch.cuda.synchronize()
+    ref = ye.cpu().numpy().view(np.uint32)
+    v = torch.zeros(max(info["n_active"], 1) * pool.v_stride, dtype=torch.float32, device="cuda")
+    yg = torch.empty_like(y0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        yg.copy_(y0)
+        lib.shrink(pool, routing, xd, v)
+        lib.expand(pool, routing, v, yg)
+    for i in range(3):
+        yg.fill_(float("nan"))
+        v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(yg.cpu().numpy().view(np.uint32), ref), i
