@@ -11,7 +11,7 @@ from .lora import (
     lora_plan_routing,
     lora_routing_token_slots, lora_build_routing_device, lora_build_routing_moe,
     lora_build_routing_rows, lora_plan_rows,
-    lora_routing_device_counts, moe_slot,
+    lora_routing_device_counts, moe_slot, moe_row_slots,
     lora_shrink, lora_expand, lora_workspace_bytes,
     lora_delta_apply,
 )
@@ -20,4 +20,5 @@ _lib.load()
 
 __all__ = [n for n in dir() if n.startswith(("lora_", "Lora")) or n in (
     "Pool", "Routing", "make_desc", "workspace_for", "shrink", "expand", "delta_apply",
-    "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS", "moe_slot")]
+    "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS", "moe_slot",
+    "moe_row_slots")]

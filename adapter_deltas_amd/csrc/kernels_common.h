@@ -65,6 +65,19 @@ __device__ __forceinline__ int xcd_task(int b, int n)
     return xcd * q + min(xcd, rem) + local;
 }
 
+// Slice j and tile within the slice of tile number `rem` of a segment, by
+// compares and selects on the widths in the kernel arguments, so every task
+// of a launch is a live tile and none waits for a table load to find that out.
+template <int TILE>
+__device__ __forceinline__ void slice_tile(const LaneGeom &g, int rem, int &j, int &tile)
+{
+    const int c1 = (g.h_out[0] + TILE - 1) / TILE;
+    const int c2 = c1 + (g.h_out[1] + TILE - 1) / TILE;
+    const int c3 = c2 + (g.h_out[2] + TILE - 1) / TILE;
+    j = (rem >= c1) + (rem >= c2) + (rem >= c3);
+    tile = rem - (rem >= c3 ? c3 : rem >= c2 ? c2 : rem >= c1 ? c1 : 0);
+}
+
 // Entry j (0..3) of a 4-entry array held in the kernel arguments, taken by
 // selects: indexing the argument segment with a runtime value would make the
 // load of the entry wait for that value, one more dependent scalar load

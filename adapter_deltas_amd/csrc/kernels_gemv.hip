@@ -82,26 +82,24 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
 template <int C, int LC>
 __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneGeom g, PoolDev p,
                                                                    RoutingDev r, int n_tasks,
-                                                                   int tiles_per_slice,
+                                                                   int tiles_per_seg,
                                                                    const float *__restrict__ v,
                                                                    float *__restrict__ y,
                                                                    int64_t ldy)
 {
     constexpr int kExpandWaves = kDecodeSegRows / C;
+    constexpr int TILE = 64 * LC;
     touch_args(n_tasks, g, p, r, ldy);
-    const int per_seg = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
-    const int si = task / per_seg;
-    const int rem = task - si * per_seg;
-    const int j = rem / tiles_per_slice;
-    const int tile = rem - j * tiles_per_slice;
+    const int si = task / tiles_per_seg;
+    int j, tile;
+    slice_tile<TILE>(g, task - si * tiles_per_seg, j, tile);
     const int hj = pick4(g.h_out, j);
     const int col_off = pick4(g.col_off, j);
     const int64_t bt_off = pick4(g.bt_slice_off, j);
     Seg sd;
     const bool live = decode_seg(r, si, sd);
-    constexpr int TILE = 64 * LC;
-    if (!live || tile * TILE >= hj) return;
+    if (!live) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c0 = wave * C;                    // first segment row of this wave
@@ -174,7 +172,7 @@ __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneG
 // with 768-wide slices: 35 -> 163 us).
 template <bool FP16X>
 __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev p, RoutingDev r,
-                                                            int n_tasks, int tiles_per_slice,
+                                                            int n_tasks, int tiles_per_seg,
                                                             const uint16_t *__restrict__ x,
                                                             int64_t ldx, float *__restrict__ y,
                                                             int64_t ldy)
@@ -182,18 +180,16 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
     constexpr int KB = kFusedMaxRank / kKBlock;   // rank blocks at most
     static_assert(kParts == kDecodeSegRows, "one part and one row per wave");
     touch_args(n_tasks, g, p, r, ldy);
-    const int per_seg = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
-    const int si = task / per_seg;
-    const int rem = task - si * per_seg;
-    const int j = rem / tiles_per_slice;
-    const int tile = rem - j * tiles_per_slice;
+    const int si = task / tiles_per_seg;
+    int j, tile;
+    slice_tile<kExpandTile>(g, task - si * tiles_per_seg, j, tile);
     const int hj = pick4(g.h_out, j);
     const int col_off = pick4(g.col_off, j);
     const int64_t bt_off = pick4(g.bt_slice_off, j);
     Seg sd;
     const bool live = decode_seg(r, si, sd);
-    if (!live || tile * kExpandTile >= hj) return;       // the whole workgroup
+    if (!live) return;       // the whole workgroup
     const float scale = p.scale[sd.slot() * kMetaStride + j];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -329,20 +325,21 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
 }
 
 hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                             int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
-                             int64_t ldy, hipStream_t s)
+                             int n_seg, const void *x, int64_t ldx, float *y, int64_t ldy,
+                             hipStream_t s)
 {
-    const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
+    const int tiles_per_seg = lane_tiles(g, kExpandTile);
+    const int64_t blocks = (int64_t)n_seg * tiles_per_seg;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
     const dim3 grid((unsigned)blocks), block(64 * kParts);
     if (g.x_fp16)
         hipLaunchKernelGGL(k_delta_gemv<true>, grid, block, 0, s, g, p, r, (int)blocks,
-                           tiles_per_slice, xp, ldx, y, ldy);
+                           tiles_per_seg, xp, ldx, y, ldy);
     else
         hipLaunchKernelGGL(k_delta_gemv<false>, grid, block, 0, s, g, p, r, (int)blocks,
-                           tiles_per_slice, xp, ldx, y, ldy);
+                           tiles_per_seg, xp, ldx, y, ldy);
     return hipGetLastError();
 }
 
@@ -350,16 +347,15 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
                               int n_seg, int rows_per_wave, int lane_cols, const float *v,
                               float *y, int64_t ldy, hipStream_t s)
 {
-    int hmax = 0;
-    for (int j = 0; j < g.n_slices; ++j) hmax = std::max(hmax, g.h_out[j]);
-    const int tiles_per_slice = (hmax + 64 * lane_cols - 1) / (64 * lane_cols);
-    const int64_t blocks = (int64_t)n_seg * g.n_slices * tiles_per_slice;
+    // only live tiles: ceil(h_j / columns per task) for each slice j
+    const int tiles_per_seg = lane_tiles(g, 64 * lane_cols);
+    const int64_t blocks = (int64_t)n_seg * tiles_per_seg;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
 #define LAUNCH_EXPAND(C, LC)                                                                      \
     hipLaunchKernelGGL((k_expand_gemv<C, LC>), grid, dim3(64 * (kDecodeSegRows / C)), 0, s, g, p, \
-                       r, (int)blocks, tiles_per_slice, v, y, ldy)
+                       r, (int)blocks, tiles_per_seg, v, y, ldy)
     if (rows_per_wave == 4 && lane_cols == 8) LAUNCH_EXPAND(4, 8);
     else if (rows_per_wave == 4 && lane_cols == 4) LAUNCH_EXPAND(4, 4);
     else if (rows_per_wave == 2 && lane_cols == 8) LAUNCH_EXPAND(2, 8);

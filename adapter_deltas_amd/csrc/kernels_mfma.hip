@@ -265,7 +265,7 @@ template <int NK, bool GATHER, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES == 1 ? (NK <= 2 ? 2 : 1) : NK == 1 ? 3 : NK <= 4 ? 2 : 1)))
 void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
                                                       int seg_begin, int seg_end, int group,
-                                                      int tiles_per_slice,
+                                                      int tiles_per_grp,
                                                       const float *__restrict__ v,
                                                       float *__restrict__ y, int64_t ldy)
 {
@@ -277,17 +277,14 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
     constexpr int CPR = KR / 8;                   // 16-byte chunks per staged B row
     static_assert(COLS == 128, "two rows of y per wave instruction");
     touch_args(n_tasks, g, p, r, ldy);
-    const int per_grp = g.n_slices * tiles_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
-    const int grp = task / per_grp;
-    const int rem = task - grp * per_grp;
-    const int j = rem / tiles_per_slice;
-    const int tile = rem - j * tiles_per_slice;
+    const int grp = task / tiles_per_grp;
+    int j, tile;
+    slice_tile<COLS>(g, task - grp * tiles_per_grp, j, tile);
     const int hj = pick4(g.h_out, j);
     const int col_off = pick4(g.col_off, j);
     const int64_t bt_off = pick4(g.bt_slice_off, j);
     const int o_base = tile * COLS;
-    if (o_base >= hj) return;
     const int s_first = seg_begin + grp * group;
     int s_last = min(s_first + group, seg_end);
     if (r.counts) s_last = min(s_last, seg_begin + r.counts[kCntGather]);   // device-built routing
@@ -567,30 +564,32 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
 template <int NK>
 static void launch_expand_nk(bool gather, bool one_wave, dim3 grid, hipStream_t s,
                              const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                             int seg_begin, int seg_end, int group, int tiles_per_slice,
+                             int seg_begin, int seg_end, int group, int tiles_per_grp,
                              const float *v, float *y, int64_t ldy)
 {
     if (gather && one_wave)
         hipLaunchKernelGGL((k_expand_mfma<NK, true, 1>), grid, dim3(64), 0, s, g, p, r,
-                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_grp, v, y, ldy);
     else if (gather)
         hipLaunchKernelGGL((k_expand_mfma<NK, true, 4>), grid, dim3(256), 0, s, g, p, r,
-                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_grp, v, y, ldy);
     else
         hipLaunchKernelGGL((k_expand_mfma<NK, false, 4>), grid, dim3(256), 0, s, g, p, r,
-                           (int)grid.x, seg_begin, seg_end, group, tiles_per_slice, v, y, ldy);
+                           (int)grid.x, seg_begin, seg_end, group, tiles_per_grp, v, y, ldy);
 }
 
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              bool gather, int seg_begin, int n_seg, int group,
-                              int tiles_per_slice, int max_rank, int max_seg_rows,
-                              const float *v, float *y, int64_t ldy, hipStream_t s)
+                              bool gather, int seg_begin, int n_seg, int group, int max_rank,
+                              int max_seg_rows, const float *v, float *y, int64_t ldy,
+                              hipStream_t s)
 {
     if (n_seg <= 0) return hipSuccess;
     if (group < 1 || max_rank < 1 || max_rank > 256) return hipErrorInvalidValue;
     if (max_seg_rows < 1 || max_seg_rows > kPrefillSegRows) return hipErrorInvalidValue;
     const int64_t groups = (n_seg + group - 1) / group;
-    const int64_t blocks = groups * g.n_slices * tiles_per_slice;
+    // only live tiles: ceil(h_j / 128) for each slice j
+    const int tiles_per_grp = lane_tiles(g, kMfmaExpandCols);
+    const int64_t blocks = groups * tiles_per_grp;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const int seg_end = seg_begin + n_seg;
@@ -599,16 +598,16 @@ hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const Routing
     const bool one_wave = gather && max_seg_rows <= 16;
     if (nk <= 1)
         launch_expand_nk<1>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
-                            tiles_per_slice, v, y, ldy);
+                            tiles_per_grp, v, y, ldy);
     else if (nk <= 2)
         launch_expand_nk<2>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
-                            tiles_per_slice, v, y, ldy);
+                            tiles_per_grp, v, y, ldy);
     else if (nk <= 4)
         launch_expand_nk<4>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
-                            tiles_per_slice, v, y, ldy);
+                            tiles_per_grp, v, y, ldy);
     else
         launch_expand_nk<8>(gather, one_wave, grid, s, g, p, r, seg_begin, seg_end, group,
-                            tiles_per_slice, v, y, ldy);
+                            tiles_per_grp, v, y, ldy);
     return hipGetLastError();
 }
 

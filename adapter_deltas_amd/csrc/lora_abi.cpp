@@ -13,8 +13,10 @@
 using namespace lora;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
+
+namespace lora {
 
 int32_t fail(int32_t code, const char *fmt, ...)
 {
@@ -31,6 +33,10 @@ int32_t hip_fail(hipError_t e, const char *what)
 {
     return fail(LORA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+}  // namespace lora
+
+namespace {
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -263,8 +269,6 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     const lora_routing_info &I = r->info;
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
-    int hmax = 0;
-    for (int j = 0; j < p->desc.n_slices; ++j) hmax = std::max(hmax, p->desc.h_out[j]);
     if (decode && I.n_decode_segments > 0) {
         // Waves of 4 rows (two per task) when the decode segments are close
         // to full (at least 7 of 8 rows on average): fewer waves load the
@@ -285,8 +289,7 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     }
     // Consecutive segments share a task (and its staged B tile) while the
     // grid still has about kExpandTargetBlocks workgroups.
-    const int tiles = (hmax + kMfmaExpandCols - 1) / kMfmaExpandCols;
-    const int64_t per_group = (int64_t)p->desc.n_slices * tiles;
+    const int64_t per_group = lane_tiles(p->geom, kMfmaExpandCols);
     auto group_for = [&](int n) {
         const int64_t fit = (int64_t)n * per_group / kExpandTargetBlocks;
         return (int)std::max<int64_t>(1, std::min<int64_t>(kExpandMaxGroup, fit));
@@ -295,15 +298,14 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
     if (I.n_prefill_segments > 0) {
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, false, I.n_decode_segments,
                                           I.n_prefill_segments, group_for(I.n_prefill_segments),
-                                          tiles, kmax, kPrefillSegRows, v, y, ldy, s);
+                                          kmax, kPrefillSegRows, v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (prefill) launch");
     }
     if (I.n_gather_segments > 0) {
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, true,
                                           I.n_decode_segments + I.n_prefill_segments,
                                           I.n_gather_segments, group_for(I.n_gather_segments),
-                                          tiles, kmax, std::max(1, r->max_gather_rows), v, y,
-                                          ldy, s);
+                                          kmax, std::max(1, r->max_gather_rows), v, y, ldy, s);
         if (e != hipSuccess) return hip_fail(e, "expand (gather) launch");
     }
     return LORA_OK;
@@ -693,7 +695,14 @@ int32_t lora_pool_load(lora_pool *p, int32_t adapter_id, int32_t slot, const voi
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const LaneGeom &g = p->geom;
+    // An id moving to another slot leaves its old slot empty: that slot's
+    // ranks go to zero on the device too (as lora_pool_unload does), so a
+    // routing built on the device treats it as holding no adapter.
+    const int32_t vacated =
+        (it != p->id_to_slot.end() && it->second != target) ? it->second : 0;
     hipError_t e = hipSuccess;
+    if (vacated) e = launch_set_meta(p->rank_tab, p->scale_tab, vacated, 0, nullptr, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "clearing the vacated slot's ranks");
     if (src_on_device) {
         for (int j = 0; j < d.n_slices && e == hipSuccess; ++j) {
             e = launch_pack_a(slot_a(p, target, j), static_cast<const uint16_t *>(A[j]), lda[j],
@@ -741,7 +750,13 @@ int32_t lora_pool_load(lora_pool *p, int32_t adapter_id, int32_t slot, const voi
         if (e != hipSuccess) return hip_fail(e, "copying adapter factors");
     }
     // bookkeeping: evict this id from an old slot, and the old occupant of target
-    if (it != p->id_to_slot.end() && it->second != target) p->slot_to_id[it->second] = 0;
+    if (vacated) {
+        p->slot_to_id[vacated] = 0;
+        for (int j = 0; j < kMetaStride; ++j) {
+            p->h_rank[(size_t)vacated * kMetaStride + j] = 0;
+            p->h_scale[(size_t)vacated * kMetaStride + j] = 0.f;
+        }
+    }
     if (int32_t old = p->slot_to_id[target]; old != 0 && old != adapter_id)
         p->id_to_slot.erase(old);
     p->id_to_slot[adapter_id] = target;
@@ -1243,6 +1258,21 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
 {
     if (int32_t rc = check_pair(p, r)) return rc;
     if (r->info.n_active == 0) return LORA_OK;
+    if (!workspace) return fail(LORA_ERR_ARG, "workspace is null");
+    return delta_apply_ws(p, r, x, ldx, y, ldy, workspace, workspace_bytes,
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace lora {
+
+int32_t delta_apply_ws(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
+                       float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                       hipStream_t st)
+{
+    if (int32_t rc = check_pair(p, r)) return rc;
+    if (r->info.n_active == 0) return LORA_OK;
     if (int32_t rc = check_x(p, x, ldx)) return rc;
     if (int32_t rc = check_y(p, y, ldy)) return rc;
     int64_t need = 0;
@@ -1252,20 +1282,15 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
     if (workspace_bytes < need)
         return fail(LORA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
                     (long long)workspace_bytes, (long long)need);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     float *v = static_cast<float *>(workspace);
     // Decode segments of small ranks: shrink and expand in one launch, with
     // the same arithmetic as the two kernels (bit-identical results).  Each
     // column tile of a slice recomputes the segment's v, re-reading the
     // slice's A; the one launch is taken while those extra bytes stay below
     // about a microsecond of HBM time, the cost of the launch it saves.
-    int hmax = 0;
     int64_t extra_tiles = 0;
-    for (int j = 0; j < p->desc.n_slices; ++j) {
-        hmax = std::max(hmax, p->desc.h_out[j]);
+    for (int j = 0; j < p->desc.n_slices; ++j)
         extra_tiles += (p->desc.h_out[j] + kExpandTile - 1) / kExpandTile - 1;
-    }
-    const int tiles = (hmax + kExpandTile - 1) / kExpandTile;
     const int kmax = batch_max_rank(p, r);
     const int64_t extra_bytes = extra_tiles * kmax * (int64_t)p->desc.h_in * 2 *
                                 r->info.n_decode_segments;
@@ -1276,7 +1301,7 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
     int32_t rc = LORA_OK;
     if (fused) {
         hipError_t e = launch_delta_gemv(p->geom, pool_dev(p), routing_dev(r),
-                                         r->info.n_decode_segments, tiles, x, ldx, y, ldy, cs.dec);
+                                         r->info.n_decode_segments, x, ldx, y, ldy, cs.dec);
         if (e != hipSuccess) rc = hip_fail(e, "delta (decode) launch");
     }
     if (rc == LORA_OK) rc = enqueue_shrink(p, r, x, ldx, v, cs, !fused);
@@ -1285,4 +1310,4 @@ int32_t lora_delta_apply(const lora_pool *p, const lora_routing *r, const void *
     return rc ? rc : rj;
 }
 
-}  // extern "C"
+}  // namespace lora

@@ -59,6 +59,15 @@ struct LaneGeom {
     int64_t bt_slice_off[LORA_MAX_SLICES];
 };
 
+// Column tiles of tile_cols columns: slice j has ceil(h_out[j] / tile_cols) of
+// them (slices past n_slices have width 0, so none), and the tiles of a
+// segment are numbered slice after slice.  Tiles of the lane per segment:
+__host__ __device__ inline int lane_tiles(const LaneGeom &g, int tile_cols)
+{
+    return (g.h_out[0] + tile_cols - 1) / tile_cols + (g.h_out[1] + tile_cols - 1) / tile_cols +
+           (g.h_out[2] + tile_cols - 1) / tile_cols + (g.h_out[3] + tile_cols - 1) / tile_cols;
+}
+
 // Device views of a pool.  Slot s >= 1 is stored at index s - 1; the
 // metadata tables have a row for slot 0 that stays zero.
 struct PoolDev {
@@ -96,8 +105,8 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
                               float *v, hipStream_t s);
 hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                             int n_seg, int tiles_per_slice, const void *x, int64_t ldx, float *y,
-                             int64_t ldy, hipStream_t s);
+                             int n_seg, const void *x, int64_t ldx, float *y, int64_t ldy,
+                             hipStream_t s);
 hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int rows_per_wave, int lane_cols, const float *v,
                               float *y, int64_t ldy, hipStream_t s);
@@ -105,9 +114,9 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
                               const void *x, int64_t ldx, float *v, hipStream_t s);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                              bool gather, int seg_begin, int n_seg, int group,
-                              int tiles_per_slice, int max_rank, int max_seg_rows,
-                              const float *v, float *y, int64_t ldy, hipStream_t s);
+                              bool gather, int seg_begin, int n_seg, int group, int max_rank,
+                              int max_seg_rows, const float *v, float *y, int64_t ldy,
+                              hipStream_t s);
 hipError_t launch_route_decode(const int32_t *tok_slot, int n_tok, const MoeDispatch *moe,
                                const int32_t *rank_tab, int max_slots, int max_dec,
                                int max_gather, int32_t *seg, int32_t *rows, int32_t *tok,
@@ -125,6 +134,21 @@ hipError_t launch_set_meta(int32_t *rank_tab, float *scale_tab, int slot, int n_
 hipError_t launch_clear_meta(int32_t *rank_tab, float *scale_tab, int n_rows,
                              hipStream_t s);
 
+// ---- host side shared between the ABI's source files ----
+// Record a thread-local error message and return `code`.
+int32_t fail(int32_t code, const char *fmt, ...);
+int32_t hip_fail(hipError_t e, const char *what);
+
+}  // namespace lora
+
+struct lora_pool;
+struct lora_routing;
+namespace lora {
+// lora_delta_apply after the handle check: validates x, y and the workspace
+// (v, workspace_bytes bytes at `workspace`) and enqueues the kernels.
+int32_t delta_apply_ws(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
+                       float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                       hipStream_t st);
 }  // namespace lora
 
 // ---- opaque handles ----

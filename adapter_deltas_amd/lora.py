@@ -153,9 +153,17 @@ def lora_routing_destroy(routing) -> None:
     _check(_lib().lora_routing_destroy(routing))
 
 
+def _seq_ids(seq_adapter_id) -> np.ndarray:
+    """int32 registry ids per sequence; a missing id (None) is the base model,
+    id 0 (tokenspeed PR #976, first commit message: the front end turns a
+    request without a LoRA id into id 0)."""
+    return np.ascontiguousarray([0 if a is None else a for a in seq_adapter_id],
+                                dtype=np.int32)
+
+
 def lora_build_routing(pool, seq_adapter_id, seq_len, max_loras, prefill_min_len,
                        routing, stream=None):
-    ids = np.ascontiguousarray(seq_adapter_id, dtype=np.int32)
+    ids = _seq_ids(seq_adapter_id)
     lens = np.ascontiguousarray(seq_len, dtype=np.int32)
     n = len(ids)
     if len(lens) != n:
@@ -185,7 +193,7 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
     seg (int32 [n_seg, 16]), rows (int32 [n_active]) and tok_slot (int32 [T]).
     """
     i32p = ctypes.POINTER(ctypes.c_int32)
-    ids = np.ascontiguousarray(seq_adapter_id, dtype=np.int32)
+    ids = _seq_ids(seq_adapter_id)
     lens = np.ascontiguousarray(seq_len, dtype=np.int32)
     rid = np.ascontiguousarray(list(resident.keys()), dtype=np.int32)
     rsl = np.ascontiguousarray(list(resident.values()), dtype=np.int32)
@@ -277,6 +285,20 @@ def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:
     """Pool slot of (adapter slot, expert) in an expert projection's pool
     (LORA_MOE_SLOT)."""
     return (adapter_slot - 1) * n_experts + expert + 1
+
+
+def moe_row_slots(tok_slot, row_token, row_expert, n_experts, row_edited=None):
+    """Pool slot of every dispatched row of a MoE layer, for
+    lora_build_routing_rows: moe_slot(adapter slot of the row's token, the
+    row's expert), or 0 for a row of a base token (slot 0) or a row whose
+    adapter does not edit its expert (row_edited False)."""
+    a = np.asarray(tok_slot, dtype=np.int64)[np.asarray(row_token, dtype=np.int64)]
+    e = np.asarray(row_expert, dtype=np.int64)
+    s = moe_slot(a, e, n_experts)
+    keep = a != 0
+    if row_edited is not None:
+        keep &= np.asarray(row_edited, dtype=bool)
+    return np.where(keep, s, 0).astype(np.int32)
 
 
 def lora_routing_device_counts(routing) -> int:
@@ -449,3 +471,4 @@ def delta_apply(pool: Pool, routing: Routing, x, y, workspace=None, stream=None)
     lora_delta_apply(pool.handle, routing.handle, x, x.stride(0), y, y.stride(0),
                      workspace, workspace.numel(), stream)
     return workspace
+

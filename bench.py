@@ -62,21 +62,41 @@ COPY_CALIBRATION_BYTES = 268435456
 
 
 def call_kernels(call: str, info) -> str:
-    """The kernels one lora_shrink / lora_expand call launches."""
+    """The kernels one lora_shrink / lora_expand / lora_delta_apply call
+    launches, by the kinds of segment in the batch."""
+    steps = ("shrink", "expand") if call == "delta_apply" else (call,)
     ks = []
-    if info["n_decode_segments"]:
-        ks.append(f"k_{call}_gemv")
-    if info["n_prefill_segments"] or info["n_gather_segments"]:
-        ks.append(f"k_{call}_mfma")
+    for st in steps:
+        if info["n_decode_segments"]:
+            ks.append(f"k_{st}_gemv")
+        if info["n_prefill_segments"] or info["n_gather_segments"]:
+            ks.append(f"k_{st}_mfma")
     return f"lora_{call}: " + " + ".join(ks)
 
 
+PMC_STEPS, PMC_WARMUP, PMC_LAYERS = 2, 1, 8
+PMC_RUN = (f"--steps {PMC_STEPS} --warmup {PMC_WARMUP} --layers {PMC_LAYERS} --only-apply")
+
+
+def kernel_step(name: str) -> str:
+    """Which step of the delta a library kernel belongs to, from its name
+    (k_shrink_*, k_expand_*, k_delta_* -- the last is both in one launch)."""
+    m = re.search(r"\bk_(shrink|expand|delta)_\w+", name)
+    return m.group(1) if m else ""
+
+
 def summarize_pmc(pmc_dir: str, configs):
-    """profiles/traffic.json from rocprofv3 --pmc runs: per workload and call,
-    the mean HBM bytes per launch, FETCH_SIZE and WRITE_SIZE each scaled by
-    what the same counter reads for a plain copy of COPY_CALIBRATION_BYTES."""
+    """profiles/traffic.json from rocprofv3 --pmc runs of `bench.py --config
+    <cfg> {PMC_RUN}`, whose only library work is lora_delta_apply on every lane
+    of every layer, (warmup + steps) x layers times per lane: per workload, the
+    mean HBM bytes per delta_apply call and per step of it (shrink kernels,
+    expand kernels), FETCH_SIZE and WRITE_SIZE each scaled by what the same
+    counter reads for a plain copy of COPY_CALIBRATION_BYTES."""
     import csv
     import statistics
+
+    from workloads import CONFIGS, MOE_CONFIGS
+    lanes_of = {c.name: len(c.lanes) for c in (*CONFIGS, *MOE_CONFIGS)}
 
     def per_kernel(run):
         out = {}
@@ -95,30 +115,22 @@ def summarize_pmc(pmc_dir: str, configs):
     for cfg in configs:
         fetch = per_kernel(f"{cfg}_fetch")
         write = per_kernel(f"{cfg}_write")
+        calls = (PMC_STEPS + PMC_WARMUP) * PMC_LAYERS * lanes_of[cfg]
         entry = {}
-        for call in ("shrink", "expand"):
-            names = [k for k in fetch if f"k_{call}_" in k]
+        for part, steps in (("delta_apply", ("shrink", "expand", "delta")),
+                            ("shrink", ("shrink",)), ("expand", ("expand",))):
+            names = [k for k in fetch if kernel_step(k) in steps]
             if not names:
                 continue
-            # A call launches one kernel per segment kind present (decode
-            # GEMV, prefill MFMA, gather MFMA), and lanes may use different
-            # template instances of them; the mean per call is the total over
-            # all dispatches divided by the number of calls, which is the
-            # dispatch count of any one kind.
-            def kind(k):
-                return "gemv" if "_gemv" in k else ("gather" if "true>" in k else "mfma")
-            counts = {}
-            for k in names:
-                counts[kind(k)] = counts.get(kind(k), 0) + len(fetch[k])
-            calls = max(counts.values())
             f_kib = sum(sum(fetch[k]) for k in names) / calls
             w_kib = sum(sum(write[k]) for k in names) / calls
-            entry[call] = {
+            entry[part] = {
                 "kernels": sorted({re.search(r"k_\w+", k).group(0) for k in names}),
-                "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib,
+                "calls": calls,
+                "fetch_kib_per_call": f_kib, "write_kib_per_call": w_kib,
                 "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-                "hbm_bytes_per_launch": int(f_kib * 1024 * fetch_scale +
-                                            w_kib * 1024 * write_scale),
+                "hbm_bytes_per_call": int(f_kib * 1024 * fetch_scale +
+                                          w_kib * 1024 * write_scale),
                 "sources_sha256": sources_digest(),
                 "commands": [
                     f"rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py "
@@ -126,11 +138,9 @@ def summarize_pmc(pmc_dir: str, configs):
                     f"rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py "
                     f"--copy-calibration {COPY_CALIBRATION_BYTES}",
                     f"rocprofv3 --pmc FETCH_SIZE --output-format csv -- python3 bench.py "
-                    f"--config {cfg} --steps 2 --warmup 1 --layers 8 --graph-reps 1 "
-                    f"--cpu-seconds 0.1",
+                    f"--config {cfg} {PMC_RUN}",
                     f"rocprofv3 --pmc WRITE_SIZE --output-format csv -- python3 bench.py "
-                    f"--config {cfg} --steps 2 --warmup 1 --layers 8 --graph-reps 1 "
-                    f"--cpu-seconds 0.1"],
+                    f"--config {cfg} {PMC_RUN}"],
             }
         doc[cfg] = entry
     with open(path, "w") as f:
@@ -168,7 +178,7 @@ def recorded_traffic(config: str, kernel: str):
         rec = json.load(f).get(config, {}).get(kernel)
     if not rec or rec.get("sources_sha256") != sources_digest():
         return None
-    return rec["hbm_bytes_per_launch"]
+    return rec.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(w, lanes, seconds, threads=1):
@@ -251,8 +261,7 @@ def main_moe(args, spec):
     import torch
     import adapter_deltas_amd as m
     from workloads import generate_moe
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import to_device_x, to_device_y, moe_row_slots
+    from workloads.device import to_device_x, to_device_y
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -296,7 +305,10 @@ def main_moe(args, spec):
     R = w.n_rows
     first = lanes[0]
     routing = m.Routing(R, R, device=dev)
-    row_slot = moe_row_slots(w, [aslot[int(a)] if a else 0 for a in w.tok_adapter])
+    edited = np.array([bool(a) and (int(a), int(e)) in w.factors
+                       for a, e in zip(w.tok_adapter[w.row_token], w.row_expert)], dtype=bool)
+    row_slot = m.moe_row_slots([aslot[int(a)] if a else 0 for a in w.tok_adapter],
+                               w.row_token, w.row_expert, E, edited)
     row_prefill = w.row_prefill.astype(np.uint8)
 
     def route(pool):
@@ -321,6 +333,13 @@ def main_moe(args, spec):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.only_apply:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"only_apply": spec.name, "calls_per_lane":
+                          (args.warmup + args.steps) * args.layers, "lanes": len(lanes)}))
+        return
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
@@ -384,11 +403,8 @@ def main_moe(args, spec):
         for k in ("shrink", "expand"):
             alg[k][0] += a[k][0] / len(lanes)
             alg[k][1] += a[k][1] / len(lanes)
-    dominant = "expand" if expand_us >= shrink_us else "shrink"
-    dom_us = expand_us if dominant == "expand" else shrink_us
-    dom_bytes = alg[dominant][0]
-    achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     total_bytes = alg["shrink"][0] + alg["expand"][0]
+    achieved_gbs = total_bytes / (apply_us * 1e-6) / 1e9
     info = routing.info()
 
     log(f"cpu baseline ~{args.cpu_seconds}s")
@@ -433,12 +449,14 @@ def main_moe(args, spec):
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
         "graph_step_ms": round(step_us * 1e-3, 4) if step_us is not None else None,
         "roofline": {
-            "kernel": call_kernels(dominant, info),
+            "kernel": call_kernels("delta_apply", info),
             "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(spec.name, dominant),
-            "algorithmic_bytes_per_launch": int(dom_bytes),
-            "us_per_launch": round(dom_us, 3),
+            "traffic": recorded_traffic(spec.name, "delta_apply"),
+            "algorithmic_bytes_per_launch": int(total_bytes),
+            "us_per_launch": round(apply_us, 3),
+            "note": "one lora_delta_apply call of one expert projection, its kernels "
+                    "back to back in a replayed graph, HIP events on the launching stream",
         },
         "per_lane_layer": {
             "delta_apply_us": round(apply_us, 3),
@@ -470,6 +488,9 @@ def main():
     ap.add_argument("--graph-reps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill-min-len", type=int, default=64)
+    ap.add_argument("--only-apply", action="store_true",
+                    help="only run the steps (routing + delta_apply per lane and layer), "
+                         "for counter passes: no graph timing, no CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 10 times (the "
                          "reference kernel that scales HBM byte counters)")
@@ -508,8 +529,7 @@ def main():
     import torch
     import adapter_deltas_amd as m
     from workloads import config_by_name, generate
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import to_device_x, to_device_y
+    from workloads.device import to_device_x, to_device_y
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -569,6 +589,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.only_apply:
+        # a counter pass: the library's only work is delta_apply on every lane
+        # of every layer, (warmup + steps) x layers times per lane
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"only_apply": spec.name, "calls_per_lane":
+                          (args.warmup + args.steps) * args.layers, "lanes": len(lanes)}))
+        return
 
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -622,6 +651,18 @@ def main():
         torch.cuda.synchronize()
         return g0.elapsed_time(g1) * 1e3 / args.graph_reps
 
+    # The host half of the step alone: admission, segments, pinned staging and
+    # the enqueue of the copy (the copy itself runs on the device).
+    log("host routing timing")
+    n_route = 200
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_route):
+        routing.build(layers[0][build_lane][0], w.seq_adapter, w.seq_len, spec.max_loras,
+                      args.prefill_min_len)
+    route_host_us = (time.perf_counter() - t0) * 1e6 / n_route
+    torch.cuda.synchronize()
+
     log("graph replay timing")
     per_apply_us = graph_us(lambda ln, pool, x, y: m.delta_apply(pool, routing, x, y, ws[ln]))
     shrink_us = graph_us(lambda ln, pool, x, y: m.shrink(pool, routing, x, vbuf[ln]))
@@ -663,16 +704,16 @@ def main():
         for k in ("shrink", "expand"):
             alg[k][0] += a[k][0] / len(lanes)
             alg[k][1] += a[k][1] / len(lanes)
-    dominant = "expand" if expand_us >= shrink_us else "shrink"
-    dom_us = expand_us if dominant == "expand" else shrink_us
-    dom_bytes = alg[dominant][0]
-    achieved_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
     total_bytes = alg["shrink"][0] + alg["expand"][0]
-    traffic = recorded_traffic(spec.name, dominant)
+    # The headline is the whole delta of a lane: lora_delta_apply (shrink and
+    # expand) priced with all its algorithmic bytes over the time per call.
+    achieved_gbs = total_bytes / (per_apply_us * 1e-6) / 1e9
+    traffic = recorded_traffic(spec.name, "delta_apply")
 
     log(f"cpu baseline ~{args.cpu_seconds}s")
     cpu_rate, cpu_dt, cpu_reps = cpu_baseline(w, lanes, args.cpu_seconds)
-    n_thr = max(1, min(16, os.cpu_count() or 1))
+    host_cpus = os.cpu_count() or 1
+    n_thr = max(1, min(16, host_cpus))
     log(f"cpu baseline on {n_thr} threads ~{args.cpu_seconds / 2}s")
     par_rate, par_dt, par_reps = cpu_baseline(w, lanes, args.cpu_seconds / 2, n_thr)
     log("stream copy context")
@@ -703,13 +744,29 @@ def main():
             "step": "routing build + delta_apply on every lane of every layer",
         },
         "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+        "routing_host_us": round(route_host_us, 2),
         "roofline": {
-            "kernel": call_kernels(dominant, info),
+            "kernel": call_kernels("delta_apply", info),
             "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(dom_bytes),
-            "us_per_launch": round(dom_us, 3),
+            "algorithmic_bytes_per_launch": int(total_bytes),
+            "us_per_launch": round(per_apply_us, 3),
+            "note": "one lora_delta_apply call of one lane: its kernels back to back "
+                    "in a replayed graph of every layer's call, HIP events on the "
+                    "launching stream",
+        },
+        "per_launch": {
+            "shrink": {"kernel": call_kernels("shrink", info), "us": round(shrink_us, 3),
+                       "algorithmic_bytes": int(alg["shrink"][0]),
+                       "frac": round(alg["shrink"][0] / (shrink_us * 1e-6) / 1e9 /
+                                     HBM_PEAK_GBS, 4),
+                       "traffic": recorded_traffic(spec.name, "shrink")},
+            "expand": {"kernel": call_kernels("expand", info), "us": round(expand_us, 3),
+                       "algorithmic_bytes": int(alg["expand"][0]),
+                       "frac": round(alg["expand"][0] / (expand_us * 1e-6) / 1e9 /
+                                     HBM_PEAK_GBS, 4),
+                       "traffic": recorded_traffic(spec.name, "expand")},
         },
         "per_lane_layer": {
             "delta_apply_us": round(per_apply_us, 3),
@@ -722,16 +779,17 @@ def main():
         },
         "cpu_baseline": {
             "value": round(cpu_rate, 1), "unit": "delta tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": host_cpus,
             "sample": f"fp64 C oracle over the whole {spec.name} batch "
                       f"({info['n_active']} active rows x {len(lanes)} lanes), "
-                      f"{cpu_reps} repetitions in {cpu_dt:.1f} s",
+                      f"{cpu_reps} repetitions in {cpu_dt:.1f} s, one thread",
         },
         "cpu_baseline_threads": {
             "value": round(par_rate, 1), "unit": "delta tokens/s", "cores": n_thr,
-            "kind": "oracle",
-            "sample": f"the same oracle on row chunks of the batch over {n_thr} threads, "
-                      f"{par_reps} repetitions in {par_dt:.1f} s",
+            "kind": "oracle", "host_cpus": host_cpus,
+            "sample": f"the same oracle on row chunks of the batch over {n_thr} threads "
+                      f"(the host reports {host_cpus} CPUs; at most 16 are used, the "
+                      f"CPU share of one GPU), {par_reps} repetitions in {par_dt:.1f} s",
         },
         "device_routing": device_routing,
         "context": {

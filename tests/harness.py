@@ -12,6 +12,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from workloads.device import to_device_x, to_device_y  # noqa: F401  (re-exported)
+
 REL_TOL = 1e-2
 NORM_ABS_TOL = 2e-3
 
@@ -77,16 +79,6 @@ def load_lane_pool(Pool, workload, lane_name, max_slots=None, max_rank=None,
     return pool
 
 
-def to_device_x(x_bits, device="cuda"):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(device)
-
-
-def to_device_y(y, device="cuda"):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(device)
-
-
 def load_moe_pool(Pool, workload, lane_name, adapter_slot=None, device="cuda"):
     """Pool of one expert projection of a MoE workload: the pair of (adapter,
     expert) in slot moe_slot(adapter slot, expert, n_experts).
@@ -116,12 +108,58 @@ def moe_row_slots(workload, tok_slot):
     """Pool slot of every dispatched row of a MoE workload (0 for rows of base
     tokens and of experts the token's adapter does not edit), for
     lora_build_routing_rows."""
-    from adapter_deltas_amd import moe_slot
-    E = workload.spec.n_experts
+    from adapter_deltas_amd import moe_row_slots as slots
+    return slots(tok_slot, workload.row_token, workload.row_expert, workload.spec.n_experts,
+                 moe_rows_edited(workload))
+
+
+def moe_rows_edited(workload):
+    """Whether each dispatched row's token runs an adapter that edits the row's
+    expert (has factors for it)."""
     ids = workload.tok_adapter[workload.row_token]
-    out = np.zeros(workload.n_rows, dtype=np.int32)
-    for p in range(workload.n_rows):
-        a = int(tok_slot[workload.row_token[p]])
-        if a and (int(ids[p]), int(workload.row_expert[p])) in workload.factors:
-            out[p] = moe_slot(a, int(workload.row_expert[p]), E)
-    return out
+    return np.array([bool(a) and (int(a), int(e)) in workload.factors
+                     for a, e in zip(ids, workload.row_expert)], dtype=bool)
+
+
+def oracle_row_chunks(workload, lane_name, rows, chunk=256, threads=None):
+    """Yields (row indices, oracle delta float64 [len, H_out]) over `rows` in
+    chunks, the chunks computed by the fp64 oracle on host threads (its C loop
+    runs without the interpreter lock), in order."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    rows = np.asarray(rows, dtype=np.int64)
+    parts = [rows[i:i + chunk] for i in range(0, len(rows), chunk)]
+    n = threads or max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        futs = [ex.submit(lambda r: oracle.workload_lane_delta(workload, lane_name, rows=r)[0], r)
+                for r in parts]
+        for r, f in zip(parts, futs):
+            yield r, f.result()
+
+
+def check_rows_against_oracle(workload, lane_name, tok_adapter, x_bits, y0, y):
+    """Rows of a batch given per row as registry ids (0 = base): base rows keep
+    the bits of y0, the others hold y0 + delta, exactly for integer inputs and
+    within the tolerance rule otherwise.  x_bits, y0 and y are the batch's own
+    rows (host arrays)."""
+    import oracle
+    L = workload.lanes[lane_name]
+    tok = np.asarray(tok_adapter, dtype=np.int64)
+    factors = {aid: [(s.A, s.B, s.rank, s.scale) for s in ad.lanes[lane_name]]
+               for aid, ad in workload.adapters.items()}
+    off = tok == 0
+    y = np.asarray(y)
+    assert np.array_equal(y[off].view(np.uint32), np.asarray(y0)[off].view(np.uint32))
+    act = np.nonzero(~off)[0]
+    if len(act) == 0:
+        return
+    d = oracle.lane_delta(x_bits, L.spec.x_dtype, tok, factors, L.spec.h_out, L.spec.a_col0,
+                          L.spec.h_in, rows=act)
+    if workload.mode == "int":
+        assert np.array_equal(y[act].astype(np.float64),
+                              np.asarray(y0)[act].astype(np.float64) + d)
+    else:
+        st = compare(y, y0, d, L.spec.h_out, rows=act)
+        assert st["ok"], st

@@ -95,6 +95,45 @@ def test_moe_slot_layout(m):
     assert m.moe_slot(1, 0, E) == 1 and m.moe_slot(A, E - 1, E) == A * E
 
 
+def test_moe_slot_matches_the_header_macro(m, tmp_path):
+    """moe_slot and moe_row_slots of the binding give what LORA_MOE_SLOT in
+    include/lora.h gives, for several expert counts (a C program built with
+    gcc from the header prints the macro's values)."""
+    import subprocess
+    cases = [(a, e, n) for n in (1, 3, 8, 128) for a in (1, 2, 5) for e in range(min(n, 4))]
+    prog = tmp_path / "moe_slot.c"
+    body = "".join(f'    printf("%d\\n", LORA_MOE_SLOT({a}, {e}, {n}));\n' for a, e, n in cases)
+    prog.write_text('#include <stdio.h>\n#include "lora.h"\nint main(void)\n{\n' + body +
+                    "    return 0;\n}\n")
+    exe = tmp_path / "moe_slot"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)],
+                   check=True)
+    want = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert [m.moe_slot(a, e, n) for a, e, n in cases] == want
+    # the per-row form: base tokens and unedited experts give 0
+    tok_slot = np.array([0, 2, 5], np.int32)
+    row_token = np.array([1, 0, 2, 1, 2], np.int32)
+    row_expert = np.array([3, 1, 0, 7, 2], np.int32)
+    edited = np.array([True, True, True, False, True])
+    got = m.moe_row_slots(tok_slot, row_token, row_expert, 8, edited)
+    assert got.tolist() == [m.moe_slot(2, 3, 8), 0, m.moe_slot(5, 0, 8), 0, m.moe_slot(5, 2, 8)]
+
+
+def test_missing_id_is_the_base_model(m):
+    """A sequence whose adapter id is None runs the base model, as id 0 does
+    (tokenspeed PR #976, first commit message): the same plan, and it never
+    counts against max_loras."""
+    resident = {5: 1, 6: 2}
+    a = m.lora_plan_routing([5, None, 6, None], [1, 3, 2, 1], 1, 64, resident, 4, 16)
+    b = m.lora_plan_routing([5, 0, 6, 0], [1, 3, 2, 1], 1, 64, resident, 4, 16)
+    for k in ("seg", "rows", "tok_slot", "admitted"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["info"] == b["info"]
+    assert list(a["admitted"]) == [True, True, False, True]
+    assert a["tok_slot"].tolist() == [1, 0, 0, 0, 0, 0, 0]
+
+
 def test_pool_bytes_layout(m):
     # A + B^T + B + two metadata tables, each 256-byte aligned
     d = m.make_desc(4096, [4096, 1024, 1024], 8, 16)

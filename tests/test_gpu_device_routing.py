@@ -1,12 +1,13 @@
 """Routing of decode batches built on the device (lora_build_routing_device):
-the delta is bit-identical to the one a host-built routing gives, rows whose
-slot holds no adapter are counted and left untouched, and one captured graph
-of the routing and the delta serves any mix of adapters."""
+the delta matches the fp64 oracle and is bit-identical to the one a host-built
+routing gives, rows whose slot holds no adapter are counted and left
+untouched, and one captured graph of the routing and the delta serves any mix
+of adapters."""
 import numpy as np
 import pytest
 
 from workloads import LaneSpec, WorkloadSpec, config_by_name, generate
-from harness import load_lane_pool, to_device_x, to_device_y
+from harness import check_rows_against_oracle, load_lane_pool, to_device_x, to_device_y
 
 pytestmark = pytest.mark.gpu
 
@@ -71,17 +72,21 @@ def lane_setup(lib, w, lane):
     return pool, to_device_x(L.x), to_device_y(L.y0)
 
 
+@pytest.mark.parametrize("mode", ["real", "int"])
 @pytest.mark.parametrize("cfg,lane,path", [("decode_mix", "qkv", "apply"),
                                            ("decode_mix", "qkv", "split"),
                                            ("device_mix", "qkv_like", "apply"),
                                            ("device_mix", "qkv_like", "split"),
                                            ("device_mix", "fp16_share", "apply")])
-def test_device_routing_matches_host(lib, cfg, lane, path):
-    w = generate(DEVICE_MIX) if cfg == "device_mix" else generate(config_by_name(cfg))
+def test_device_routing_matches_host(lib, cfg, lane, path, mode):
+    spec = DEVICE_MIX if cfg == "device_mix" else config_by_name(cfg)
+    w = generate(spec, mode=mode)
     pool, x, y0 = lane_setup(lib, w, lane)
     ids = np.repeat(w.seq_adapter, w.seq_len)
     yh, rh = host_apply(lib, pool, x, y0, ids)
     yd, rd = device_apply(lib, pool, x, y0, slots_of(pool, ids), path)
+    L = w.lanes[lane]
+    check_rows_against_oracle(w, lane, ids, L.x, L.y0, yd.cpu().numpy())
     assert np.array_equal(bits(yd), bits(yh))
     c = rd.device_counts().cpu().numpy()
     hi, di = rh.info(), rd.info()
@@ -115,6 +120,8 @@ def test_device_routing_sizes(lib, n):
     if n == 0:
         assert np.array_equal(bits(yd), bits(y0))
         return
+    check_rows_against_oracle(w, "qkv_like", ids, x.cpu().numpy().view(np.uint16),
+                              y0.cpu().numpy(), yd.cpu().numpy())
     yh, _ = host_apply(lib, pool, x, y0, ids)
     assert np.array_equal(bits(yd), bits(yh))
 
@@ -213,6 +220,8 @@ def test_device_routing_graph_serves_any_mixture(lib):
         y.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
+        L = w.lanes["qkv_like"]
+        check_rows_against_oracle(w, "qkv_like", ids, L.x, L.y0, y.cpu().numpy())
         yh, _ = host_apply(lib, pool, x, y0, ids)
         assert np.array_equal(bits(y), bits(yh)), i
 
@@ -236,3 +245,40 @@ def test_device_routing_padded_rows_copy_their_original(lib):
     yb = bits(yd)
     assert np.array_equal(yb[:n], bits(yh))
     assert np.array_equal(yb[n:], yb[src])
+
+
+def test_relocated_adapter_leaves_its_old_slot_empty(lib):
+    """Loading a resident id into another slot moves it: the old slot holds no
+    adapter for the device routing (rows naming it are counted invalid and
+    left untouched) nor for a plan from per-row slots (an error), and rows
+    naming the new slot get the adapter's exact bits."""
+    import torch
+    w = generate(DEVICE_MIX)
+    lane = "qkv_like"
+    L = w.lanes[lane]
+    pool = load_lane_pool(lib.Pool, w, lane, max_slots=8)   # slots 7 and 8 free
+    x, y0 = to_device_x(L.x), to_device_y(L.y0)
+    ids = np.repeat(w.seq_adapter, w.seq_len)
+    yh, _ = host_apply(lib, pool, x, y0, ids)
+    moved = int(w.adapter_ids[1])
+    s_old = pool.slot_of(moved)
+    before = slots_of(pool, ids)
+    ad = w.adapters[moved].lanes[lane]
+    pool.load(moved, [s.A for s in ad], [s.B for s in ad], [s.rank for s in ad],
+              [s.scale for s in ad], a_col0=L.spec.a_col0, slot=8)
+    assert pool.slot_of(moved) == 8
+    hit = before == s_old
+    assert hit.any()
+    # the old slot number, as a stale caller might still write it
+    yd, rd = device_apply(lib, pool, x, y0, before)
+    assert rd.device_counts().cpu().numpy()[4] == int(hit.sum())
+    assert np.array_equal(bits(yd)[hit], bits(y0)[hit])
+    assert np.array_equal(bits(yd)[~hit], bits(yh)[~hit])
+    r = lib.Routing(len(before), len(before))
+    with pytest.raises(lib.LoraError) as e:
+        r.build_rows(pool, before)
+    assert e.value.status == "LORA_ERR_SLOT"
+    # the new slot gives the adapter's bits
+    yd2, _ = device_apply(lib, pool, x, y0, slots_of(pool, ids))
+    assert np.array_equal(bits(yd2), bits(yh))
+    check_rows_against_oracle(w, lane, ids, L.x, L.y0, yd2.cpu().numpy())

@@ -10,7 +10,8 @@ import pytest
 import oracle
 from workloads import (LaneSpec, WorkloadSpec, config_by_name, generate)
 
-from harness import compare, load_lane_pool, seq_starts, to_device_x, to_device_y
+from harness import (compare, load_lane_pool, oracle_row_chunks, seq_starts, to_device_x,
+                     to_device_y)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,7 +191,57 @@ def test_gated_q_lane_full_parity(lib, mode, path):
     check_full(w, "qkv_gate", y, adm)
 
 
-# ------------------------------------------- full-size configs, sampled rows
+# ------------------------------------------- ranks the ABI accepts, all paths
+
+# Decode rows of ranks 65..127 on the GEMV path (shrink tasks of rank blocks
+# 9..16, the expand's rank loop past 64) next to ranks 8 and 64 in one batch,
+# so some rank-block tasks of the launch end early.
+HIGH_RANK_GEMV = WorkloadSpec(
+    name="high_rank_gemv", seed=25,
+    lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
+           LaneSpec("fp16_share", 4616, (264,), "fp16", tp_size=2, tp_rank=1)),
+    n_adapters=5, ranks=(65, 100, 127, 8, 64), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=127,
+    decode_rows=120, base_prob=0.2, prefill_seqs=0, prefill_len=(1, 1))
+
+# Ranks up to LORA_MAX_RANK on the matrix cores: prefill segments and gather
+# rows of ranks 192 and 256 (the 8-step MFMA expand tile with data in every
+# step), rank 130, and a rank-8 adapter whose decode rows take the GEMV path.
+HIGH_RANK_MFMA = WorkloadSpec(
+    name="high_rank_mfma", seed=26,
+    lanes=(LaneSpec("qkv_like", 1544, (520, 136, 8)),
+           LaneSpec("fp16_share", 4616, (264,), "fp16", tp_size=2, tp_rank=1)),
+    n_adapters=4, ranks=(192, 256, 130, 8), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=256,
+    decode_rows=100, base_prob=0.2, prefill_seqs=5, prefill_len=(1, 200))
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("path", ["apply", "split"])
+@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
+def test_gemv_ranks_65_to_127(lib, lane, path, mode):
+    w = generate(HIGH_RANK_GEMV, mode=mode)
+    y, adm, info = run_lane(lib, w, lane, path=path)
+    assert info["n_decode_segments"] > 0
+    assert info["n_prefill_segments"] == 0 and info["n_gather_segments"] == 0
+    check_full(w, lane, y, adm)
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("path", ["apply", "split"])
+@pytest.mark.parametrize("lane", ["qkv_like", "fp16_share"])
+@pytest.mark.parametrize("prefill_min_len", [64, 1])
+def test_matrix_core_ranks_to_256(lib, lane, path, mode, prefill_min_len):
+    w = generate(HIGH_RANK_MFMA, mode=mode)
+    y, adm, info = run_lane(lib, w, lane, path=path, prefill_min_len=prefill_min_len)
+    assert info["n_prefill_segments"] > 0
+    if prefill_min_len == 64:
+        # decode rows of ranks 130, 192 and 256 gathered, rank 8 on the GEMV path
+        assert info["n_gather_segments"] > 0 and info["n_decode_segments"] > 0
+    check_full(w, lane, y, adm, prefill_min_len=prefill_min_len)
+
+
+# ------------------------------------------------- full-size configs, every row
 
 @pytest.mark.slow
 @pytest.mark.parametrize("mode", ["real", "int"])
@@ -198,7 +249,10 @@ def test_gated_q_lane_full_parity(lib, mode, path):
                                       ("many_tenants", "down_proj"),
                                       ("many_tenants", "o_proj"),
                                       ("tp_share", "attn_out"), ("tp_share", "shexp_w2")])
-def test_full_size_sampled(lib, cfg, lane, mode):
+def test_full_size_every_row(lib, cfg, lane, mode):
+    """Full-size workloads in the launch configuration the benchmark times:
+    every active row against the oracle (computed on host threads in row
+    chunks), every other row bit-identical to y0."""
     w = generate(config_by_name(cfg), mode=mode, lanes=(lane,))
     y, adm, info = run_lane(lib, w, lane)
     L = w.lanes[lane]
@@ -207,14 +261,13 @@ def test_full_size_sampled(lib, cfg, lane, mode):
     off = tok == 0
     assert np.array_equal(y[off].view(np.uint32), L.y0[off].view(np.uint32))
     act = np.nonzero(~off)[0]
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([act[:3], act[-3:], rng.choice(act, 40, replace=False)]))
-    d_ref, _, _ = oracle.workload_lane_delta(w, lane, rows=rows)
-    if mode == "int":
-        assert np.array_equal(y[rows].astype(np.float64), L.y0[rows].astype(np.float64) + d_ref)
-    else:
-        st = compare(y, L.y0, d_ref, L.spec.h_out, rows=rows)
-        assert st["ok"], st
+    for rows, d_ref in oracle_row_chunks(w, lane, act):
+        if mode == "int":
+            assert np.array_equal(y[rows].astype(np.float64),
+                                  L.y0[rows].astype(np.float64) + d_ref)
+        else:
+            st = compare(y, L.y0, d_ref, L.spec.h_out, rows=rows)
+            assert st["ok"], st
 
 
 # ---------------------------------------------------------------- invariants
