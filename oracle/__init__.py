@@ -27,6 +27,14 @@ What it follows:
     runs the base model, or whose adapter does not edit that expert, gets no
     delta.
 
+  * the base projection with the delta in its partial sum -- TensorFold PR
+    #47, third commit message and PR body "What this changes": the delta is
+    added in fp32 to the partial sum the base projection produces, before the
+    cross-rank reduction.  The reading taken: the projection's output is
+    y = x W^T + delta, with W the linear layer's bf16 weight in its usual
+    [out_features, in_features] orientation (this GPU's input columns for a
+    row-parallel share), and a base-model row gets x W^T alone.
+
   * A folded onto a transformed input -- TensorFold PR #47, first and third
     commit messages: the packed shared expert's down projection reads a
     rotated, scaled fp16 hidden state x' = M x, and its adapter's A is
@@ -79,6 +87,8 @@ def _load():
         lib.oracle_slice_delta.argtypes = [
             I, P, I, P, I, ctypes.c_int32, I, P, I, I, I, P, I,
             ctypes.c_double, P, I, I]
+        lib.oracle_linear_rows.restype = ctypes.c_int
+        lib.oracle_linear_rows.argtypes = [I, P, I, P, I, ctypes.c_int32, I, P, I, P, I]
         _lib = lib
     return _lib
 
@@ -229,6 +239,48 @@ def moe_lane_delta(workload, lane_name, rows=None):
     d = lane_delta(lane.x, lane.spec.x_dtype, row_key, factors, lane.spec.h_out,
                    lane.spec.a_col0, lane.spec.h_in, rows)
     return d, row_pair
+
+
+def base_product(x_bits, x_dtype, W_bits, h_in, rows=None):
+    """fp64 base projection x W^T of the given rows (default: all rows of x).
+
+    x_bits [T, >= h_in] (bf16 or fp16 bits), W_bits [h_out, >= h_in] bf16
+    bits.  Returns float64 [len(rows), h_out]."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    if rows is None:
+        rows = np.arange(x_bits.shape[0], dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    h_out = W_bits.shape[0]
+    out = np.zeros((len(rows), h_out), dtype=np.float64)
+    if len(rows) == 0 or h_out == 0:
+        return out
+    assert W_bits.shape[1] >= h_in and x_bits.shape[1] >= h_in
+    rc = lib.oracle_linear_rows(len(rows), rows.ctypes.data, h_in, x_bits.ctypes.data,
+                                x_bits.shape[1], X_KIND[x_dtype], h_out, W_bits.ctypes.data,
+                                W_bits.shape[1], out.ctypes.data, h_out)
+    if rc != 0:
+        raise MemoryError("oracle_linear_rows")
+    return out
+
+
+def linear_lane(x_bits, x_dtype, W_bits, tok_adapter, factors, h_out, a_col0, h_in,
+                rows=None):
+    """fp64 output of a lane's projection with the delta in its partial sum:
+    x W^T for every row, plus the delta for rows with an adapter (lane_delta's
+    arguments).  Returns float64 [len(rows), sum(h_out)]."""
+    base = base_product(x_bits, x_dtype, W_bits, h_in, rows)
+    return base + lane_delta(x_bits, x_dtype, tok_adapter, factors, h_out, a_col0, h_in, rows)
+
+
+def workload_linear_lane(workload, lane_name, W_bits, max_loras=None, rows=None):
+    """Routing, base projection and delta for one lane of a generated
+    workload.  Returns (y float64 [n_rows, H_out], tok_adapter, admitted)."""
+    d, tok, admitted = workload_lane_delta(workload, lane_name, max_loras, rows)
+    lane = workload.lanes[lane_name]
+    base = base_product(lane.x, lane.spec.x_dtype, W_bits, lane.spec.h_in, rows)
+    return base + d, tok, admitted
 
 
 def bf16_nearest_bits(v):

@@ -105,3 +105,42 @@ int oracle_slice_delta(int64_t n_rows, const int64_t *rows,
     free(xr);
     return 0;
 }
+
+/*
+ * The base projection of a lane for a list of rows: out[p][o] =
+ * sum_i W[o][i] x[rows[p]][i], i ascending, in binary64 from exact decodes.
+ * This is the fp32 partial sum that the delta above is added to (TensorFold
+ * PR #47, third commit message and PR body "What this changes": the delta
+ * lands in the projection's partial sum before the cross-rank reduction).  W
+ * is the linear layer's weight in its usual [out_features, in_features]
+ * orientation, bf16; under tensor parallelism a row-parallel layer's GPU
+ * holds the columns of its input share, which is what W holds here.
+ *
+ *   x    [*, ldx] bits, x_kind 1 = bf16, 2 = fp16; row t holds h_in features
+ *   W    [h_out, ldw] bf16 bits, columns [0, h_in)
+ *   out  [n_rows, ldo] binary64, columns [0, h_out)
+ *
+ * Returns 0, or -1 when scratch memory cannot be had.
+ */
+int oracle_linear_rows(int64_t n_rows, const int64_t *rows, int64_t h_in, const uint16_t *x,
+                       int64_t ldx, int32_t x_kind, int64_t h_out, const uint16_t *W,
+                       int64_t ldw, double *out, int64_t ldo)
+{
+    double *xr = (double *)malloc((size_t)(h_in > 0 ? h_in : 1) * sizeof(double));
+    if (!xr) return -1;
+    for (int64_t p = 0; p < n_rows; ++p) {
+        const uint16_t *xt = x + rows[p] * ldx;
+        for (int64_t i = 0; i < h_in; ++i)
+            xr[i] = decode(xt[i], x_kind);
+        double *op = out + p * ldo;
+        for (int64_t o = 0; o < h_out; ++o) {
+            const uint16_t *wo = W + o * ldw;
+            double s = 0.0;
+            for (int64_t i = 0; i < h_in; ++i)
+                s += oracle_bf16_value(wo[i]) * xr[i];
+            op[o] = s;
+        }
+    }
+    free(xr);
+    return 0;
+}

@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 from workloads import (CONFIGS, WorkloadSpec, LaneSpec, generate, config_by_name,
-                       f32_to_bf16_bits, bf16_bits_to_f32, MoeSpec, generate_moe)
+                       f32_to_bf16_bits, bf16_bits_to_f32, MoeSpec, generate_moe,
+                       draw_base_weight)
 from workloads.gen import f32_to_fp16_bits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -367,3 +368,103 @@ def test_fold_reads_the_transformed_input():
 def test_draw_fold_is_an_inverse():
     M, fold = draw_fold(7, 256)
     assert np.allclose(M @ fold.astype(np.float64), np.eye(256), atol=1e-6)
+
+
+# ------------------------------------------- base projection + delta (fused)
+
+def test_linear_worked_examples():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        cases = json.load(f)["linear_cases"]
+    for c in cases:
+        x = _bits([c["x"], c["x"]])                 # row 0 runs the adapter, row 1 base
+        W = _bits(c["W"])
+        A, B = _bits(c["A"]), _bits(c["B"])
+        h_in = x.shape[1]
+        f = {5: [(A, B, A.shape[0], c["scale"])]}
+        y = oracle.linear_lane(x, "bf16", W, [5, 0], f, [B.shape[0]], c.get("a_col0", 0), h_in)
+        assert y.tolist() == [c["y_adapter"], c["y_base"]], c["name"]
+
+
+def _decoded(bits, dtype="bf16"):
+    return (bits.view(np.float16).astype(np.float64) if dtype == "fp16"
+            else bf16_bits_to_f32(bits).astype(np.float64))
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "fp16"])
+def test_linear_merged_weight_identity(x_dtype):
+    """One adapter on every row: x W^T + scale B (A x) equals x (W + scale B A)^T
+    with the merged [h_out, h_in] weight formed by numpy's fp64 matmul (the
+    usual LoRA merge); base rows equal x W^T from numpy's matmul."""
+    w = _single_adapter_lane(15, 96, [40, 24], 7, 13, x_dtype)
+    lane = w.lanes["l"]
+    W = draw_base_weight(w.spec, 0, lane.spec)
+    y, tok, _ = oracle.workload_linear_lane(w, "l", W)
+    xf = _decoded(lane.x, x_dtype)
+    (aid, ad), = w.adapters.items()
+    merged = []
+    for sf in ad.lanes["l"]:
+        M = np.matmul(bf16_bits_to_f32(sf.B).astype(np.float64),
+                      bf16_bits_to_f32(sf.A).astype(np.float64))
+        merged.append(np.float64(sf.scale) * M)
+    Wm = _decoded(W) + np.concatenate(merged, axis=0)
+    ref = np.matmul(xf, Wm.T)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+    base = oracle.base_product(lane.x, x_dtype, W, 96)
+    ref_b = np.matmul(xf, _decoded(W).T)
+    assert np.abs(base - ref_b).max() <= 1e-12 * np.abs(ref_b).max()
+
+
+def test_linear_integer_brute_force_and_base_rows():
+    """Integer inputs: every row against exact integer sums written out; rows
+    of the base model get the base product alone, bit for bit."""
+    spec = WorkloadSpec(
+        name="lin_int", seed=16, lanes=(LaneSpec("l", 40, (9, 5)),), n_adapters=2,
+        ranks=(3, 6), rank_mode="list", scale_mode="fixed", scale=2.0, max_rank=6,
+        decode_rows=12, base_prob=0.3)
+    w = generate(spec, mode="int")
+    lane = w.lanes["l"]
+    W = draw_base_weight(spec, 0, lane.spec, mode="int")
+    y, tok, _ = oracle.workload_linear_lane(w, "l", W)
+    x = bf16_bits_to_f32(lane.x).astype(np.int64).tolist()
+    Wi = bf16_bits_to_f32(W).astype(np.int64).tolist()
+    for t in range(len(x)):
+        base = [sum(Wi[o][i] * x[t][i] for i in range(40)) for o in range(14)]
+        want = list(base)
+        if tok[t]:
+            col = 0
+            for sf in w.adapters[int(tok[t])].lanes["l"]:
+                A = bf16_bits_to_f32(sf.A).astype(np.int64).tolist()
+                B = bf16_bits_to_f32(sf.B).astype(np.int64).tolist()
+                u = [sum(A[k][i] * x[t][i] for i in range(40)) for k in range(sf.rank)]
+                for o in range(len(B)):
+                    want[col + o] += sf.scale * sum(B[o][k] * u[k] for k in range(sf.rank))
+                col += len(B)
+        assert y[t].tolist() == want, t
+    assert (tok == 0).any() and (tok != 0).any()
+    base = oracle.base_product(lane.x, "bf16", W, 40)
+    off = tok == 0
+    assert np.array_equal(y[off].view(np.uint64), base[off].view(np.uint64))
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+def test_linear_column_shares_sum_to_unsharded(mode):
+    """A row-parallel layer cut in 8 input-column shares (W and A cut by
+    columns, B whole): the shares' outputs sum to the unsharded output, the
+    sum the cross-rank reduction forms."""
+    tp, hs = 8, 24
+    w = _single_adapter_lane(17, tp * hs, [33], 5, 7, mode=mode)
+    lane = w.lanes["l"]
+    W = draw_base_weight(w.spec, 0, lane.spec, mode=mode)
+    (aid, ad), = w.adapters.items()
+    f = {aid: [(sf.A, sf.B, sf.rank, sf.scale) for sf in ad.lanes["l"]]}
+    tok = np.full(7, aid)
+    full = oracle.linear_lane(lane.x, "bf16", W, tok, f, [33], 0, tp * hs)
+    parts = np.zeros_like(full)
+    for r in range(tp):
+        xs = np.ascontiguousarray(lane.x[:, r * hs:(r + 1) * hs])
+        Ws = np.ascontiguousarray(W[:, r * hs:(r + 1) * hs])
+        parts += oracle.linear_lane(xs, "bf16", Ws, tok, f, [33], r * hs, hs)
+    if mode == "int":
+        assert np.array_equal(parts, full)
+    else:
+        assert np.abs(parts - full).max() <= 1e-12 * np.abs(full).max()

@@ -8,7 +8,7 @@ the fp64 oracle and the HIP path can take their inputs from it.
 from .configs import CONFIGS, config_by_name, LaneSpec, WorkloadSpec
 from .gen import (
     Workload, Lane, SliceFactors, Adapter,
-    generate, f32_to_bf16_bits, bf16_bits_to_f32, hadamard, draw_fold,
+    generate, f32_to_bf16_bits, bf16_bits_to_f32, hadamard, draw_fold, draw_base_weight,
 )
 from .moe import MoeSpec, MoeWorkload, generate_moe, MOE_CONFIGS, moe_config_by_name
 
@@ -16,5 +16,6 @@ __all__ = [
     "CONFIGS", "config_by_name", "LaneSpec", "WorkloadSpec",
     "Workload", "Lane", "SliceFactors", "Adapter",
     "generate", "f32_to_bf16_bits", "bf16_bits_to_f32", "hadamard", "draw_fold",
+    "draw_base_weight",
     "MoeSpec", "MoeWorkload", "generate_moe", "MOE_CONFIGS", "moe_config_by_name",
 ]

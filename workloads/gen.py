@@ -254,3 +254,11 @@ def draw_fold(seed: int, n: int):
     M = d[:, None] * h
     fold = np.ascontiguousarray((h.T / d[None, :]).astype(np.float32))
     return M, fold
+
+
+def draw_base_weight(spec: WorkloadSpec, lane_index: int, lane: LaneSpec, mode: str = "real"):
+    """The base projection's weight of a lane as this GPU holds it: bf16 bits
+    [sum(h_out), h_in] (out_features x this GPU's input columns), drawn from
+    its own stream.  "real": N(0, 0.02^2) like the factors; "int": values in
+    {-1, 0, 1}, so x W^T of an integer-mode x is exact (|.| <= 128)."""
+    return _factor(_stream(spec.seed, 6, lane_index), (lane.h_out_total, lane.h_in), mode)
