@@ -13,12 +13,13 @@ from .lora import (
     lora_build_routing_rows, lora_plan_rows,
     lora_routing_device_counts, moe_slot, moe_row_slots,
     lora_shrink, lora_expand, lora_workspace_bytes,
-    lora_delta_apply,
+    lora_delta_apply, lora_delta_apply_noalloc, delta_apply_noalloc,
 )
 
 _lib.load()
 
 __all__ = [n for n in dir() if n.startswith(("lora_", "Lora")) or n in (
     "Pool", "Routing", "make_desc", "workspace_for", "shrink", "expand", "delta_apply",
+    "delta_apply_noalloc",
     "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS", "moe_slot",
     "moe_row_slots")]

@@ -22,6 +22,7 @@ SEG_WORDS = 16
 GATHER_MIN_RANK = 128         # LORA_GATHER_MIN_RANK
 DEVICE_ROUTING_MAX_TOKENS = 8192   # LORA_DEVICE_ROUTING_MAX_TOKENS
 PREFILL_SEG_ROWS = 64
+NOALLOC_SCRATCH_BYTES = 8388608   # LORA_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/lora.h declares
 EXPORTS = (
@@ -35,6 +36,7 @@ EXPORTS = (
     "lora_routing_token_slots", "lora_build_routing_device", "lora_build_routing_moe",
     "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
+    "lora_delta_apply_noalloc",
 )
 
 
@@ -106,6 +108,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lora_expand": (I32, [P, P, P, P, I64, P]),
         "lora_workspace_bytes": (I32, [P, P, PI64]),
         "lora_delta_apply": (I32, [P, P, P, I64, P, I64, P, I64, P]),
+        "lora_delta_apply_noalloc": (I32, [P, P, P, I64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -327,6 +327,11 @@ def lora_delta_apply(pool, routing, x, ldx, y, ldy, workspace, workspace_bytes,
                                    _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def lora_delta_apply_noalloc(pool, routing, x, ldx, y, ldy, stream=None) -> None:
+    _check(_lib().lora_delta_apply_noalloc(pool, routing, _ptr(x), ldx, _ptr(y), ldy,
+                                           _stream(stream)))
+
+
 # ------------------------------------------------------------ owning wrappers
 
 class Pool:
@@ -472,3 +477,7 @@ def delta_apply(pool: Pool, routing: Routing, x, y, workspace=None, stream=None)
                      workspace, workspace.numel(), stream)
     return workspace
 
+
+def delta_apply_noalloc(pool: Pool, routing: Routing, x, y, stream=None):
+    """delta_apply with v in the library's static scratch (no workspace)."""
+    lora_delta_apply_noalloc(pool.handle, routing.handle, x, x.stride(0), y, y.stride(0), stream)

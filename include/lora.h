@@ -463,6 +463,31 @@ int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
                          const void *x, int64_t ldx, float *y, int64_t ldy,
                          void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * lora_delta_apply for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that must not call hipMalloc, harnesses
+ * that forbid allocation.  The caller passes inputs and outputs only; v lives
+ * in a static device array of the library, LORA_NOALLOC_SCRATCH_BYTES bytes on
+ * each GPU it runs on, held until the process ends.  The kernels and the bits
+ * are those of lora_delta_apply.  The first call on a GPU looks up the
+ * array's device address there (not a stream operation; make that first call
+ * outside graph capture); no call allocates or frees device or pinned memory.
+ *
+ * Every call on one GPU shares that GPU's array, so calls that overlap on the
+ * same GPU (other streams, other threads, other graphs replayed at once) race
+ * on v and give wrong results: order them.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero.
+ *
+ * Errors as lora_delta_apply, plus CAPACITY when lora_workspace_bytes for
+ * this pool and routing exceeds LORA_NOALLOC_SCRATCH_BYTES (nothing is
+ * launched; use lora_delta_apply with a workspace), and HIP if the device or
+ * the array's address cannot be found.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES 8388608
+int32_t lora_delta_apply_noalloc(const lora_pool *pool, const lora_routing *routing,
+                                 const void *x, int64_t ldx, float *y, int64_t ldy,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif
