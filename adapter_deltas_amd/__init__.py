@@ -14,12 +14,13 @@ from .lora import (
     lora_routing_device_counts, moe_slot, moe_row_slots,
     lora_shrink, lora_expand, lora_workspace_bytes,
     lora_delta_apply, lora_delta_apply_noalloc, delta_apply_noalloc,
+    lora_linear_workspace_bytes, lora_linear_delta, linear_delta,
 )
 
 _lib.load()
 
 __all__ = [n for n in dir() if n.startswith(("lora_", "Lora")) or n in (
     "Pool", "Routing", "make_desc", "workspace_for", "shrink", "expand", "delta_apply",
-    "delta_apply_noalloc",
+    "delta_apply_noalloc", "linear_delta",
     "DEFAULT_PREFILL_MIN_LEN", "NO_PREFILL", "DEVICE_ROUTING_MAX_TOKENS", "moe_slot",
     "moe_row_slots")]

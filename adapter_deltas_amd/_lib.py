@@ -37,6 +37,7 @@ EXPORTS = (
     "lora_routing_device_counts",
     "lora_shrink", "lora_expand", "lora_workspace_bytes", "lora_delta_apply",
     "lora_delta_apply_noalloc",
+    "lora_linear_workspace_bytes", "lora_linear_delta",
 )
 
 
@@ -109,6 +110,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "lora_workspace_bytes": (I32, [P, P, PI64]),
         "lora_delta_apply": (I32, [P, P, P, I64, P, I64, P, I64, P]),
         "lora_delta_apply_noalloc": (I32, [P, P, P, I64, P, I64, P]),
+        "lora_linear_workspace_bytes": (I32, [P, P, PI64]),
+        "lora_linear_delta": (I32, [P, P, I32, P, I64, P, I64, P, I64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -14,7 +14,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora.so")
 
 SOURCES = ["lora_abi.cpp", "kernels_gemv.hip", "kernels_mfma.hip", "kernels_route.hip",
-           "kernels_fold.hip", "lora_noalloc.hip"]
+           "kernels_fold.hip", "lora_noalloc.hip", "kernels_linear.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 ALU instructions are switched off for every device compile.

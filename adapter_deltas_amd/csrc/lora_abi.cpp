@@ -149,6 +149,29 @@ int batch_max_rank(const lora_pool *p, const lora_routing *r)
     return m;
 }
 
+// Largest slice rank of the slots whose decode rows take the GEMV path (a
+// slot with a slice rank >= kGatherMinRank sends its decode rows to gather
+// segments): the rank blocks a decode kernel's grid has to cover.
+int gemv_max_rank(const lora_pool *p, const lora_routing *r)
+{
+    auto slot_max = [p](int32_t s) {
+        int m = 0;
+        for (int j = 0; j < kMetaStride; ++j) m = std::max(m, p->h_rank[(size_t)s * kMetaStride + j]);
+        return m;
+    };
+    int m = 0;
+    auto take = [&](int32_t s) {
+        const int sm = slot_max(s);
+        if (sm < kGatherMinRank) m = std::max(m, sm);
+    };
+    if (r->device_built) {
+        for (int32_t s = 1; s <= p->desc.max_slots; ++s) take(s);
+    } else {
+        for (int32_t s : r->distinct_slots) take(s);
+    }
+    return m;
+}
+
 int32_t check_pair(const lora_pool *p, const lora_routing *r)
 {
     if (!p || !r) return fail(LORA_ERR_ARG, "pool or routing is null");
@@ -242,7 +265,8 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
     if (decode && I.n_decode_segments > 0) {
-        int kb = (kmax + kKBlock - 1) / kKBlock;
+        // rank blocks of the GEMV slots only (higher-rank slots are gathered)
+        const int kb = (gemv_max_rank(p, r) + kKBlock - 1) / kKBlock;
         hipError_t e =
             launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, cs.dec);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
@@ -309,6 +333,17 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         if (e != hipSuccess) return hip_fail(e, "expand (gather) launch");
     }
     return LORA_OK;
+}
+
+// The row table lists the active rows (the rows of v, in v's order) and then
+// every other row of the batch in row order, so that a kernel walking all
+// rows of the batch (the base projection with the delta in its epilogue)
+// takes them from one table, active rows first.  Kernels of the delta read
+// only the first n_active entries.
+void append_inactive_rows(Plan &pl)
+{
+    for (size_t t = 0; t < pl.tok.size(); ++t)
+        if (pl.tok[t] == 0) pl.rows.push_back((int32_t)t);
 }
 
 template <class Ranks>
@@ -479,6 +514,7 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     pl.info.n_gather_segments = n_seg - n_dec_seg - n_pre_seg;
     pl.info.n_distinct = (int32_t)distinct_ids.size();
     pl.info.n_seqs = n_seq;
+    append_inactive_rows(pl);
     int32_t na = 0;
     for (int i = 0; i < n_seq; ++i) na += adm[i];
     pl.info.n_admitted_seqs = na;
@@ -579,6 +615,7 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     pl.info.n_gather_segments = n_seg - n_dec_seg;
     pl.info.n_distinct = (int32_t)order.size();
     pl.info.n_seqs = pl.info.n_admitted_seqs = n_rows;
+    append_inactive_rows(pl);
     pl.adm.clear();
     pl.distinct_slots = order;
     pl.slot_ranks.clear();
@@ -1291,7 +1328,7 @@ int32_t delta_apply_ws(const lora_pool *p, const lora_routing *r, const void *x,
     int64_t extra_tiles = 0;
     for (int j = 0; j < p->desc.n_slices; ++j)
         extra_tiles += (p->desc.h_out[j] + kExpandTile - 1) / kExpandTile - 1;
-    const int kmax = batch_max_rank(p, r);
+    const int kmax = gemv_max_rank(p, r);   // the one launch serves decode segments only
     const int64_t extra_bytes = extra_tiles * kmax * (int64_t)p->desc.h_in * 2 *
                                 r->info.n_decode_segments;
     const bool fused = r->info.n_decode_segments > 0 && kmax <= kFusedMaxRank &&
@@ -1311,3 +1348,83 @@ int32_t delta_apply_ws(const lora_pool *p, const lora_routing *r, const void *x,
 }
 
 }  // namespace lora
+
+extern "C" {
+
+int32_t lora_linear_workspace_bytes(const lora_pool *p, const lora_routing *r,
+                                    int64_t *bytes_out)
+{
+    if (!p || !bytes_out) return fail(LORA_ERR_ARG, "pool or bytes_out is null");
+    if (!r) {
+        *bytes_out = 0;
+        return LORA_OK;
+    }
+    return lora_workspace_bytes(p, r, bytes_out);
+}
+
+int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_rows,
+                          const void *W, int64_t ldw, const void *x, int64_t ldx, float *y,
+                          int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (!p) return fail(LORA_ERR_ARG, "pool is null");
+    if (n_rows < 0) return fail(LORA_ERR_SHAPE, "n_rows < 0");
+    if (p->desc.x_dtype != LORA_DTYPE_BF16)
+        return fail(LORA_ERR_DTYPE, "the base projection takes bf16 x (the lane's x is fp16)");
+    if (r) {
+        if (int32_t rc = check_pair(p, r)) return rc;
+        if (r->device_built)
+            return fail(LORA_ERR_ARG, "the base projection needs a routing built on the host");
+        if (r->info.n_tokens != n_rows)
+            return fail(LORA_ERR_SHAPE, "routing covers %d rows, n_rows is %d",
+                        r->info.n_tokens, n_rows);
+    }
+    if (n_rows == 0) return LORA_OK;
+    if (!W) return fail(LORA_ERR_ARG, "W is null");
+    if (!aligned16(W)) return fail(LORA_ERR_SHAPE, "W must be 16-byte aligned");
+    if (ldw < p->desc.h_in || ldw % 8)
+        return fail(LORA_ERR_SHAPE, "ldw=%lld must be >= h_in=%d and a multiple of 8",
+                    (long long)ldw, p->desc.h_in);
+    if (int32_t rc = check_x(p, x, ldx)) return rc;
+    if (int32_t rc = check_y(p, y, ldy)) return rc;
+    const int n_act = r ? r->info.n_active : 0;
+    float *v = static_cast<float *>(workspace);
+    if (n_act > 0) {
+        int64_t need = 0;
+        lora_workspace_bytes(p, r, &need);
+        if (!workspace) return fail(LORA_ERR_ARG, "workspace is null");
+        if (!aligned16(workspace))
+            return fail(LORA_ERR_SHAPE, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(LORA_ERR_CAPACITY, "workspace %lld bytes < %lld needed",
+                        (long long)workspace_bytes, (long long)need);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_act > 0) {
+        // v of the active rows, in the routing's order, by the shrink kernels
+        CallStreams cs;
+        if (int32_t rc = fork_streams(r, st, cs)) return rc;
+        const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs);
+        const int32_t rj = join_streams(r, cs);
+        if (rc) return rc;
+        if (rj) return rj;
+    }
+    LinearArgs a{};
+    a.W = static_cast<const uint16_t *>(W);
+    a.ldw = ldw;
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.y = y;
+    a.ldy = ldy;
+    a.M = n_rows;
+    a.N = p->geom.H_out;
+    a.K = p->desc.h_in;
+    a.rows = r ? r->dev + r->off_row : nullptr;
+    a.n_delta = n_act;
+    a.tok_slot = r ? r->dev + r->off_tok : nullptr;
+    a.v = v;
+    hipError_t e = launch_linear(p->geom, pool_dev(p), a, st);
+    if (e != hipSuccess) return hip_fail(e, "base projection launch");
+    return LORA_OK;
+}
+
+}  // extern "C"

@@ -82,7 +82,8 @@ struct PoolDev {
 struct RoutingDev {
     const int32_t *seg;       // kSegWords words per segment
     const int32_t *tok_slot;  // slot per token row
-    const int32_t *rows;      // token row of each active row
+    const int32_t *rows;      // token row of each active row (host-built: then the
+                              // other rows of the batch)
     const int32_t *counts;    // device-built routing: exact counts (else null)
 };
 // Entries of a device-built routing's counts.
@@ -100,7 +101,24 @@ struct MoeDispatch {
     int n_adapter_slots;   // max_slots / n_experts
 };
 
+// Arguments of the base projection with the delta in its epilogue.
+struct LinearArgs {
+    const uint16_t *W;        // [N][ldw] bf16: the projection's weight (out x in)
+    int64_t ldw;
+    const uint16_t *x;        // [*][ldx] bf16
+    int64_t ldx;
+    float *y;                 // [*][ldy] fp32, written
+    int64_t ldy;
+    int M, N, K;              // rows of the batch, sum(h_out), h_in
+    const int32_t *rows;      // GEMM row m -> token row (null: m itself)
+    int n_delta;              // GEMM rows m < n_delta carry a delta; v row m
+    const int32_t *tok_slot;  // slot per token row
+    const float *v;           // [n_delta][v_stride] fp32, the shrink's output
+};
+
 // ---- launchers (kernels_*.hip) ----
+hipError_t launch_linear(const LaneGeom &g, const PoolDev &p, const LinearArgs &a,
+                         hipStream_t s);
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
                               float *v, hipStream_t s);

@@ -332,6 +332,18 @@ def lora_delta_apply_noalloc(pool, routing, x, ldx, y, ldy, stream=None) -> None
                                            _stream(stream)))
 
 
+def lora_linear_workspace_bytes(pool, routing) -> int:
+    n = ctypes.c_int64()
+    _check(_lib().lora_linear_workspace_bytes(pool, routing, ctypes.byref(n)))
+    return n.value
+
+
+def lora_linear_delta(pool, routing, n_rows, W, ldw, x, ldx, y, ldy, workspace,
+                      workspace_bytes, stream=None) -> None:
+    _check(_lib().lora_linear_delta(pool, routing, n_rows, _ptr(W), ldw, _ptr(x), ldx, _ptr(y),
+                                    ldy, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------ owning wrappers
 
 class Pool:
@@ -481,3 +493,18 @@ def delta_apply(pool: Pool, routing: Routing, x, y, workspace=None, stream=None)
 def delta_apply_noalloc(pool: Pool, routing: Routing, x, y, stream=None):
     """delta_apply with v in the library's static scratch (no workspace)."""
     lora_delta_apply_noalloc(pool.handle, routing.handle, x, x.stride(0), y, y.stride(0), stream)
+
+
+def linear_delta(pool: Pool, routing, W, x, y, workspace=None, stream=None):
+    """y = x W^T (+ the delta of the routing's rows; routing None: no delta).
+    W: bf16 bits [sum(h_out), >= h_in] on the device."""
+    rh = routing.handle if routing is not None else None
+    if workspace is None:
+        n = lora_linear_workspace_bytes(pool.handle, rh)
+        if n > 0:
+            import torch
+            workspace = torch.empty(n, dtype=torch.uint8, device=y.device)
+    nbytes = workspace.numel() if workspace is not None else 0
+    lora_linear_delta(pool.handle, rh, x.shape[0], W, W.stride(0), x, x.stride(0), y,
+                      y.stride(0), workspace, nbytes, stream)
+    return workspace

@@ -254,6 +254,75 @@ def moe_algorithmic(w, lane_name):
     return {"shrink": (sb, sf_), "expand": (eb, ef), "active": act, "pairs": len(pairs)}
 
 
+def linear_leg(args, spec, w, layers, routing, ws, replay_us, dev, adm):
+    """The base projection with the delta in its partial sum (lora_linear_delta)
+    on each bf16 lane of the workload: the fused call, the same kernel with the
+    delta off (no routing), and torch.mm (bf16 in, fp32 out) followed by
+    lora_delta_apply as context, each captured for enough layers to pass the
+    last-level cache and replayed.  Priced against W + x + A + B + the y write
+    (HBM) and against the product's flops (matrix cores)."""
+    import torch
+    import adapter_deltas_amd as m
+    from workloads import draw_base_weight
+    out = {}
+    for li, L in enumerate(spec.lanes):
+        if L.x_dtype != "bf16":
+            continue
+        W = torch.from_numpy(draw_base_weight(spec, li, L).view(np.int16)).to(dev)
+        per_layer = W.numel() * 2 + layers[0][L.name][1].numel() * 2 + \
+            layers[0][L.name][2].numel() * 4 + layers[0][L.name][0].nbytes
+        n = min(len(layers), max(8, -(-(1 << 30) // per_layer)))
+        Ws = [W] + [W.clone() for _ in range(n - 1)]
+        lws = m.lora_linear_workspace_bytes(layers[0][L.name][0].handle, routing.handle)
+        lw = torch.empty(max(lws, 256), dtype=torch.uint8, device=dev)
+
+        def body(call):
+            def f():
+                for i in range(n):
+                    pool, x, y = layers[i][L.name]
+                    call(pool, x, y, Ws[i])
+            return f
+        fused = replay_us(body(lambda pool, x, y, Wi: m.linear_delta(pool, routing, Wi, x, y,
+                                                                      lw))) / n
+        base = replay_us(body(lambda pool, x, y, Wi: m.linear_delta(pool, None, Wi, x, y))) / n
+        mm_note = "torch.mm(x, W^T, out_dtype=float32)"
+        try:
+            def tmm(pool, x, y, Wi):
+                torch.mm(x.view(torch.bfloat16), Wi.view(torch.bfloat16).t(),
+                         out_dtype=torch.float32, out=y)
+            tmm(*layers[0][L.name], Ws[0])
+        except Exception as e:       # context only: a bf16 product copied into y
+            mm_note = f"torch.mm in bf16, copied to fp32 y (out_dtype failed: {e})"
+
+            def tmm(pool, x, y, Wi):
+                y.copy_(torch.mm(x.view(torch.bfloat16), Wi.view(torch.bfloat16).t()))
+        torch.cuda.synchronize()
+        mm_us = replay_us(body(tmm)) / n
+        mm_apply = replay_us(body(lambda pool, x, y, Wi: (
+            tmm(pool, x, y, Wi), m.delta_apply(pool, routing, x, y, ws[L.name])))) / n
+        a = algorithmic(w, L.name, adm)
+        T = w.n_tokens
+        nbytes = (W.numel() * 2 + T * L.h_in * 2 + T * L.h_out_total * 4 +
+                  (a["shrink"][0] - a["active"] * L.h_in * 2 - 4 * T) +
+                  (a["expand"][0] - a["active"] * 8 * L.h_out_total))
+        flops = 2 * T * L.h_out_total * L.h_in + a["shrink"][1] + a["expand"][1]
+        gbs = nbytes / (fused * 1e-6) / 1e9
+        out[L.name] = {
+            "layers": n,
+            "fused_us": round(fused, 3), "base_only_us": round(base, 3),
+            "delta_marginal_us": round(fused - base, 3),
+            "torch_mm_us": round(mm_us, 3), "torch_mm_plus_delta_apply_us": round(mm_apply, 3),
+            "torch_mm": mm_note,
+            "algorithmic_bytes": int(nbytes), "flops": int(flops),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (fused * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "base_only_hbm_frac": round((W.numel() * 2 + T * L.h_in * 2 + T * L.h_out_total * 4)
+                                        / (base * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del Ws
+    return out
+
+
 def main_moe(args, spec):
     """The expert LoRA delta of MoE layers: per layer, the dispatched rows are
     routed on the device to their (adapter, expert) pool slots, then the delta
@@ -488,6 +557,8 @@ def main():
     ap.add_argument("--graph-reps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill-min-len", type=int, default=64)
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the base projection with the delta in its epilogue")
     ap.add_argument("--only-apply", action="store_true",
                     help="only run the steps (routing + delta_apply per lane and layer), "
                          "for counter passes: no graph timing, no CPU baseline")
@@ -698,6 +769,11 @@ def main():
                     "per-row slots, then delta_apply on every lane of every layer",
         }
 
+    linear = None
+    if not args.no_linear and any(l.x_dtype == "bf16" for l in spec.lanes):
+        log("base projection with the delta in its epilogue")
+        linear = linear_leg(args, spec, w, layers, routing, ws, replay_us, dev, adm)
+
     alg = {"shrink": [0, 0], "expand": [0, 0]}
     for ln in lanes:
         a = algorithmic(w, ln, adm)
@@ -792,6 +868,7 @@ def main():
                       f"CPU share of one GPU), {par_reps} repetitions in {par_dt:.1f} s",
         },
         "device_routing": device_routing,
+        "linear_delta": linear,
         "context": {
             "stream_copy_gbs": round(copy_gbs, 1),
             "stream_copy": "torch copy of 1 GiB, read + write bytes per second",

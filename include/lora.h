@@ -464,6 +464,45 @@ int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
                          void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * The base projection with the delta in its fp32 partial sum, in one pass over
+ * the output (TensorFold PR #47, third commit message and PR body "What this
+ * changes": the delta is added in fp32 to the partial sum the base projection
+ * produces, before the cross-rank reduction):
+ *
+ *     y[t] = x[t] W^T                    for every row t < n_rows
+ *          + scale[s][j] B[s][j] (A[s][j] x[t])  on slice j's columns,
+ *                                        for a row whose slot s != 0
+ *
+ * The delta is added to the product's fp32 accumulator before the one store
+ * of y; y is written, not read.  Rows of the base model and rows the
+ * routing defers get x W^T alone.
+ *
+ *   routing  a routing built on the host (lora_build_routing or
+ *            lora_build_routing_rows) for exactly n_rows rows, or NULL for the
+ *            base product alone (the same kernel with no delta)
+ *   W        device bf16 [sum(h_out)][ldw]: the projection's weight in the
+ *            linear layer's [out_features, in_features] orientation (the
+ *            slices' rows stacked as in y; a row-parallel share holds this
+ *            GPU's h_in input columns), 16-byte aligned, ldw >= h_in, % 8 == 0
+ *   x, y     as lora_delta_apply; the lane's x must be bf16
+ *   workspace  device memory of lora_linear_workspace_bytes bytes (v of the
+ *            active rows), ignored when routing is NULL
+ *
+ * Sums: each output is a chain of 32-element matrix-core steps over h_in in
+ * ascending order from zero; the delta is an fp32 fma chain over the
+ * adapter's ranks from zero, then y = product + delta.  So on a decode row
+ * the result is bit-identical to lora_delta_apply applied to the result of
+ * this call with routing NULL.  Errors: ARG (null pool, W or buffers; a
+ * routing built on the device), SHAPE (n_rows != the routing's rows, widths,
+ * strides, alignment), DTYPE (fp16 lane), MISMATCH, CAPACITY (workspace), HIP.
+ */
+int32_t lora_linear_workspace_bytes(const lora_pool *pool, const lora_routing *routing,
+                                    int64_t *bytes_out);
+int32_t lora_linear_delta(const lora_pool *pool, const lora_routing *routing, int32_t n_rows,
+                          const void *W, int64_t ldw, const void *x, int64_t ldx, float *y,
+                          int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * lora_delta_apply for callers that cannot allocate device memory: code under
  * HIP graph capture, serving loops that must not call hipMalloc, harnesses
  * that forbid allocation.  The caller passes inputs and outputs only; v lives
