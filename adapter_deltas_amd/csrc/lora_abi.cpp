@@ -272,14 +272,21 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
     const int nt = (kmax + 15) / 16;
-    if (I.n_prefill_segments > 0) {
+    if (I.n_prefill_segments > 0 && I.n_gather_segments > 0) {
+        // Prefill and gather segments follow each other in the table, and the
+        // host plan's row table holds the token row of every one of their
+        // rows: one launch of the gather form covers both (it takes each row
+        // from the table; the sums are the same).
+        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
+                                          I.n_prefill_segments + I.n_gather_segments, nt, x,
+                                          ldx, v, s);
+        if (e != hipSuccess) return hip_fail(e, "shrink (prefill + gather) launch");
+    } else if (I.n_prefill_segments > 0) {
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, false, I.n_decode_segments,
                                           I.n_prefill_segments, nt, x, ldx, v, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill) launch");
-    }
-    if (I.n_gather_segments > 0) {
-        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true,
-                                          I.n_decode_segments + I.n_prefill_segments,
+    } else if (I.n_gather_segments > 0) {
+        hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
                                           I.n_gather_segments, nt, x, ldx, v, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (gather) launch");
     }
@@ -319,6 +326,14 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
         return (int)std::max<int64_t>(1, std::min<int64_t>(kExpandMaxGroup, fit));
     };
     const int kmax = batch_max_rank(p, r);
+    if (I.n_prefill_segments > 0 && I.n_gather_segments > 0) {
+        // one launch of the gather form over both kinds (as in the shrink)
+        const int n = I.n_prefill_segments + I.n_gather_segments;
+        hipError_t e = launch_expand_mfma(p->geom, pd, rd, true, I.n_decode_segments, n,
+                                          group_for(n), kmax, kPrefillSegRows, v, y, ldy, s);
+        if (e != hipSuccess) return hip_fail(e, "expand (prefill + gather) launch");
+        return LORA_OK;
+    }
     if (I.n_prefill_segments > 0) {
         hipError_t e = launch_expand_mfma(p->geom, pd, rd, false, I.n_decode_segments,
                                           I.n_prefill_segments, group_for(I.n_prefill_segments),

@@ -21,7 +21,10 @@ constexpr int kSubChunk = 512;                          // h_in elements per wav
 constexpr int kParts = 8;                               // interleaved h_in parts (one wave each)
 constexpr int kExpandTile = 512;                        // columns per decode expand task
 constexpr int kFusedMaxRank = 16;                       // ranks of the one-launch decode delta
-constexpr int64_t kFusedMaxExtraBytes = 4 << 20;        // and the A bytes its tiles re-read
+#ifndef LORA_FUSED_MAX_EXTRA_BYTES
+#define LORA_FUSED_MAX_EXTRA_BYTES (4 << 20)
+#endif
+constexpr int64_t kFusedMaxExtraBytes = LORA_FUSED_MAX_EXTRA_BYTES;  // and the A its tiles re-read
 constexpr int kMfmaExpandCols = 128;                    // columns per prefill expand task
 #ifndef LORA_EXPAND_BLOCKS
 #define LORA_EXPAND_BLOCKS 8192
