@@ -134,10 +134,12 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     }
     const uint16_t *a_slice =
         p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
+    // Rank tiles past the segment's rank read the last tile the rank has
+    // again (a cache hit, not new bytes) and are not multiplied.
     const uint16_t *ar[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i)
-        ar[i] = a_slice + (int64_t)min(16 * (t0 + i) + a, g.rank_pad - 1) * g.h_in;
+        ar[i] = a_slice + (int64_t)min(16 * (t0 + min(i, nt_here - 1)) + a, g.rank_pad - 1) * g.h_in;
 
     __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][4];   // per wave: x rows, then A rows
     uint4(*const lw)[4] = lds[wave];
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
             if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
 #pragma unroll
             for (int nt = 0; nt < NG; ++nt) {
+                if (nt >= nt_here) continue;    // uniform
                 acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
                 if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
             }
