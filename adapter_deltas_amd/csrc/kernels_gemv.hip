@@ -20,11 +20,15 @@ namespace {
 // The prologue has no branch before the descriptor and count loads are
 // issued, and the scale load follows them, so the first data loads wait for
 // about two scalar round trips rather than a chain of them.
+//
+// vsplit > 0: v is written in the split form of the base projection's
+// epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int W>
 __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
                                                          int n_tasks, int kb_per_slice,
                                                          const uint16_t *__restrict__ x,
-                                                         int64_t ldx, float *__restrict__ v)
+                                                         int64_t ldx, float *__restrict__ v,
+                                                         int vsplit)
 {
     touch_args(n_tasks, g, p, r, ldx);
     const int per_seg = g.n_slices * kb_per_slice;
@@ -68,7 +72,14 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
         const int c = lane / kKBlock;
         const int k = lane % kKBlock;
         if (c < sd.n_rows() && k < kn) {
-            v[(int64_t)(sd.v_row() + c) * g.v_stride + j * g.rank_pad + k0 + k] = scale * (q0 + q1);
+            const float val = scale * (q0 + q1);
+            if (vsplit) {
+                const float one[1] = {val};
+                store_vsplit<1>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_chunks(g.rank_pad),
+                                sd.v_row() + c, j, k0 + k, one);
+            } else {
+                v[(int64_t)(sd.v_row() + c) * g.v_stride + j * g.rank_pad + k0 + k] = val;
+            }
         }
     }
 }
@@ -289,7 +300,7 @@ __global__ void k_clear_meta(int32_t *rank_tab, float *scale_tab, int n)
 
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx, float *v,
-                              hipStream_t s)
+                              int vsplit, hipStream_t s)
 {
     const int64_t blocks = (int64_t)n_seg * g.n_slices * kb_per_slice;
     if (blocks <= 0) return hipSuccess;
@@ -308,7 +319,7 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const dim3 grid((unsigned)blocks), block(64 * w);
 #define LAUNCH_SHRINK(F, W) \
     hipLaunchKernelGGL((k_shrink_gemv<F, W>), grid, block, 0, s, g, p, r, (int)blocks, \
-                       kb_per_slice, xp, ldx, v)
+                       kb_per_slice, xp, ldx, v, vsplit)
     if (g.x_fp16) {
         if (w == 8) LAUNCH_SHRINK(true, 8);
         else if (w == 4) LAUNCH_SHRINK(true, 4);

@@ -1,4 +1,4 @@
-// The base projection with the delta in its epilogue (gfx950).
+// The base projection with the delta in its accumulator (gfx950).
 //
 // y[t] = x[t] W^T for every row t of the batch, and for a row t with adapter
 // slot s != 0 the delta of each slice is added to the fp32 accumulator before
@@ -12,15 +12,12 @@
 //           consecutive output features (4 (l / 16) .. + 3) of one row
 //           (l % 16) and stores them as one 16-byte write.  Each output sums
 //           its K-steps of 32 in ascending order, from zero.
-// Delta:    for each 16-row group and slot, d^T[o][t] = sum over rank steps of
-//           32 (ascending, from zero) of two MFMAs, B rows times v_hi then B
-//           rows times v_lo, with v = v_hi + v_lo split into bf16 (nearest
-//           even); then y = acc + d.  That is the prefill expand's arithmetic,
-//           so on a row the routing sends to the matrix cores (prefill and
-//           gather rows) the result equals lora_delta_apply applied to this
-//           kernel's base product, bit for bit.  A 16-column group that
-//           straddles a slice edge (slice widths are multiples of 8, not 16)
-//           takes an fp32 fma chain over the ranks instead.
+// Delta:    as K-tiles after the product's, in the same accumulator: per
+//           distinct slot of the tile's rows, slice and 32-rank chunk, B rows
+//           times v_hi, then B rows times v_lo (v = v_hi + v_lo, both bf16,
+//           written so by the shrink), with every other row, column and rank
+//           read as zero.  Each output sums its own product terms, then its own
+//           delta terms, in a fixed order, plus exact zeros.
 // A row's bits depend on its own x row, W and its adapter only.
 #include "kernels_common.h"
 
@@ -37,26 +34,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
-}
-
-// Two-term bf16 form of eight fp32 values: hi = bf16(f), lo = bf16(f - hi).
-__device__ __forceinline__ void split_f32x8(const float (&f)[8], uint4 &hi, uint4 &lo)
-{
-    uint32_t h[8], l[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        h[m] = bf16_bits(f[m]);
-        l[m] = bf16_bits(f[m] - __uint_as_float(h[m] << 16));
-    }
-    hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                    h[6] | (h[7] << 16));
-    lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                    l[6] | (l[7] << 16));
 }
 
 constexpr int kBK = 64;            // K elements per tile: 8 chunks of 16 bytes per row
@@ -76,13 +53,19 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 //
 // Main loop: K-tiles of kBK; the global loads of tile kt + D are issued while
 // tile kt is multiplied (D register sets in flight), then each set is moved to
-// one of two LDS buffers.  The loop is branch-free: it runs a multiple of D
-// tiles, and a tile past K loads zeros (adding exact zeros to every sum).
-// Epilogue: the accumulator tile goes through LDS to a row layout; wave w then
-// takes rows w, w + 4, ... and, per row, its lanes take the tile's columns
-// (CPL consecutive columns each), adding the row's delta with B^T loaded
-// coalesced along the columns.  Each row's token, slot and ranks are loaded
-// into the wave's lanes when the kernel starts and read back with readlane.
+// one of two LDS buffers, with its masks applied.  The loop is branch-free: it
+// runs a multiple of D tiles, and a tile past the last loads zeros.
+//
+// The delta, as K-tiles after the product's: for each distinct slot s among
+// the tile's rows (ascending), each slice j the tile's columns touch and each
+// chunk c of 32 ranks (as many as the largest rank among those slots and
+// slices needs), one tile whose W rows are B[s][j][o][32 c ..] (output-major,
+// zero past the rank; the same 32 ranks in both halves of the tile) and whose
+// x rows are v_hi of ranks 32 c .. in its first half and v_lo in its second,
+// from the split v the shrink wrote.  A row of another slot, a column of
+// another slice and a rank past the slot's rank read as zero, so each
+// output's sum gets exactly its own row's delta terms, in a fixed order, and
+// exact zeros from the rest.
 constexpr int kGroupM = 8;
 
 __device__ __forceinline__ void tile_of(int task, int n_tiles, int m_tiles, int &tn, int &tm)
@@ -93,6 +76,38 @@ __device__ __forceinline__ void tile_of(int task, int n_tiles, int m_tiles, int 
     const int gm = min(kGroupM, m_tiles - grp * kGroupM);   // row tiles in this group
     tn = in / gm;
     tm = grp * kGroupM + (in - tn * gm);
+}
+
+__device__ __forceinline__ int wave_min(int v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ int pick_rank(const int4 &rk, int j)
+{
+    return j == 0 ? rk.x : j == 1 ? rk.y : j == 2 ? rk.z : rk.w;
+}
+
+// The chunk, or zeros (masks, so no select of aggregates goes through memory).
+__device__ __forceinline__ uint4 keep_if(uint4 w, bool ok)
+{
+    const uint32_t m = ok ? ~0u : 0u;
+    return make_uint4(w.x & m, w.y & m, w.z & m, w.w & m);
+}
+
+// Zeroes the bf16 values of a 16-byte chunk from position n_ok on (0..8).
+__device__ __forceinline__ uint4 keep_first(uint4 w, int n_ok)
+{
+    uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = 2 * i < n_ok ? 0xffffu : 0u;
+        const uint32_t hi = 2 * i + 1 < n_ok ? 0xffff0000u : 0u;
+        q[i] &= lo | hi;
+    }
+    return make_uint4(q[0], q[1], q[2], q[3]);
 }
 
 template <int BN, int BM, bool DELTA>
@@ -108,13 +123,17 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     constexpr int RPW = BM / (kThreads / 64);              // epilogue rows per wave
     static_assert(ROWS * kChunks % kThreads == 0, "loads tile the threads");
     static_assert(CPL == 1 || CPL == 2, "64 or 128 columns");
-    static_assert(RPW <= 64, "one lane per epilogue row");
+    static_assert(RPW <= 64 && BM <= 128, "one lane per epilogue row");
     constexpr int kStageBytes = 2 * ROWS * kChunks * 16;
     constexpr int kTileBytes = BM * LDT * 4;
     __shared__ __align__(16) unsigned char smem[kStageBytes > kTileBytes ? kStageBytes
                                                                          : kTileBytes];
     uint4(*const lds)[ROWS][kChunks] = reinterpret_cast<uint4(*)[ROWS][kChunks]>(smem);
     float(*const tile)[LDT] = reinterpret_cast<float(*)[LDT]>(smem);
+    // the tile's distinct slots and their ranks (delta)
+    __shared__ int d_slot[DELTA ? BM : 1];
+    __shared__ int4 d_rk[DELTA ? BM : 1];
+    __shared__ int d_count[2];
 
     int tn, tm;
     tile_of(xcd_task(blockIdx.x, n_tasks), n_tiles, m_tiles, tn, tm);
@@ -123,26 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     const int wave = tid >> 6, lane = tid & 63;
     const int wn = wave >> 1, wm = wave & 1;
 
-    // The slot and ranks of the rows this lane holds in the accumulator
-    // layout (row 16 mi + li of the wave's row half), for the delta.
-    int ms[MI];
-    int4 mrk[MI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        ms[mi] = 0;
-        mrk[mi] = make_int4(0, 0, 0, 0);
-        if constexpr (DELTA) {
-            const int m = m0 + wm * (BM / 2) + 16 * mi + (lane & 15);
-            if (m < a.n_delta) {
-                ms[mi] = a.tok_slot[a.rows ? a.rows[m] : m];
-                mrk[mi] = *reinterpret_cast<const int4 *>(p.rank + ms[mi] * kMetaStride);
-            }
-        }
-    }
-
     // The epilogue rows of this wave are the RPW consecutive tile rows
-    // wave * RPW + i; lane i < RPW holds that row's token, slot and the rank of
-    // each slice, loaded now and used at the end.
+    // wave * RPW + i; lane i < RPW holds that row's token.
     const int e_row0 = wave * RPW;
     int my_t = 0;
     {
@@ -156,32 +157,171 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     const int lc = tid & 7;
     const uint16_t *src[NL];
     int lrow[NL];
+    int xslot[NL];          // delta: the slot of the x row (0 for W rows and base rows)
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int r = (tid >> 3) + 32 * i;
         lrow[i] = r;
+        xslot[i] = 0;
         if (r < BN) {
             src[i] = a.W + (int64_t)min(n0 + r, a.N - 1) * a.ldw;
         } else {
             const int m = min(m0 + r - BN, a.M - 1);
             const int t = a.rows ? a.rows[m] : m;
             src[i] = a.x + (int64_t)t * a.ldx;
+            if constexpr (DELTA)
+                if (m0 + r - BN < a.n_delta) xslot[i] = a.tok_slot[t];
         }
     }
     const int KT = (a.K + kBK - 1) / kBK;
-    uint4 st[D][NL];
-    // Loads read a clamped address; the chunks past K are zeroed when the set
-    // is written to LDS, so nothing waits for a load before it is needed.
-    auto load = [&](uint4 (&dst)[NL], int kt) {
-        const int ec = min(kt * kBK + lc * 8, a.K - 8);
-#pragma unroll
-        for (int i = 0; i < NL; ++i) dst[i] = ld16(src[i] + ec);
+
+    // Delta tiles: the tile's slices [j_lo, j_hi], distinct slots, chunks.
+    auto slice_of = [&](int col) __attribute__((always_inline)) {
+        return (g.n_slices > 1 && col >= g.col_off[1]) + (g.n_slices > 2 && col >= g.col_off[2]) +
+               (g.n_slices > 3 && col >= g.col_off[3]);
     };
-    auto store = [&](const uint4 (&from)[NL], int kt, int buf) {
-        const bool ok = kt * kBK + lc * 8 < a.K;   // K is a multiple of 8: whole chunks
+    const int j_lo = slice_of(n0), j_hi = slice_of(min(n0 + BN - 1, a.N - 1));
+    const int ns = j_hi - j_lo + 1;
+    int n_dist = 0, nchk = 1;
+    if constexpr (DELTA) {
+        if (wave == 0) {
+            // each lane holds the slots and ranks of rows lane and lane + 64
+            int sa = 0, sb = 0;
+            int4 ra = make_int4(0, 0, 0, 0), rb = make_int4(0, 0, 0, 0);
+            {
+                const int ma = m0 + lane, mb = m0 + lane + 64;
+                if (lane < BM && ma < a.n_delta) {
+                    sa = a.tok_slot[a.rows ? a.rows[ma] : ma];
+                    ra = *reinterpret_cast<const int4 *>(p.rank + sa * kMetaStride);
+                }
+                if (lane + 64 < BM && mb < a.n_delta) {
+                    sb = a.tok_slot[a.rows ? a.rows[mb] : mb];
+                    rb = *reinterpret_cast<const int4 *>(p.rank + sb * kMetaStride);
+                }
+            }
+            // the distinct nonzero slots, ascending, by repeated minimum
+            int last = 0, n = 0, rmax = 0;
+            for (;;) {
+                const int c = wave_min(min(sa > last ? sa : INT32_MAX, sb > last ? sb : INT32_MAX));
+                if (c == INT32_MAX) break;
+                const uint64_t ha = __builtin_amdgcn_ballot_w64(sa == c);
+                const uint64_t hb = __builtin_amdgcn_ballot_w64(sb == c);
+                int4 rk;
+                if (ha) {
+                    const int l = (int)__builtin_ctzll(ha);
+                    rk = make_int4(__builtin_amdgcn_readlane(ra.x, l), __builtin_amdgcn_readlane(ra.y, l),
+                                   __builtin_amdgcn_readlane(ra.z, l), __builtin_amdgcn_readlane(ra.w, l));
+                } else {
+                    const int l = (int)__builtin_ctzll(hb);
+                    rk = make_int4(__builtin_amdgcn_readlane(rb.x, l), __builtin_amdgcn_readlane(rb.y, l),
+                                   __builtin_amdgcn_readlane(rb.z, l), __builtin_amdgcn_readlane(rb.w, l));
+                }
+                if (lane == 0) {
+                    d_slot[n] = c;
+                    d_rk[n] = rk;
+                }
+                for (int j = j_lo; j <= j_hi; ++j) rmax = max(rmax, pick_rank(rk, j));
+                ++n;
+                last = c;
+            }
+            if (lane == 0) {
+                d_count[0] = n;
+                d_count[1] = rmax;
+            }
+        }
+        __syncthreads();
+        n_dist = __builtin_amdgcn_readfirstlane(d_count[0]);
+        nchk = max(1, (__builtin_amdgcn_readfirstlane(d_count[1]) + 31) / 32);
+    }
+    const int T_d = n_dist * ns * nchk;      // delta K-tiles (0 without a delta)
+    const int KT_all = KT + T_d;
+    const int C = vsplit_chunks(g.rank_pad);
+    const int vs_len = g.n_slices * C * 64;
+    const uint16_t *vs = reinterpret_cast<const uint16_t *>(a.v);
+
+    // per-slice widths and offsets, selected by slice below
+    const int hj_[4] = {g.h_out[0], g.h_out[1], g.h_out[2], g.h_out[3]};
+    const int cj_[4] = {g.col_off[0], g.col_off[1], g.col_off[2], g.col_off[3]};
+    const int64_t bo_[4] = {g.bt_slice_off[0], g.bt_slice_off[1], g.bt_slice_off[2],
+                            g.bt_slice_off[3]};
+    auto sel = [](int j, auto v0, auto v1, auto v2, auto v3) __attribute__((always_inline)) {
+        return j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3;
+    };
+    auto h_of = [&](int j) __attribute__((always_inline)) { return sel(j, hj_[0], hj_[1], hj_[2], hj_[3]); };
+    auto c_of = [&](int j) __attribute__((always_inline)) { return sel(j, cj_[0], cj_[1], cj_[2], cj_[3]); };
+    auto b_of = [&](int j) __attribute__((always_inline)) { return sel(j, bo_[0], bo_[1], bo_[2], bo_[3]); };
+
+    // delta tile t: slot index d, slice j, chunk c
+    struct DTile { int s, j, c, rank; };
+    auto dtile = [&](int t) __attribute__((always_inline)) {
+        DTile dt;
+        const int per_d = ns * nchk;
+        const int d = t / per_d;
+        const int rem = t - d * per_d;
+        dt.j = j_lo + rem / nchk;
+        dt.c = rem - (rem / nchk) * nchk;
+        dt.s = __builtin_amdgcn_readfirstlane(d_slot[d]);
+        dt.rank = __builtin_amdgcn_readfirstlane(pick_rank(d_rk[d], dt.j));
+        return dt;
+    };
+
+    uint4 st[D][NL];
+    // Loads read a clamped address; masks are applied when a set is written
+    // to LDS, so nothing waits for a load before it is needed.
+    auto load = [&](uint4 (&dst)[NL], int kt) __attribute__((always_inline)) {
+        if (kt < KT || kt >= KT_all) {           // the product's tile (or past the last)
+            const int ec = min(kt * kBK + lc * 8, a.K - 8);
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-            lds[buf][lrow[i]][swz(lrow[i], lc)] = ok ? from[i] : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < NL; ++i) dst[i] = ld16(src[i] + ec);
+        } else {
+            const DTile dt = dtile(kt - KT);
+            const int hj = h_of(dt.j), cj = c_of(dt.j);
+            const uint16_t *bn = p.Bn + (int64_t)(dt.s - 1) * g.bt_slot_stride + b_of(dt.j) +
+                                 min(32 * dt.c + 8 * (lc & 3), g.rank_pad - 8);
+            const uint16_t *vc = vs + (dt.j * C + dt.c) * 64 + 8 * lc;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int r = lrow[i];
+                if (r < BN) {
+                    const int ol = min(max(n0 + r - cj, 0), hj - 1);
+                    dst[i] = ld16(bn + (int64_t)ol * g.rank_pad);
+                } else {
+                    const int m = min(m0 + r - BN, a.n_delta - 1);
+                    dst[i] = ld16(vc + (int64_t)m * vs_len);
+                }
+            }
+        }
+    };
+    auto store = [&](const uint4 (&from)[NL], int kt, int buf) __attribute__((always_inline)) {
+        if (kt < KT) {
+            const bool ok = kt * kBK + lc * 8 < a.K;   // K is a multiple of 8: whole chunks
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                lds[buf][lrow[i]][swz(lrow[i], lc)] = keep_if(from[i], ok);
+        } else if (kt < KT_all) {
+            const DTile dt = dtile(kt - KT);
+            const int hj = h_of(dt.j), cj = c_of(dt.j);
+            const int kb = 32 * dt.c + 8 * (lc & 3);      // first rank of this chunk
+            const int n_ok = min(max(dt.rank - kb, 0), 8);
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int r = lrow[i];
+                uint4 w;
+                if (r < BN) {
+                    const int ol = n0 + r - cj;
+                    const bool ok = n0 + r < a.N && ol >= 0 && ol < hj && kb < g.rank_pad;
+                    w = keep_if(from[i], ok);
+                } else {
+                    const bool ok = m0 + r - BN < a.n_delta && xslot[i] == dt.s;
+                    w = keep_first(from[i], ok ? n_ok : 0);
+                }
+                lds[buf][r][swz(r, lc)] = w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                lds[buf][lrow[i]][swz(lrow[i], lc)] = make_uint4(0, 0, 0, 0);
+        }
     };
 
     f32x4_t acc[NI][MI];
@@ -191,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
         for (int mi = 0; mi < MI; ++mi) acc[ni][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int li = lane & 15, lg = lane >> 4;
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
             const int cq = ks * 4 + lg;
@@ -215,14 +355,12 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     };
 
     // Register set kt % D holds K-tile kt from its load until its move to LDS;
-    // the loop is unrolled by D so every set is named at compile time, and
-    // every step runs (tiles past K are zeros), so no load waits behind a
-    // branch.
+    // the loop is unrolled by D so every set is named at compile time.
 #pragma unroll
     for (int d = 0; d < D; ++d) load(st[d], d);
     store(st[0], 0, 0);
     __syncthreads();
-    auto step = [&](auto slot, int kt) {
+    auto step = [&](auto slot, int kt) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         load(st[S], kt + D);
         __builtin_amdgcn_sched_barrier(0);
@@ -231,118 +369,11 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
         store(st[(S + 1) % D], kt + 1, (kt + 1) & 1);
         __syncthreads();
     };
-    const int KTD = (KT + D - 1) / D * D;
+    const int KTD = (KT_all + D - 1) / D * D;
     for (int kt = 0; kt < KTD; kt += D) {
         step(std::integral_constant<int, 0>{}, kt);
         step(std::integral_constant<int, 1>{}, kt + 1);
         if constexpr (D > 2) step(std::integral_constant<int, 2>{}, kt + 2);
-    }
-
-    if constexpr (DELTA) {
-        auto slice_of = [&](int col) {
-            return (g.n_slices > 1 && col >= g.col_off[1]) + (g.n_slices > 2 && col >= g.col_off[2]) +
-                   (g.n_slices > 3 && col >= g.col_off[3]);
-        };
-        auto pick_rank = [](const int4 &rk, int j) {
-            return j == 0 ? rk.x : j == 1 ? rk.y : j == 2 ? rk.z : rk.w;
-        };
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int m_row = m0 + wm * (BM / 2) + 16 * mi + li;   // this lane's row
-            const int vrow = min(m_row, max(a.n_delta, 1) - 1);    // a readable v row
-            // one pass per distinct slot among the group's 16 rows (lanes
-            // 0..15 hold them; usually one, as rows come grouped by adapter)
-            uint64_t pend = __builtin_amdgcn_ballot_w64(lane < 16 && ms[mi] != 0);
-            while (pend) {
-                const int lead = (int)__builtin_ctzll(pend);
-                const int s = __builtin_amdgcn_readlane(ms[mi], lead);
-                const bool in = ms[mi] == s;                      // this lane's row has slot s
-                pend &= ~__builtin_amdgcn_ballot_w64(lane < 16 && in);
-                int4 rk;
-                rk.x = __builtin_amdgcn_readlane(mrk[mi].x, lead);
-                rk.y = __builtin_amdgcn_readlane(mrk[mi].y, lead);
-                rk.z = __builtin_amdgcn_readlane(mrk[mi].z, lead);
-                rk.w = __builtin_amdgcn_readlane(mrk[mi].w, lead);
-                // per column group: its slice, whether it straddles a slice
-                // edge, and its B and v rows
-                int jn[NI], rn[NI];
-                bool mf[NI];
-                const uint16_t *bn[NI];
-                const float *vn[NI];
-                int rmax = 0;
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    const int c0 = n0 + wn * (BN / 2) + 16 * ni;    // the 16-column group
-                    const int j = slice_of(min(c0, a.N - 1));
-                    jn[ni] = j;
-                    mf[ni] = c0 < a.N && slice_of(min(c0 + 15, a.N - 1)) == j;
-                    rn[ni] = pick_rank(rk, j);
-                    rmax = max(rmax, mf[ni] ? rn[ni] : 0);
-                    bn[ni] = p.Bn + (int64_t)(s - 1) * g.bt_slot_stride + pick4(g.bt_slice_off, j) +
-                             (int64_t)(min(c0 + li, a.N - 1) - pick4(g.col_off, j)) * g.rank_pad;
-                    vn[ni] = a.v + (int64_t)vrow * g.v_stride + j * g.rank_pad;
-                }
-                // matrix cores: the prefill expand's chain per column group,
-                // B rows from the output-major copy (zero past the rank); each
-                // rank step's loads for every group are issued before its MFMAs
-                f32x4_t d[NI];
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) d[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                for (int ks = 0; ks * 32 < rmax; ++ks) {
-                    const int kk = 32 * ks + 8 * lg;
-                    const int kc = min(kk, g.rank_pad - 8);       // inside the row
-                    uint4 bv[NI];
-                    float4 va[NI], vb[NI];
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) {
-                        bv[ni] = ld16(bn[ni] + kc);
-                        va[ni] = *reinterpret_cast<const float4 *>(vn[ni] + kc);
-                        vb[ni] = *reinterpret_cast<const float4 *>(vn[ni] + kc + 4);
-                    }
-#pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) {
-                        if (!mf[ni] || ks * 32 >= rn[ni]) continue;   // uniform
-                        const float t[8] = {va[ni].x, va[ni].y, va[ni].z, va[ni].w,
-                                            vb[ni].x, vb[ni].y, vb[ni].z, vb[ni].w};
-                        float f[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) f[q] = (in && kk + q < rn[ni]) ? t[q] : 0.f;
-                        uint4 vhi, vlo;
-                        split_f32x8(f, vhi, vlo);
-                        d[ni] = mfma16x16x32(bv[ni], vhi, d[ni]);
-                        d[ni] = mfma16x16x32(bv[ni], vlo, d[ni]);
-                    }
-                }
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    const int c0 = n0 + wn * (BN / 2) + 16 * ni;
-                    if (!in || c0 >= a.N) continue;
-                    if (mf[ni]) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[ni][mi][q] += d[ni][q];
-                    } else {
-                        // a group across a slice edge: per output, an fp32 fma
-                        // chain over its slice's ranks from 0, then y = acc + d
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int o = c0 + 4 * lg + q;
-                            if (o >= a.N) continue;
-                            const int jq = slice_of(o);
-                            const int rank = pick_rank(rk, jq);
-                            const uint16_t *bt = p.Bt + (int64_t)(s - 1) * g.bt_slot_stride +
-                                                 pick4(g.bt_slice_off, jq) + (o - pick4(g.col_off, jq));
-                            const int hq = pick4(g.h_out, jq);
-                            const float *vq = a.v + (int64_t)vrow * g.v_stride + jq * g.rank_pad;
-                            float dq = 0.f;
-                            for (int k = 0; k < rank; ++k)
-                                dq = __builtin_fmaf(__uint_as_float((uint32_t)bt[(int64_t)k * hq] << 16),
-                                                    vq[k], dq);
-                            acc[ni][mi][q] += dq;
-                        }
-                    }
-                }
-            }
-        }
     }
 
     // Accumulator tile to LDS: lane holds, per (ni, mi), outputs

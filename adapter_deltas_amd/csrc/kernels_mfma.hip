@@ -89,10 +89,12 @@ __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1
 // the tiles' A rows coalesced (four consecutive lanes read one row's 64
 // bytes), and reorders them through the wave's own LDS into the MFMA operand
 // layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
+// vsplit > 0: v is written in the split form of the base projection's
+// epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int NG, int RT, bool GATHER>
 __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
-    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v)
+    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v, int vsplit)
 {
     touch_args(n_tasks, g, p, r, ldx);
     constexpr int D = kShrinkDepth, ROWS = 16 * RT;
@@ -251,7 +253,13 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
                 for (int w = 0; w < kShrinkParts; ++w) t[w] = red[w][orow][ok4 + i];
                 uf[i] = scale * ((t[0] + t[1]) + (t[2] + t[3]));
             }
-            *reinterpret_cast<float4 *>(vrow + 16 * nt) = u;
+            if (vsplit) {
+                const float four[4] = {u.x, u.y, u.z, u.w};
+                store_vsplit<4>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_chunks(g.rank_pad),
+                                sd.v_row() + rb + orow, j, 16 * (t0 + nt) + ok4, four);
+            } else {
+                *reinterpret_cast<float4 *>(vrow + 16 * nt) = u;
+            }
         }
     }
 }
@@ -503,39 +511,43 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
 template <int NG, int RT>
 static void launch_shrink_t(bool fp16, bool gather, dim3 grid, hipStream_t s, const LaneGeom &g,
                             const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
-                            const uint16_t *x, int64_t ldx, float *v)
+                            const uint16_t *x, int64_t ldx, float *v, int vsplit)
 {
     const dim3 block(64 * kShrinkParts);
     if (fp16 && gather)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
     else if (fp16)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
     else if (gather)
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
     else
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v);
+                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
 }
 
 template <int NG>
 static void launch_shrink_ng(int rt, bool fp16, bool gather, dim3 grid, hipStream_t s,
                              const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
-                             int seg_begin, int groups, const uint16_t *x, int64_t ldx, float *v)
+                             int seg_begin, int groups, const uint16_t *x, int64_t ldx, float *v,
+                             int vsplit)
 {
     if (rt == 1)
-        launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+        launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
+                               vsplit);
     else if (rt == 2)
-        launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+        launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
+                               vsplit);
     else
-        launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v);
+        launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
+                               vsplit);
 }
 
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
-                              const void *x, int64_t ldx, float *v, hipStream_t s)
+                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s)
 {
     if (n_seg <= 0) return hipSuccess;
     // Task shape: whole segments and up to 4 rank tiles (x and A read the
@@ -556,11 +568,14 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
     const dim3 grid((unsigned)blocks);
     const bool fp16 = g.x_fp16 != 0;
     if (ng == 1)
-        launch_shrink_ng<1>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+        launch_shrink_ng<1>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v,
+                                vsplit);
     else if (ng == 2)
-        launch_shrink_ng<2>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+        launch_shrink_ng<2>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v,
+                                vsplit);
     else
-        launch_shrink_ng<4>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v);
+        launch_shrink_ng<4>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v,
+                                vsplit);
     return hipGetLastError();
 }
 

@@ -254,10 +254,17 @@ int32_t join_streams(const lora_routing *r, const CallStreams &cs)
     return LORA_OK;
 }
 
+// bf16 values per active row of v in the base projection's split form.
+int linear_v_len(const lora_pool *p)
+{
+    return p->geom.n_slices * vsplit_chunks(p->geom.rank_pad) * 64;
+}
+
 // The kernels of each call.  With decode = false the decode segments are left
 // to the caller (the one-launch decode delta of lora_delta_apply).
+// vsplit > 0: v in the split form of the base projection (rows of vsplit bf16).
 int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x, int64_t ldx,
-                       float *v, const CallStreams &cs, bool decode = true)
+                       float *v, const CallStreams &cs, bool decode = true, int vsplit = 0)
 {
     hipStream_t s = cs.main;
     const lora_routing_info &I = r->info;
@@ -267,8 +274,8 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
     if (decode && I.n_decode_segments > 0) {
         // rank blocks of the GEMV slots only (higher-rank slots are gathered)
         const int kb = (gemv_max_rank(p, r) + kKBlock - 1) / kKBlock;
-        hipError_t e =
-            launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v, cs.dec);
+        hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v,
+                                          vsplit, cs.dec);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
     const int nt = (kmax + 15) / 16;
@@ -279,15 +286,15 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
         // from the table; the sums are the same).
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
                                           I.n_prefill_segments + I.n_gather_segments, nt, x,
-                                          ldx, v, s);
+                                          ldx, v, vsplit, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill + gather) launch");
     } else if (I.n_prefill_segments > 0) {
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, false, I.n_decode_segments,
-                                          I.n_prefill_segments, nt, x, ldx, v, s);
+                                          I.n_prefill_segments, nt, x, ldx, v, vsplit, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill) launch");
     } else if (I.n_gather_segments > 0) {
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
-                                          I.n_gather_segments, nt, x, ldx, v, s);
+                                          I.n_gather_segments, nt, x, ldx, v, vsplit, s);
         if (e != hipSuccess) return hip_fail(e, "shrink (gather) launch");
     }
     return LORA_OK;
@@ -1374,7 +1381,9 @@ int32_t lora_linear_workspace_bytes(const lora_pool *p, const lora_routing *r,
         *bytes_out = 0;
         return LORA_OK;
     }
-    return lora_workspace_bytes(p, r, bytes_out);
+    if (int32_t rc = check_pair(p, r)) return rc;
+    *bytes_out = round_up((int64_t)r->info.n_active * linear_v_len(p) * 2, 256);
+    return LORA_OK;
 }
 
 int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_rows,
@@ -1405,7 +1414,7 @@ int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_r
     float *v = static_cast<float *>(workspace);
     if (n_act > 0) {
         int64_t need = 0;
-        lora_workspace_bytes(p, r, &need);
+        lora_linear_workspace_bytes(p, r, &need);
         if (!workspace) return fail(LORA_ERR_ARG, "workspace is null");
         if (!aligned16(workspace))
             return fail(LORA_ERR_SHAPE, "workspace must be 16-byte aligned");
@@ -1415,10 +1424,11 @@ int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_r
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (n_act > 0) {
-        // v of the active rows, in the routing's order, by the shrink kernels
+        // v of the active rows, in the routing's order and the split bf16
+        // form the projection's delta K-tiles read, by the shrink kernels
         CallStreams cs;
         if (int32_t rc = fork_streams(r, st, cs)) return rc;
-        const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs);
+        const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs, true, linear_v_len(p));
         const int32_t rj = join_streams(r, cs);
         if (rc) return rc;
         if (rj) return rj;

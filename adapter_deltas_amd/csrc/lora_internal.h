@@ -62,6 +62,12 @@ struct LaneGeom {
     int64_t bt_slice_off[LORA_MAX_SLICES];
 };
 
+// v in the split form the base projection's delta K-tiles read: per row, per
+// slice, per chunk of 32 ranks, 32 bf16 values v_hi = bf16(v) and then 32 bf16
+// values v_lo = bf16(v - v_hi) (nearest even; v = v_hi + v_lo to about 16
+// significant bits).  A row is n_slices * vsplit_chunks(rank_pad) * 64 bf16.
+__host__ __device__ inline int vsplit_chunks(int rank_pad) { return (rank_pad + 31) / 32; }
+
 // Column tiles of tile_cols columns: slice j has ceil(h_out[j] / tile_cols) of
 // them (slices past n_slices have width 0, so none), and the tiles of a
 // segment are numbered slice after slice.  Tiles of the lane per segment:
@@ -124,7 +130,7 @@ hipError_t launch_linear(const LaneGeom &g, const PoolDev &p, const LinearArgs &
                          hipStream_t s);
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
-                              float *v, hipStream_t s);
+                              float *v, int vsplit, hipStream_t s);
 hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                              int n_seg, const void *x, int64_t ldx, float *y, int64_t ldy,
                              hipStream_t s);
@@ -133,7 +139,7 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
                               float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
-                              const void *x, int64_t ldx, float *v, hipStream_t s);
+                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int group, int max_rank,
                               int max_seg_rows, const float *v, float *y, int64_t ldy,

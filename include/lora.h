@@ -486,13 +486,16 @@ int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
  *            GPU's h_in input columns), 16-byte aligned, ldw >= h_in, % 8 == 0
  *   x, y     as lora_delta_apply; the lane's x must be bf16
  *   workspace  device memory of lora_linear_workspace_bytes bytes (v of the
- *            active rows), ignored when routing is NULL
+ *            active rows as bf16 pairs v_hi + v_lo per rank, about 16
+ *            significant bits), ignored when routing is NULL
  *
  * Sums: each output is a chain of 32-element matrix-core steps over h_in in
- * ascending order from zero; the delta is an fp32 fma chain over the
- * adapter's ranks from zero, then y = product + delta.  So on a decode row
- * the result is bit-identical to lora_delta_apply applied to the result of
- * this call with routing NULL.  Errors: ARG (null pool, W or buffers; a
+ * ascending order from zero, continued over the delta's terms in the same
+ * accumulator: per 32-rank chunk of the row's slice, B times v_hi, then B
+ * times v_lo, with zeros for the terms of other rows' adapters.  A row's bits
+ * depend on its own x row, W and adapter only (not on the other rows of the
+ * batch), and base rows equal the product of a call with routing NULL.
+ * Errors: ARG (null pool, W or buffers; a
  * routing built on the device), SHAPE (n_rows != the routing's rows, widths,
  * strides, alignment), DTYPE (fp16 lane), MISMATCH, CAPACITY (workspace), HIP.
  */

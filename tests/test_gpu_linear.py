@@ -5,9 +5,8 @@ y = x W^T for every row, plus the delta of each adapter row added to the
 accumulator before the one store.  Real inputs are held to the tolerance rule
 of tests/harness.py (with y0 = 0, so the rule applies to y itself), integer
 inputs must be exact; base rows must equal the same kernel's base product bit
-for bit, and on rows the routing sends to the matrix cores the result must
-equal lora_delta_apply applied to that base product, bit for bit (the epilogue
-adds the delta with the prefill expand's arithmetic).
+for bit, and with W = 0 the result is the delta alone, held to the same rule
+(so a wrong delta cannot hide under a large base product).
 """
 import numpy as np
 import pytest
@@ -112,22 +111,21 @@ def test_linear_matches_oracle(lib, cfg, lane, mode):
 
 
 @pytest.mark.parametrize("mode", ["real", "int"])
-@pytest.mark.parametrize("cfg,lane", [("decode_mix", "qkv"), ("high_rank", "wide")])
-def test_linear_equals_delta_apply_on_its_base_product(lib, cfg, lane, mode):
-    """Rows on the matrix-core path (prefill_min_len = 1 sends every sequence
-    there): lora_linear_delta == lora_delta_apply(base product), bit for bit,
-    since the epilogue adds the delta with the prefill expand's arithmetic."""
-    import torch
-    spec = HIGH_RANK if cfg == "high_rank" else config_by_name(cfg)
-    w = generate(spec, mode=mode)
-    W = draw_base_weight(spec, 0, spec.lanes[0], mode=mode)
-    y, info, pool, routing = run_linear(lib, w, lane, W, prefill_min_len=1)
-    assert info["n_decode_segments"] == 0 and info["n_prefill_segments"] > 0
-    yb, _, _, _ = run_linear(lib, w, lane, W, with_routing=False, pool=pool)
-    yt = torch.from_numpy(yb).cuda()
-    lib.delta_apply(pool, routing, to_device_x(w.lanes[lane].x), yt)
-    torch.cuda.synchronize()
-    assert np.array_equal(y.view(np.uint32), yt.cpu().numpy().view(np.uint32))
+@pytest.mark.parametrize("cfg,lane,pml", [("decode_mix", "qkv", 64), ("high_rank", "wide", 1),
+                                          ("ragged", "qkv_like", 64)])
+def test_linear_zero_weight_gives_the_delta(lib, cfg, lane, pml, mode):
+    """W = 0: every row is its delta alone (zero on base rows), against the
+    oracle's delta on every row; prefill_min_len = 1 sends every sequence to
+    the matrix-core shrink."""
+    spec = {"ragged": RAGGED, "high_rank": HIGH_RANK}.get(cfg) or config_by_name(cfg)
+    w = generate(spec, mode=mode, lanes=(lane,))
+    li = [l.name for l in spec.lanes].index(lane)
+    W = np.zeros((spec.lanes[li].h_out_total, spec.lanes[li].h_in), dtype=np.uint16)
+    y, info, _, _ = run_linear(lib, w, lane, W, prefill_min_len=pml)
+    if pml == 1:
+        assert info["n_decode_segments"] == 0 and info["n_prefill_segments"] > 0
+    tok = check_against_oracle(w, lane, W, y)
+    assert np.all(y[tok == 0] == 0)
 
 
 def test_linear_permutation_and_solo_bit_exact(lib):
