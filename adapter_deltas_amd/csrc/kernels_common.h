@@ -127,19 +127,19 @@ __device__ __forceinline__ bool decode_seg(const RoutingDev &r, int si, Seg &sd)
     return si < n_dec && sd.n_rows() > 0;
 }
 
-// v in the split form (vsplit_chunks) is written by store_vsplit.
+// v in the split form (vsplit_groups) is written by store_vsplit.
 __device__ __forceinline__ uint16_t bf16_rne(float f)
 {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Stores n (1 or 4) consecutive ranks k .. k + n - 1 (within one chunk) of
-// row p, slice j.
+// Stores n (1 or 4) consecutive ranks k .. k + n - 1 (within one group of 16)
+// of row p, slice j; a row holds row_len bf16.
 template <int N>
-__device__ __forceinline__ void store_vsplit(uint16_t *vs, int row_len, int chunks, int p, int j,
+__device__ __forceinline__ void store_vsplit(uint16_t *vs, int row_len, int groups, int p, int j,
                                              int k, const float (&val)[N])
 {
-    uint16_t *at = vs + (int64_t)p * row_len + (j * chunks + k / 32) * 64 + k % 32;
+    uint16_t *at = vs + (int64_t)p * row_len + (j * groups + k / 16) * 32 + k % 16;
     uint16_t hi[N], lo[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -149,11 +149,11 @@ __device__ __forceinline__ void store_vsplit(uint16_t *vs, int row_len, int chun
     if constexpr (N == 4) {
         *reinterpret_cast<uint2 *>(at) =
             make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-        *reinterpret_cast<uint2 *>(at + 32) =
+        *reinterpret_cast<uint2 *>(at + 16) =
             make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
     } else {
         at[0] = hi[0];
-        at[32] = lo[0];
+        at[16] = lo[0];
     }
 }
 

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
             const float val = scale * (q0 + q1);
             if (vsplit) {
                 const float one[1] = {val};
-                store_vsplit<1>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_chunks(g.rank_pad),
+                store_vsplit<1>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_groups(g.rank_pad),
                                 sd.v_row() + c, j, k0 + k, one);
             } else {
                 v[(int64_t)(sd.v_row() + c) * g.v_stride + j * g.rank_pad + k0 + k] = val;

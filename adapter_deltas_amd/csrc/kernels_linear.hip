@@ -12,12 +12,13 @@
 //           consecutive output features (4 (l / 16) .. + 3) of one row
 //           (l % 16) and stores them as one 16-byte write.  Each output sums
 //           its K-steps of 32 in ascending order, from zero.
-// Delta:    as K-tiles after the product's, in the same accumulator: per
-//           distinct slot of the tile's rows, slice and 32-rank chunk, B rows
-//           times v_hi, then B rows times v_lo (v = v_hi + v_lo, both bf16,
-//           written so by the shrink), with every other row, column and rank
-//           read as zero.  Each output sums its own product terms, then its own
-//           delta terms, in a fixed order, plus exact zeros.
+// Delta:    as K-steps after the product's, in the same accumulator: per
+//           distinct slot of the tile's rows, slice and group of 16 ranks,
+//           one 32-wide step of B rows against (v_hi, v_lo) of those ranks
+//           (v = v_hi + v_lo, both bf16, written so by the shrink), with every
+//           other row, column and rank read as zero.  Each output sums its own
+//           product terms, then its own delta steps in a fixed order, plus
+//           steps of exact zeros.
 // A row's bits depend on its own x row, W and its adapter only.
 #include "kernels_common.h"
 
@@ -56,16 +57,15 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 // one of two LDS buffers, with its masks applied.  The loop is branch-free: it
 // runs a multiple of D tiles, and a tile past the last loads zeros.
 //
-// The delta, as K-tiles after the product's: for each distinct slot s among
+// The delta, as K-steps after the product's: for each distinct slot s among
 // the tile's rows (ascending), each slice j the tile's columns touch and each
-// chunk c of 32 ranks (as many as the largest rank among those slots and
-// slices needs), one tile whose W rows are B[s][j][o][32 c ..] (output-major,
-// zero past the rank; the same 32 ranks in both halves of the tile) and whose
-// x rows are v_hi of ranks 32 c .. in its first half and v_lo in its second,
-// from the split v the shrink wrote.  A row of another slot, a column of
-// another slice and a rank past the slot's rank read as zero, so each
-// output's sum gets exactly its own row's delta terms, in a fixed order, and
-// exact zeros from the rest.
+// group k of 16 ranks the slot has on that slice, one step of 32: W rows
+// B[s][j][o][16 k ..] (output-major) for both halves, x rows v_hi of those
+// ranks in the first half and v_lo in the second, from the split v the shrink
+// wrote.  Two steps make a K-tile.  A row of another slot, a column of another
+// slice and a rank past the slot's rank read as zero, so each output's sum
+// gets exactly its own row's delta terms, always at the same positions of the
+// same steps whatever the other rows are, and exact zeros from the rest.
 constexpr int kGroupM = 8;
 
 __device__ __forceinline__ void tile_of(int task, int n_tiles, int m_tiles, int &tn, int &tm)
@@ -111,7 +111,7 @@ __device__ __forceinline__ uint4 keep_first(uint4 w, int n_ok)
 }
 
 template <int BN, int BM, bool DELTA>
-__global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, LinearArgs a,
+__global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, LinearArgs a,
                                                       int n_tasks, int n_tiles, int m_tiles)
 {
     constexpr int NI = BN / 32, MI = BM / 32;              // 16-wide tiles per wave
@@ -175,14 +175,27 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     }
     const int KT = (a.K + kBK - 1) / kBK;
 
-    // Delta tiles: the tile's slices [j_lo, j_hi], distinct slots, chunks.
+    uint4 st[D][NL];
+    // Product tiles: loads read a clamped address; masks are applied when a
+    // set is written to LDS, so nothing waits for a load before it is needed.
+    auto load_base = [&](uint4 (&dst)[NL], int kt) __attribute__((always_inline)) {
+        const int ec = min(kt * kBK + lc * 8, a.K - 8);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) dst[i] = ld16(src[i] + ec);
+    };
+    // The first product tiles are in flight while the slots are found.
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < KT) load_base(st[d], d);
+
+    // Delta steps of the tile: its slices [j_lo, j_hi], distinct slots, and
+    // per (slot, slice) one step per 16 ranks.
     auto slice_of = [&](int col) __attribute__((always_inline)) {
         return (g.n_slices > 1 && col >= g.col_off[1]) + (g.n_slices > 2 && col >= g.col_off[2]) +
                (g.n_slices > 3 && col >= g.col_off[3]);
     };
     const int j_lo = slice_of(n0), j_hi = slice_of(min(n0 + BN - 1, a.N - 1));
-    const int ns = j_hi - j_lo + 1;
-    int n_dist = 0, nchk = 1;
+    int n_dist = 0, n_steps = 0;
     if constexpr (DELTA) {
         if (wave == 0) {
             // each lane holds the slots and ranks of rows lane and lane + 64
@@ -200,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
                 }
             }
             // the distinct nonzero slots, ascending, by repeated minimum
-            int last = 0, n = 0, rmax = 0;
+            int last = 0, n = 0, steps = 0;
             for (;;) {
                 const int c = wave_min(min(sa > last ? sa : INT32_MAX, sb > last ? sb : INT32_MAX));
                 if (c == INT32_MAX) break;
@@ -220,23 +233,23 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
                     d_slot[n] = c;
                     d_rk[n] = rk;
                 }
-                for (int j = j_lo; j <= j_hi; ++j) rmax = max(rmax, pick_rank(rk, j));
+                for (int j = j_lo; j <= j_hi; ++j) steps += (pick_rank(rk, j) + 15) / 16;
                 ++n;
                 last = c;
             }
             if (lane == 0) {
                 d_count[0] = n;
-                d_count[1] = rmax;
+                d_count[1] = steps;
             }
         }
         __syncthreads();
         n_dist = __builtin_amdgcn_readfirstlane(d_count[0]);
-        nchk = max(1, (__builtin_amdgcn_readfirstlane(d_count[1]) + 31) / 32);
+        n_steps = __builtin_amdgcn_readfirstlane(d_count[1]);
     }
-    const int T_d = n_dist * ns * nchk;      // delta K-tiles (0 without a delta)
+    const int T_d = (n_steps + 1) / 2;       // delta K-tiles, two steps each
     const int KT_all = KT + T_d;
-    const int C = vsplit_chunks(g.rank_pad);
-    const int vs_len = g.n_slices * C * 64;
+    const int G = vsplit_groups(g.rank_pad);
+    const int vs_len = g.n_slices * G * 32;
     const uint16_t *vs = reinterpret_cast<const uint16_t *>(a.v);
 
     // per-slice widths and offsets, selected by slice below
@@ -247,38 +260,70 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     auto sel = [](int j, auto v0, auto v1, auto v2, auto v3) __attribute__((always_inline)) {
         return j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3;
     };
-    auto h_of = [&](int j) __attribute__((always_inline)) { return sel(j, hj_[0], hj_[1], hj_[2], hj_[3]); };
-    auto c_of = [&](int j) __attribute__((always_inline)) { return sel(j, cj_[0], cj_[1], cj_[2], cj_[3]); };
-    auto b_of = [&](int j) __attribute__((always_inline)) { return sel(j, bo_[0], bo_[1], bo_[2], bo_[3]); };
 
-    // delta tile t: slot index d, slice j, chunk c
-    struct DTile { int s, j, c, rank; };
-    auto dtile = [&](int t) __attribute__((always_inline)) {
-        DTile dt;
-        const int per_d = ns * nchk;
-        const int d = t / per_d;
-        const int rem = t - d * per_d;
-        dt.j = j_lo + rem / nchk;
-        dt.c = rem - (rem / nchk) * nchk;
-        dt.s = __builtin_amdgcn_readfirstlane(d_slot[d]);
-        dt.rank = __builtin_amdgcn_readfirstlane(pick_rank(d_rk[d], dt.j));
-        return dt;
+    // A step (slot index d, slice j, 16-rank group k); past the last one
+    // d == n_dist.  Steps are walked in order by two cursors, one for the
+    // loads and one for the moves to LDS, each wave-uniform.
+    struct Step { int d, j, k, n_k, rank, s; };
+    auto enter = [&](Step &c) __attribute__((always_inline)) {
+        // from (d, j) with k = 0 to the first (slot, slice) that has ranks
+        while (c.d < n_dist) {
+            c.rank = __builtin_amdgcn_readfirstlane(pick_rank(d_rk[c.d], c.j));
+            c.n_k = (c.rank + 15) / 16;
+            if (c.n_k > 0) break;
+            if (++c.j > j_hi) {
+                c.j = j_lo;
+                ++c.d;
+            }
+        }
+        c.s = c.d < n_dist ? __builtin_amdgcn_readfirstlane(d_slot[c.d]) : 0;
+    };
+    auto next = [&](Step &c) __attribute__((always_inline)) {
+        if (++c.k >= c.n_k) {
+            c.k = 0;
+            if (++c.j > j_hi) {
+                c.j = j_lo;
+                ++c.d;
+            }
+            enter(c);
+        }
+    };
+    Step lcur{0, j_lo, 0, 0, 0, 0}, scur{0, j_lo, 0, 0, 0, 0};
+    if constexpr (DELTA) {
+        enter(lcur);
+        scur = lcur;
+    }
+    // This thread's 16 bytes of a delta tile: step h of the two, chunk q of
+    // the step's four (ranks 8 (q & 1) .., v_hi for q < 2, v_lo after).
+    const int h = lc >> 2, q = lc & 3;
+    // The two steps of the tile a cursor is on; advances the cursor past them.
+    auto take = [&](Step &c) __attribute__((always_inline)) {
+        const Step s0 = c;
+        next(c);
+        const Step s1 = c;
+        next(c);
+        Step r;
+        r.d = h ? s1.d : s0.d;
+        r.j = h ? s1.j : s0.j;
+        r.k = h ? s1.k : s0.k;
+        r.rank = h ? s1.rank : s0.rank;
+        r.s = h ? s1.s : s0.s;
+        r.n_k = 0;
+        return r;
     };
 
-    uint4 st[D][NL];
-    // Loads read a clamped address; masks are applied when a set is written
-    // to LDS, so nothing waits for a load before it is needed.
     auto load = [&](uint4 (&dst)[NL], int kt) __attribute__((always_inline)) {
         if (kt < KT || kt >= KT_all) {           // the product's tile (or past the last)
-            const int ec = min(kt * kBK + lc * 8, a.K - 8);
-#pragma unroll
-            for (int i = 0; i < NL; ++i) dst[i] = ld16(src[i] + ec);
+            load_base(dst, kt);
         } else {
-            const DTile dt = dtile(kt - KT);
-            const int hj = h_of(dt.j), cj = c_of(dt.j);
-            const uint16_t *bn = p.Bn + (int64_t)(dt.s - 1) * g.bt_slot_stride + b_of(dt.j) +
-                                 min(32 * dt.c + 8 * (lc & 3), g.rank_pad - 8);
-            const uint16_t *vc = vs + (dt.j * C + dt.c) * 64 + 8 * lc;
+            const Step dt = take(lcur);
+            const int hj = sel(dt.j, hj_[0], hj_[1], hj_[2], hj_[3]);
+            const int cj = sel(dt.j, cj_[0], cj_[1], cj_[2], cj_[3]);
+            const int64_t bo = sel(dt.j, bo_[0], bo_[1], bo_[2], bo_[3]);
+            // past the last step: any slot's address (the move writes zeros)
+            const uint16_t *bn = p.Bn + (int64_t)(max(dt.s, 1) - 1) * g.bt_slot_stride + bo +
+                                 16 * dt.k + 8 * (q & 1);
+            const uint16_t *vc = vs + (dt.j * G + dt.k) * 32 + 8 * q;
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 const int r = lrow[i];
@@ -299,9 +344,11 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
             for (int i = 0; i < NL; ++i)
                 lds[buf][lrow[i]][swz(lrow[i], lc)] = keep_if(from[i], ok);
         } else if (kt < KT_all) {
-            const DTile dt = dtile(kt - KT);
-            const int hj = h_of(dt.j), cj = c_of(dt.j);
-            const int kb = 32 * dt.c + 8 * (lc & 3);      // first rank of this chunk
+            const Step dt = take(scur);
+            const int hj = sel(dt.j, hj_[0], hj_[1], hj_[2], hj_[3]);
+            const int cj = sel(dt.j, cj_[0], cj_[1], cj_[2], cj_[3]);
+            const int kb = 16 * dt.k + 8 * (q & 1);        // first rank of this chunk
+            const bool live = dt.d < n_dist;
             const int n_ok = min(max(dt.rank - kb, 0), 8);
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -309,10 +356,10 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
                 uint4 w;
                 if (r < BN) {
                     const int ol = n0 + r - cj;
-                    const bool ok = n0 + r < a.N && ol >= 0 && ol < hj && kb < g.rank_pad;
+                    const bool ok = live && n0 + r < a.N && ol >= 0 && ol < hj && kb < dt.rank;
                     w = keep_if(from[i], ok);
                 } else {
-                    const bool ok = m0 + r - BN < a.n_delta && xslot[i] == dt.s;
+                    const bool ok = live && m0 + r - BN < a.n_delta && xslot[i] == dt.s;
                     w = keep_first(from[i], ok ? n_ok : 0);
                 }
                 lds[buf][r][swz(r, lc)] = w;
@@ -357,9 +404,24 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
     // Register set kt % D holds K-tile kt from its load until its move to LDS;
     // the loop is unrolled by D so every set is named at compile time.
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(st[d], d);
+    for (int d = 0; d < D; ++d)
+        if (d >= KT) load(st[d], d);
     store(st[0], 0, 0);
     __syncthreads();
+    // Product iterations whose loads and moves are all product tiles run a
+    // loop with no branch in it; the last ones and the delta tiles follow.
+    auto step_base = [&](auto slot, int kt) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        load_base(st[S], kt + D);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kt & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool ok = (kt + 1) * kBK + lc * 8 < a.K;
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            lds[(kt + 1) & 1][lrow[i]][swz(lrow[i], lc)] = keep_if(st[(S + 1) % D][i], ok);
+        __syncthreads();
+    };
     auto step = [&](auto slot, int kt) __attribute__((always_inline)) {
         constexpr int S = decltype(slot)::value;
         load(st[S], kt + D);
@@ -369,8 +431,14 @@ __global__ __launch_bounds__(kThreads) void k_linear(LaneGeom g, PoolDev p, Line
         store(st[(S + 1) % D], kt + 1, (kt + 1) & 1);
         __syncthreads();
     };
+    int kt = 0;
+    for (; kt + 2 * D <= KT; kt += D) {
+        step_base(std::integral_constant<int, 0>{}, kt);
+        step_base(std::integral_constant<int, 1>{}, kt + 1);
+        if constexpr (D > 2) step_base(std::integral_constant<int, 2>{}, kt + 2);
+    }
     const int KTD = (KT_all + D - 1) / D * D;
-    for (int kt = 0; kt < KTD; kt += D) {
+    for (; kt < KTD; kt += D) {
         step(std::integral_constant<int, 0>{}, kt);
         step(std::integral_constant<int, 1>{}, kt + 1);
         if constexpr (D > 2) step(std::integral_constant<int, 2>{}, kt + 2);

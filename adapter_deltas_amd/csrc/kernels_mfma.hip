@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
             }
             if (vsplit) {
                 const float four[4] = {u.x, u.y, u.z, u.w};
-                store_vsplit<4>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_chunks(g.rank_pad),
+                store_vsplit<4>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_groups(g.rank_pad),
                                 sd.v_row() + rb + orow, j, 16 * (t0 + nt) + ok4, four);
             } else {
                 *reinterpret_cast<float4 *>(vrow + 16 * nt) = u;

@@ -257,7 +257,7 @@ int32_t join_streams(const lora_routing *r, const CallStreams &cs)
 // bf16 values per active row of v in the base projection's split form.
 int linear_v_len(const lora_pool *p)
 {
-    return p->geom.n_slices * vsplit_chunks(p->geom.rank_pad) * 64;
+    return p->geom.n_slices * vsplit_groups(p->geom.rank_pad) * 32;
 }
 
 // The kernels of each call.  With decode = false the decode segments are left

@@ -62,11 +62,11 @@ struct LaneGeom {
     int64_t bt_slice_off[LORA_MAX_SLICES];
 };
 
-// v in the split form the base projection's delta K-tiles read: per row, per
-// slice, per chunk of 32 ranks, 32 bf16 values v_hi = bf16(v) and then 32 bf16
+// v in the split form the base projection's delta K-steps read: per row, per
+// slice, per group of 16 ranks, 16 bf16 values v_hi = bf16(v) and then 16 bf16
 // values v_lo = bf16(v - v_hi) (nearest even; v = v_hi + v_lo to about 16
-// significant bits).  A row is n_slices * vsplit_chunks(rank_pad) * 64 bf16.
-__host__ __device__ inline int vsplit_chunks(int rank_pad) { return (rank_pad + 31) / 32; }
+// significant bits).  A row is n_slices * vsplit_groups(rank_pad) * 32 bf16.
+__host__ __device__ inline int vsplit_groups(int rank_pad) { return (rank_pad + 15) / 16; }
 
 // Column tiles of tile_cols columns: slice j has ceil(h_out[j] / tile_cols) of
 // them (slices past n_slices have width 0, so none), and the tiles of a
