@@ -85,6 +85,13 @@ __device__ __forceinline__ int wave_min(int v)
     return v;
 }
 
+// One delta step in a word: slot (17 bits), slice j (2), 16-rank group k (4),
+// the slot's rank on slice j (9 bits, <= 256).
+__device__ __forceinline__ uint32_t step_word(int slot, int j, int k, int rank)
+{
+    return (uint32_t)slot | ((uint32_t)j << 17) | ((uint32_t)k << 19) | ((uint32_t)rank << 23);
+}
+
 __device__ __forceinline__ int pick_rank(const int4 &rk, int j)
 {
     return j == 0 ? rk.x : j == 1 ? rk.y : j == 2 ? rk.z : rk.w;
@@ -130,10 +137,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
                                                                          : kTileBytes];
     uint4(*const lds)[ROWS][kChunks] = reinterpret_cast<uint4(*)[ROWS][kChunks]>(smem);
     float(*const tile)[LDT] = reinterpret_cast<float(*)[LDT]>(smem);
-    // the tile's distinct slots and their ranks (delta)
-    __shared__ int d_slot[DELTA ? BM : 1];
-    __shared__ int4 d_rk[DELTA ? BM : 1];
-    __shared__ int d_count[2];
+    // the tile's delta steps (see step_word), and their count
+    __shared__ uint32_t d_step[DELTA ? kLinearMaxSteps : 1];
+    __shared__ int d_count;
 
     int tn, tm;
     tile_of(xcd_task(blockIdx.x, n_tasks), n_tiles, m_tiles, tn, tm);
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
             const int t = a.rows ? a.rows[m] : m;
             src[i] = a.x + (int64_t)t * a.ldx;
             if constexpr (DELTA)
-                if (m0 + r - BN < a.n_delta) xslot[i] = a.tok_slot[t];
+                if (m0 + r - BN < a.n_delta) xslot[i] = a.row_meta[4 * (m0 + r - BN)];
         }
     }
     const int KT = (a.K + kBK - 1) / kBK;
@@ -195,25 +201,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
                (g.n_slices > 3 && col >= g.col_off[3]);
     };
     const int j_lo = slice_of(n0), j_hi = slice_of(min(n0 + BN - 1, a.N - 1));
-    int n_dist = 0, n_steps = 0;
+    int n_steps = 0;
     if constexpr (DELTA) {
         if (wave == 0) {
-            // each lane holds the slots and ranks of rows lane and lane + 64
+            // each lane holds the slots and ranks of rows lane and lane + 64,
+            // from the routing's per-row table (one load each)
             int sa = 0, sb = 0;
             int4 ra = make_int4(0, 0, 0, 0), rb = make_int4(0, 0, 0, 0);
+            auto unpack = [](int4 w, int &slot, int4 &rk) {
+                slot = w.x;
+                rk = make_int4(w.y & 0xffff, (int)((uint32_t)w.y >> 16), w.z & 0xffff,
+                               (int)((uint32_t)w.z >> 16));
+            };
             {
                 const int ma = m0 + lane, mb = m0 + lane + 64;
-                if (lane < BM && ma < a.n_delta) {
-                    sa = a.tok_slot[a.rows ? a.rows[ma] : ma];
-                    ra = *reinterpret_cast<const int4 *>(p.rank + sa * kMetaStride);
-                }
-                if (lane + 64 < BM && mb < a.n_delta) {
-                    sb = a.tok_slot[a.rows ? a.rows[mb] : mb];
-                    rb = *reinterpret_cast<const int4 *>(p.rank + sb * kMetaStride);
-                }
+                if (lane < BM && ma < a.n_delta)
+                    unpack(*reinterpret_cast<const int4 *>(a.row_meta + 4 * ma), sa, ra);
+                if (lane + 64 < BM && mb < a.n_delta)
+                    unpack(*reinterpret_cast<const int4 *>(a.row_meta + 4 * mb), sb, rb);
             }
-            // the distinct nonzero slots, ascending, by repeated minimum
-            int last = 0, n = 0, steps = 0;
+            // the distinct nonzero slots, ascending, by repeated minimum; the
+            // steps of each are written at once, lane l writing its step l
+            int last = 0, base = 0;
             for (;;) {
                 const int c = wave_min(min(sa > last ? sa : INT32_MAX, sb > last ? sb : INT32_MAX));
                 if (c == INT32_MAX) break;
@@ -229,22 +238,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
                     rk = make_int4(__builtin_amdgcn_readlane(rb.x, l), __builtin_amdgcn_readlane(rb.y, l),
                                    __builtin_amdgcn_readlane(rb.z, l), __builtin_amdgcn_readlane(rb.w, l));
                 }
-                if (lane == 0) {
-                    d_slot[n] = c;
-                    d_rk[n] = rk;
+                // lane l: step l of this slot (slice j, group k), at most 4 x 16
+                int rest = lane, j = -1, k = 0, rank = 0;
+                for (int jj = j_lo; jj <= j_hi; ++jj) {
+                    const int rj = pick_rank(rk, jj), nk = (rj + 15) / 16;
+                    if (j < 0 && rest < nk) {
+                        j = jj;
+                        k = rest;
+                        rank = rj;
+                    }
+                    rest -= nk;
                 }
-                for (int j = j_lo; j <= j_hi; ++j) steps += (pick_rank(rk, j) + 15) / 16;
-                ++n;
+                if (j >= 0 && base + lane < kLinearMaxSteps)
+                    d_step[base + lane] = step_word(c, j, k, rank);
+                for (int jj = j_lo; jj <= j_hi; ++jj) base += (pick_rank(rk, jj) + 15) / 16;
                 last = c;
             }
-            if (lane == 0) {
-                d_count[0] = n;
-                d_count[1] = steps;
-            }
+            if (lane == 0) d_count = min(base, kLinearMaxSteps);
         }
         __syncthreads();
-        n_dist = __builtin_amdgcn_readfirstlane(d_count[0]);
-        n_steps = __builtin_amdgcn_readfirstlane(d_count[1]);
+        n_steps = __builtin_amdgcn_readfirstlane(d_count);
     }
     const int T_d = (n_steps + 1) / 2;       // delta K-tiles, two steps each
     const int KT_all = KT + T_d;
@@ -261,66 +274,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
         return j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3;
     };
 
-    // A step (slot index d, slice j, 16-rank group k); past the last one
-    // d == n_dist.  Steps are walked in order by two cursors, one for the
-    // loads and one for the moves to LDS, each wave-uniform.
-    struct Step { int d, j, k, n_k, rank, s; };
-    auto enter = [&](Step &c) __attribute__((always_inline)) {
-        // from (d, j) with k = 0 to the first (slot, slice) that has ranks
-        while (c.d < n_dist) {
-            c.rank = __builtin_amdgcn_readfirstlane(pick_rank(d_rk[c.d], c.j));
-            c.n_k = (c.rank + 15) / 16;
-            if (c.n_k > 0) break;
-            if (++c.j > j_hi) {
-                c.j = j_lo;
-                ++c.d;
-            }
-        }
-        c.s = c.d < n_dist ? __builtin_amdgcn_readfirstlane(d_slot[c.d]) : 0;
-    };
-    auto next = [&](Step &c) __attribute__((always_inline)) {
-        if (++c.k >= c.n_k) {
-            c.k = 0;
-            if (++c.j > j_hi) {
-                c.j = j_lo;
-                ++c.d;
-            }
-            enter(c);
-        }
-    };
-    Step lcur{0, j_lo, 0, 0, 0, 0}, scur{0, j_lo, 0, 0, 0, 0};
-    if constexpr (DELTA) {
-        enter(lcur);
-        scur = lcur;
-    }
-    // This thread's 16 bytes of a delta tile: step h of the two, chunk q of
+    // This thread's 16 bytes of a delta tile: step h of its two, chunk q of
     // the step's four (ranks 8 (q & 1) .., v_hi for q < 2, v_lo after).
+    // Past the last step: slot 0 (reads any valid address, moves zeros).
     const int h = lc >> 2, q = lc & 3;
-    // The two steps of the tile a cursor is on; advances the cursor past them.
-    auto take = [&](Step &c) __attribute__((always_inline)) {
-        const Step s0 = c;
-        next(c);
-        const Step s1 = c;
-        next(c);
-        Step r;
-        r.d = h ? s1.d : s0.d;
-        r.j = h ? s1.j : s0.j;
-        r.k = h ? s1.k : s0.k;
-        r.rank = h ? s1.rank : s0.rank;
-        r.s = h ? s1.s : s0.s;
-        r.n_k = 0;
-        return r;
+    struct Step { int s, j, k, rank; };
+    auto step_of = [&](int kt) __attribute__((always_inline)) {
+        const int si = 2 * (kt - KT) + h;
+        const uint32_t w = si < n_steps ? d_step[si] : 0u;
+        return Step{(int)(w & 0x1ffffu), (int)((w >> 17) & 3u), (int)((w >> 19) & 15u),
+                    (int)(w >> 23)};
     };
 
     auto load = [&](uint4 (&dst)[NL], int kt) __attribute__((always_inline)) {
         if (kt < KT || kt >= KT_all) {           // the product's tile (or past the last)
             load_base(dst, kt);
         } else {
-            const Step dt = take(lcur);
+            const Step dt = step_of(kt);
             const int hj = sel(dt.j, hj_[0], hj_[1], hj_[2], hj_[3]);
             const int cj = sel(dt.j, cj_[0], cj_[1], cj_[2], cj_[3]);
             const int64_t bo = sel(dt.j, bo_[0], bo_[1], bo_[2], bo_[3]);
-            // past the last step: any slot's address (the move writes zeros)
             const uint16_t *bn = p.Bn + (int64_t)(max(dt.s, 1) - 1) * g.bt_slot_stride + bo +
                                  16 * dt.k + 8 * (q & 1);
             const uint16_t *vc = vs + (dt.j * G + dt.k) * 32 + 8 * q;
@@ -344,11 +317,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
             for (int i = 0; i < NL; ++i)
                 lds[buf][lrow[i]][swz(lrow[i], lc)] = keep_if(from[i], ok);
         } else if (kt < KT_all) {
-            const Step dt = take(scur);
+            const Step dt = step_of(kt);
             const int hj = sel(dt.j, hj_[0], hj_[1], hj_[2], hj_[3]);
             const int cj = sel(dt.j, cj_[0], cj_[1], cj_[2], cj_[3]);
             const int kb = 16 * dt.k + 8 * (q & 1);        // first rank of this chunk
-            const bool live = dt.d < n_dist;
+            const bool live = dt.s != 0;
             const int n_ok = min(max(dt.rank - kb, 0), 8);
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
@@ -488,22 +461,30 @@ void launch_t(const LaneGeom &g, const PoolDev &p, const LinearArgs &a, hipStrea
                            p, a, n_tasks, n_tiles, m_tiles);
 }
 
+
+// The largest tile that still gives the chip at least two workgroups per
+// CU; small batches (decode) take 64 x 64 tiles.
+constexpr int64_t kWantTasks = 512;
+int64_t linear_tasks(int64_t M, int64_t N, int bn, int bm)
+{
+    return ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+}
+
 }  // namespace
+
+int linear_tile_rows(int64_t M, int64_t N)
+{
+    return linear_tasks(M, N, 128, 128) >= kWantTasks ? 128 : 64;
+}
 
 hipError_t launch_linear(const LaneGeom &g, const PoolDev &p, const LinearArgs &a,
                          hipStream_t s)
 {
     if (a.M <= 0) return hipSuccess;
     if (a.K < 8 || a.K % 8 || a.N < 8 || a.N % 8) return hipErrorInvalidValue;
-    // The largest tile that still gives the chip at least two workgroups per
-    // CU; small batches (decode) take 64 x 64 tiles.
-    auto tasks = [&](int bn, int bm) {
-        return (int64_t)((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm);
-    };
-    constexpr int64_t kWant = 512;
-    if (tasks(64, 64) > INT32_MAX) return hipErrorInvalidConfiguration;
-    if (tasks(128, 128) >= kWant) launch_t<128, 128>(g, p, a, s);
-    else if (tasks(128, 64) >= kWant) launch_t<128, 64>(g, p, a, s);
+    if (linear_tasks(a.M, a.N, 64, 64) > INT32_MAX) return hipErrorInvalidConfiguration;
+    if (linear_tasks(a.M, a.N, 128, 128) >= kWantTasks) launch_t<128, 128>(g, p, a, s);
+    else if (linear_tasks(a.M, a.N, 128, 64) >= kWantTasks) launch_t<128, 64>(g, p, a, s);
     else launch_t<64, 64>(g, p, a, s);
     return hipGetLastError();
 }

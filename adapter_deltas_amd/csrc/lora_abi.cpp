@@ -362,6 +362,48 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
 // rows of the batch (the base projection with the delta in its epilogue)
 // takes them from one table, active rows first.  Kernels of the delta read
 // only the first n_active entries.
+// Slot and ranks of every active row (rows holds the active rows only when
+// this is called), for the base projection's delta.
+template <class Ranks>
+void fill_row_meta(Plan &pl, Ranks ranks)
+{
+    pl.meta.clear();
+    pl.meta.reserve(pl.rows.size() * 4);
+    for (int32_t t : pl.rows) {
+        const int32_t s = pl.tok[(size_t)t];
+        pl.meta.push_back(s);
+        pl.meta.push_back((ranks(s, 0) & 0xffff) | (ranks(s, 1) << 16));
+        pl.meta.push_back((ranks(s, 2) & 0xffff) | (ranks(s, 3) << 16));
+        pl.meta.push_back(0);
+    }
+    // delta steps of each 64- and 128-row tile: per distinct slot, one per 16
+    // ranks of every slice (a bound on what the tile's columns need)
+    auto steps = [&](int32_t s) {
+        int32_t n = 0;
+        for (int j = 0; j < kMetaStride; ++j) n += (ranks(s, j) + 15) / 16;
+        return n;
+    };
+    const int64_t n = (int64_t)pl.rows.size();
+    for (int b = 0; b < 2; ++b) {
+        const int64_t bm = b == 0 ? 64 : 128;
+        int32_t most = 0;
+        std::vector<int32_t> seen;
+        for (int64_t m0 = 0; m0 < n; m0 += bm) {
+            seen.clear();
+            int32_t tot = 0;
+            for (int64_t m = m0; m < std::min(n, m0 + bm); ++m) {
+                const int32_t s = pl.tok[(size_t)pl.rows[(size_t)m]];
+                if (std::find(seen.begin(), seen.end(), s) == seen.end()) {
+                    seen.push_back(s);
+                    tot += steps(s);
+                }
+            }
+            most = std::max(most, tot);
+        }
+        pl.tile_steps[b] = most;
+    }
+}
+
 void append_inactive_rows(Plan &pl)
 {
     for (size_t t = 0; t < pl.tok.size(); ++t)
@@ -536,6 +578,7 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     pl.info.n_gather_segments = n_seg - n_dec_seg - n_pre_seg;
     pl.info.n_distinct = (int32_t)distinct_ids.size();
     pl.info.n_seqs = n_seq;
+    fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
     int32_t na = 0;
     for (int i = 0; i < n_seq; ++i) na += adm[i];
@@ -637,6 +680,7 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     pl.info.n_gather_segments = n_seg - n_dec_seg;
     pl.info.n_distinct = (int32_t)order.size();
     pl.info.n_seqs = pl.info.n_admitted_seqs = n_rows;
+    fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
     pl.adm.clear();
     pl.distinct_slots = order;
@@ -941,7 +985,8 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
         }
     }
     std::memset(&r->info, 0, sizeof r->info);
-    r->off_seg = r->off_row = r->off_tok = 0;
+    r->off_seg = r->off_row = r->off_tok = r->off_meta = 0;
+    r->tile_steps[0] = r->tile_steps[1] = 0;
     r->pool_max_slots = 0;
     r->device_built = false;
     r->off_counts = 0;
@@ -1043,6 +1088,9 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->off_seg = 0;
     r->off_row = (int32_t)pl.off_row();
     r->off_tok = (int32_t)pl.off_tok();
+    r->off_meta = (int32_t)pl.off_meta();
+    r->tile_steps[0] = pl.tile_steps[0];
+    r->tile_steps[1] = pl.tile_steps[1];
     r->device_built = false;
     r->info = pl.info;
     r->pool_max_slots = p->desc.max_slots;
@@ -1423,16 +1471,6 @@ int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_r
                         (long long)workspace_bytes, (long long)need);
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n_act > 0) {
-        // v of the active rows, in the routing's order and the split bf16
-        // form the projection's delta K-tiles read, by the shrink kernels
-        CallStreams cs;
-        if (int32_t rc = fork_streams(r, st, cs)) return rc;
-        const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs, true, linear_v_len(p));
-        const int32_t rj = join_streams(r, cs);
-        if (rc) return rc;
-        if (rj) return rj;
-    }
     LinearArgs a{};
     a.W = static_cast<const uint16_t *>(W);
     a.ldw = ldw;
@@ -1444,8 +1482,27 @@ int32_t lora_linear_delta(const lora_pool *p, const lora_routing *r, int32_t n_r
     a.N = p->geom.H_out;
     a.K = p->desc.h_in;
     a.rows = r ? r->dev + r->off_row : nullptr;
+    if (n_act > 0 &&
+        r->tile_steps[linear_tile_rows(n_rows, p->geom.H_out) == 64 ? 0 : 1] > kLinearMaxSteps) {
+        // more delta steps in one row tile than the kernel holds: the base
+        // product, then the delta added by lora_delta_apply (the workspace
+        // holds v in fp32 as well)
+        hipError_t e = launch_linear(p->geom, pool_dev(p), a, st);
+        if (e != hipSuccess) return hip_fail(e, "base projection launch");
+        return delta_apply_ws(p, r, x, ldx, y, ldy, workspace, workspace_bytes, st);
+    }
+    if (n_act > 0) {
+        // v of the active rows, in the routing's order and the split bf16
+        // form the projection's delta K-tiles read, by the shrink kernels
+        CallStreams cs;
+        if (int32_t rc = fork_streams(r, st, cs)) return rc;
+        const int32_t rc = enqueue_shrink(p, r, x, ldx, v, cs, true, linear_v_len(p));
+        const int32_t rj = join_streams(r, cs);
+        if (rc) return rc;
+        if (rj) return rj;
+    }
     a.n_delta = n_act;
-    a.tok_slot = r ? r->dev + r->off_tok : nullptr;
+    a.row_meta = r ? r->dev + r->off_meta : nullptr;
     a.v = v;
     hipError_t e = launch_linear(p->geom, pool_dev(p), a, st);
     if (e != hipSuccess) return hip_fail(e, "base projection launch");

@@ -62,6 +62,11 @@ struct LaneGeom {
     int64_t bt_slice_off[LORA_MAX_SLICES];
 };
 
+// Delta steps (one per slot, slice and 16 ranks) a row tile of the base
+// projection holds in LDS; a batch with more in one tile takes the base
+// product and lora_delta_apply instead.
+constexpr int kLinearMaxSteps = 1024;
+
 // v in the split form the base projection's delta K-steps read: per row, per
 // slice, per group of 16 ranks, 16 bf16 values v_hi = bf16(v) and then 16 bf16
 // values v_lo = bf16(v - v_hi) (nearest even; v = v_hi + v_lo to about 16
@@ -121,13 +126,16 @@ struct LinearArgs {
     int M, N, K;              // rows of the batch, sum(h_out), h_in
     const int32_t *rows;      // GEMM row m -> token row (null: m itself)
     int n_delta;              // GEMM rows m < n_delta carry a delta; v row m
-    const int32_t *tok_slot;  // slot per token row
-    const float *v;           // [n_delta][v_stride] fp32, the shrink's output
+    const int32_t *row_meta;  // per GEMM row m < n_delta: [slot, rank0 | rank1 << 16,
+                              // rank2 | rank3 << 16, 0]
+    const float *v;           // v of rows m < n_delta in the split bf16 form
 };
 
 // ---- launchers (kernels_*.hip) ----
 hipError_t launch_linear(const LaneGeom &g, const PoolDev &p, const LinearArgs &a,
                          hipStream_t s);
+// Rows per tile (64 or 128) launch_linear takes for an M x N product.
+int linear_tile_rows(int64_t M, int64_t N);
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
                               float *v, int vsplit, hipStream_t s);
@@ -198,6 +206,12 @@ namespace lora {
 // [segments: kSegWords each][active rows][pad to 4][token slots][pad to 4].
 struct Plan {
     std::vector<int32_t> seg, rows, tok;
+    // per active row (the first n_active entries of rows): its slot and the
+    // slot's ranks, 4 words [slot, rank0 | rank1 << 16, rank2 | rank3 << 16, 0]
+    std::vector<int32_t> meta;
+    // most delta steps of one 64- and one 128-row tile of the active rows
+    // (every slice of the slot counted)
+    int32_t tile_steps[2] = {0, 0};
     std::vector<int32_t> slot_ranks;   // per distinct slot: kMetaStride ranks
     std::vector<uint8_t> adm;
     std::vector<int32_t> distinct_slots;
@@ -205,7 +219,8 @@ struct Plan {
     lora_routing_info info{};
     int64_t off_row() const { return (int64_t)seg.size(); }  // multiple of 4
     int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
-    int64_t words() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
+    int64_t off_meta() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
+    int64_t words() const { return off_meta() + (int64_t)meta.size(); }
     void pack(int32_t *w) const
     {
         int64_t o = 0;
@@ -213,7 +228,8 @@ struct Plan {
         for (int32_t a : rows) w[o++] = a;
         while (o < off_tok()) w[o++] = 0;
         for (int32_t a : tok) w[o++] = a;
-        while (o < words()) w[o++] = 0;
+        while (o < off_meta()) w[o++] = 0;
+        for (int32_t a : meta) w[o++] = a;
     }
 };
 }  // namespace lora
@@ -228,6 +244,8 @@ struct lora_routing {
     int32_t stage_next;
     // device views of the current batch (offsets into dev)
     int32_t off_seg, off_row, off_tok;
+    int32_t off_meta;                 // per active row slot and ranks (host-built only)
+    int32_t tile_steps[2];            // Plan::tile_steps of the current batch
     lora_routing_info info;
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
     bool device_built;                // counts on the device, info holds bounds

@@ -38,6 +38,17 @@ HIGH_RANK = WorkloadSpec(
     decode_rows=60, base_prob=0.2, prefill_seqs=3, prefill_len=(1, 90))
 
 
+# every decode row its own adapter of rank 256 on two slices: about 60
+# distinct slots in a 64-row tile, 32 delta steps each, past what one tile
+# holds, so the call takes the base product and then lora_delta_apply
+STEP_OVERFLOW = WorkloadSpec(
+    name="linear_step_overflow", seed=53,
+    lanes=(LaneSpec("two", 136, (72, 64)),),
+    n_adapters=96, ranks=(256,) * 96, rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 2.0), max_rank=256,
+    decode_rows=128, base_prob=0.0, popularity="uniform")
+
+
 @pytest.fixture(scope="module")
 def lib():
     import torch
@@ -126,6 +137,18 @@ def test_linear_zero_weight_gives_the_delta(lib, cfg, lane, pml, mode):
         assert info["n_decode_segments"] == 0 and info["n_prefill_segments"] > 0
     tok = check_against_oracle(w, lane, W, y)
     assert np.all(y[tok == 0] == 0)
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+def test_linear_more_steps_than_a_tile_holds(lib, mode):
+    """A batch whose row tiles need more delta steps than the kernel keeps
+    (the two-pass form: base product, then lora_delta_apply) still matches
+    the oracle, and its base product is the one of a call with no routing."""
+    w = generate(STEP_OVERFLOW, mode=mode)
+    W = draw_base_weight(STEP_OVERFLOW, 0, STEP_OVERFLOW.lanes[0], mode=mode)
+    y, info, pool, _ = run_linear(lib, w, "two", W)
+    assert info["n_distinct"] > 60
+    check_against_oracle(w, "two", W, y)
 
 
 def test_linear_permutation_and_solo_bit_exact(lib):
