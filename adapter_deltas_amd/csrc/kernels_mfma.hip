@@ -23,6 +23,8 @@
 // only, so a row's bits do not depend on the rest of the batch.
 #include "kernels_common.h"
 
+#include <type_traits>
+
 namespace lora {
 namespace {
 
@@ -92,17 +94,17 @@ __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1
 // vsplit > 0: v is written in the split form of the base projection's
 // epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int NG, int RT, bool GATHER>
-__global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
-    LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
-    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v, int vsplit)
+__device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDev &p,
+                                                 const RoutingDev &r, int task, int seg_begin,
+                                                 int groups_per_slice,
+                                                 const uint16_t *__restrict__ x, int64_t ldx,
+                                                 float *__restrict__ v, int vsplit)
 {
-    touch_args(n_tasks, g, p, r, ldx);
     constexpr int D = kShrinkDepth, ROWS = 16 * RT;
     static_assert(kRowTiles % RT == 0, "row chunks tile the segment");
     // task order within a segment: row chunk, slice, rank group
     const int per_chunk = g.n_slices * groups_per_slice;
     const int per_seg = per_chunk * (kRowTiles / RT);
-    const int task = xcd_task(blockIdx.x, n_tasks);
     const int si = seg_begin + task / per_seg;
     const int rem = task % per_seg;
     const int rc = rem / per_chunk;
@@ -136,12 +138,6 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     }
     const uint16_t *a_slice =
         p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
-    // Rank tiles past the segment's rank read the last tile the rank has
-    // again (a cache hit, not new bytes) and are not multiplied.
-    const uint16_t *ar[NG];
-#pragma unroll
-    for (int i = 0; i < NG; ++i)
-        ar[i] = a_slice + (int64_t)min(16 * (t0 + min(i, nt_here - 1)) + a, g.rank_pad - 1) * g.h_in;
 
     __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][4];   // per wave: x rows, then A rows
     uint4(*const lw)[4] = lds[wave];
@@ -156,66 +152,84 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
     // loop is branch-free so the loads stay in flight: every load has a valid
     // (clamped) address, and K-steps past h_in and the padding steps that
     // round a wave's count up to a multiple of the depth multiply zeros.
+    // The loop is instantiated for the task's count of live rank tiles NTH
+    // (the rank tiles past the segment's rank are neither loaded nor
+    // multiplied), so no branch sits between its products: a branch per
+    // product had every product wait for its own LDS read.
     const int n_ks = (g.h_in + 31) / 32;
     const int my_steps = (n_ks - wave + kShrinkParts - 1) / kShrinkParts;
-    uint4 xs[D][RT], as[D][NG];
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    auto load = [&](uint4 (&xt)[RT], uint4 (&at)[NG], int step) {
-        const int e = min((wave + kShrinkParts * step) * 32 + 8 * q, g.h_in - 8);
+    auto run = [&](auto nth_c) {
+        constexpr int NTH = decltype(nth_c)::value;
+        const uint16_t *ar[NTH];
 #pragma unroll
-        for (int i = 0; i < RT; ++i) xt[i] = ld16(xr[i] + e);
+        for (int i = 0; i < NTH; ++i)
+            ar[i] = a_slice + (int64_t)min(16 * (t0 + i) + a, g.rank_pad - 1) * g.h_in;
+        uint4 xs[D][RT], as[D][NTH];
+        const uint4 zero = make_uint4(0, 0, 0, 0);
+        auto load = [&](uint4 (&xt)[RT], uint4 (&at)[NTH], int step) {
+            const int e = min((wave + kShrinkParts * step) * 32 + 8 * q, g.h_in - 8);
 #pragma unroll
-        for (int i = 0; i < NG; ++i) at[i] = ld16(ar[i] + e);
-    };
-    auto mma = [&](const uint4 (&xt)[RT], const uint4 (&at)[NG], int step) {
-        // chunks past h_in are staged as zeros, in both operands
-        const bool e_ok = (wave + kShrinkParts * step) * 32 + 8 * q < g.h_in;
-        auto keep = [&](uint4 w) {   // by value: a select between lvalues spills
-            return e_ok ? w : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < RT; ++i) xt[i] = ld16(xr[i] + e);
+#pragma unroll
+            for (int i = 0; i < NTH; ++i) at[i] = ld16(ar[i] + e);
         };
+        auto mma = [&](const uint4 (&xt)[RT], const uint4 (&at)[NTH], int step) {
+            // chunks past h_in are staged as zeros, in both operands
+            const bool e_ok = (wave + kShrinkParts * step) * 32 + 8 * q < g.h_in;
+            auto keep = [&](uint4 w) {   // by value: a select between lvalues spills
+                return e_ok ? w : make_uint4(0, 0, 0, 0);
+            };
 #pragma unroll
-        for (int i = 0; i < RT; ++i) lw[16 * i + a][chunk_pos(a, q)] = keep(xt[i]);
+            for (int i = 0; i < RT; ++i) lw[16 * i + a][chunk_pos(a, q)] = keep(xt[i]);
 #pragma unroll
-        for (int i = 0; i < NG; ++i) lw[16 * (RT + i) + a][chunk_pos(a, q)] = keep(at[i]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint4 af[NG];
+            for (int i = 0; i < NTH; ++i) lw[16 * (RT + i) + a][chunk_pos(a, q)] = keep(at[i]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint4 af[NTH];
 #pragma unroll
-        for (int nt = 0; nt < NG; ++nt) af[nt] = lw[16 * (RT + nt) + li][chunk_pos(li, lg)];
+            for (int nt = 0; nt < NTH; ++nt) af[nt] = lw[16 * (RT + nt) + li][chunk_pos(li, lg)];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const uint4 xv = lw[16 * rt + li][chunk_pos(li, lg)];
-            uint4 xhi = xv, xlo = zero;
-            if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
+            for (int rt = 0; rt < RT; ++rt) {
+                const uint4 xv = lw[16 * rt + li][chunk_pos(li, lg)];
+                uint4 xhi = xv, xlo = zero;
+                if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
 #pragma unroll
-            for (int nt = 0; nt < NG; ++nt) {
-                if (nt >= nt_here) continue;    // uniform
-                acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
-                if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
+                for (int nt = 0; nt < NTH; ++nt) {
+                    acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
+                    if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
+                }
+            }
+            // the next step's writes stay behind these reads
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+        // The scheduling fences keep every load group in source order, in the
+        // first fill as in the loop, and each refill after the step that reads
+        // the registers it overwrites.  The loads of a pass are then consumed
+        // in the next pass and stay in flight across the loop's back edge.
+#pragma unroll
+        for (int st = 0; st < D; ++st) {
+            load(xs[st], as[st], st);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int base = 0; base < my_steps; base += D) {
+#pragma unroll
+            for (int st = 0; st < D; ++st) {
+                mma(xs[st], as[st], base + st);
+                __builtin_amdgcn_sched_barrier(0);
+                load(xs[st], as[st], base + st + D);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // the next step's writes stay behind these reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    // The scheduling fences keep every load group in source order, in the
-    // first fill as in the loop, and each refill after the step that reads
-    // the registers it overwrites.  The loads of a pass are then consumed in
-    // the next pass and stay in flight across the loop's back edge.
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-        load(xs[s], as[s], s);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int base = 0; base < my_steps; base += D) {
-#pragma unroll
-        for (int s = 0; s < D; ++s) {
-            mma(xs[s], as[s], base + s);
-            __builtin_amdgcn_sched_barrier(0);
-            load(xs[s], as[s], base + s + D);
-            __builtin_amdgcn_sched_barrier(0);
+    if (nt_here >= NG) run(std::integral_constant<int, NG>{});
+    else if constexpr (NG > 1) {
+        if (nt_here == 1) run(std::integral_constant<int, 1>{});
+        else if constexpr (NG > 2) {
+            if (nt_here == 2) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 3>{});
         }
     }
 
@@ -262,6 +276,16 @@ __global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
             }
         }
     }
+}
+
+template <bool FP16X, int NG, int RT, bool GATHER>
+__global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
+    LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
+    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v, int vsplit)
+{
+    touch_args(n_tasks, g, p, r, ldx);
+    shrink_mfma_task<FP16X, NG, RT, GATHER>(g, p, r, xcd_task(blockIdx.x, n_tasks), seg_begin,
+                                            groups_per_slice, x, ldx, v, vsplit);
 }
 
 // A task is one 128-column tile of one slice over a group of consecutive

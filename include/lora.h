@@ -280,8 +280,11 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  *                 first, rows being consecutive; gather: unused, the token
  *                 rows being those of its active rows)} at word
  *                 offsets_out[0], decode segments first, then prefill, then
- *                 gather; the token row of each active row at offsets_out[1];
- *                 and one slot per token row at offsets_out[2]
+ *                 gather; the token row of each active row at offsets_out[1]
+ *                 (then the rows outside the delta, ascending); one slot per
+ *                 token row at offsets_out[2]; and, from the next multiple
+ *                 of 4 words on, 4 words per active row {slot, rank0 |
+ *                 rank1 << 16, rank2 | rank3 << 16, 0}
  *   offsets_out   host int32 [3]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]
@@ -494,7 +497,11 @@ int32_t lora_delta_apply(const lora_pool *pool, const lora_routing *routing,
  * accumulator: per 32-rank chunk of the row's slice, B times v_hi, then B
  * times v_lo, with zeros for the terms of other rows' adapters.  A row's bits
  * depend on its own x row, W and adapter only (not on the other rows of the
- * batch), and base rows equal the product of a call with routing NULL.
+ * batch), and base rows equal the product of a call with routing NULL.  A
+ * row tile (64 or 128 consecutive active rows) holds at most 1024 delta steps
+ * (one per slot, slice and 16 ranks); a batch that would need more in one
+ * tile -- many distinct high-rank adapters side by side -- is computed as the
+ * base product followed by lora_delta_apply, whose sums it then has.
  * Errors: ARG (null pool, W or buffers; a
  * routing built on the device), SHAPE (n_rows != the routing's rows, widths,
  * strides, alignment), DTYPE (fp16 lane), MISMATCH, CAPACITY (workspace), HIP.
