@@ -58,6 +58,8 @@ def algorithmic(w, lane_name, admitted):
 
 
 KERNEL_SOURCES = ("include/lora.h", "adapter_deltas_amd/csrc")
+# the base projection's kernel is not among the counted ones (delta_apply's)
+NOT_COUNTED_SOURCES = ("kernels_linear.hip",)
 COPY_CALIBRATION_BYTES = 268435456
 
 
@@ -151,7 +153,9 @@ def summarize_pmc(pmc_dir: str, configs):
 def sources_digest() -> str:
     """sha256 over the library's code: a counter summary taken from other code
     no longer describes the kernels that run.  Comments and whitespace are
-    left out, so edits to the documentation keep the summary valid."""
+    left out, so edits to the documentation keep the summary valid, and so is
+    the base projection's kernel source, whose kernel the counters do not
+    cover."""
     import hashlib
     h = hashlib.sha256()
     comment = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
@@ -159,7 +163,7 @@ def sources_digest() -> str:
         path = os.path.join(ROOT, top)
         files = [path] if os.path.isfile(path) else sorted(
             os.path.join(path, f) for f in os.listdir(path)
-            if f.endswith((".h", ".hip", ".cpp")))
+            if f.endswith((".h", ".hip", ".cpp")) and f not in NOT_COUNTED_SOURCES)
         for f in files:
             h.update(os.path.relpath(f, ROOT).encode())
             with open(f, encoding="utf-8") as fh:
