@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace lora {
 namespace {
@@ -78,6 +79,18 @@ __device__ __forceinline__ void tile_of(int task, int n_tiles, int m_tiles, int 
     tm = grp * kGroupM + (in - tn * gm);
 }
 
+// f(integral_constant<int, i>) for i = 0 .. N - 1, in order, at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void unroll_seq(F f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unroll(F f)
+{
+    unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ int wave_min(int v)
 {
 #pragma unroll
@@ -124,7 +137,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
     constexpr int NI = BN / 32, MI = BM / 32;              // 16-wide tiles per wave
     constexpr int ROWS = BN + BM;                          // LDS rows per K-tile
     constexpr int NL = ROWS * kChunks / kThreads;          // 16-byte loads per thread
-    constexpr int D = NL <= 4 ? 3 : 2;                     // K-tiles of loads in flight
+    // K-tiles of loads in flight (64 x 64 tiles on decode_mix QKV, per call:
+    // 3 -> 40.4 us, 4 -> 39.2, 6 -> 41.9, 8 -> 41.4: the tile's L2 traffic,
+    // not its loads in flight, sets the time)
+    constexpr int D = NL <= 4 ? 3 : 2;
     constexpr int LDT = BN + 4;                            // padded row of the output tile
     constexpr int CPL = BN / 64;                           // epilogue columns per lane
     constexpr int RPW = BM / (kThreads / 64);              // epilogue rows per wave
@@ -406,15 +422,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_linear(LaneGeom g, PoolDev p, L
     };
     int kt = 0;
     for (; kt + 2 * D <= KT; kt += D) {
-        step_base(std::integral_constant<int, 0>{}, kt);
-        step_base(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (D > 2) step_base(std::integral_constant<int, 2>{}, kt + 2);
+        unroll<D>([&](auto c) __attribute__((always_inline)) { step_base(c, kt + c.value); });
     }
     const int KTD = (KT_all + D - 1) / D * D;
     for (; kt < KTD; kt += D) {
-        step(std::integral_constant<int, 0>{}, kt);
-        step(std::integral_constant<int, 1>{}, kt + 1);
-        if constexpr (D > 2) step(std::integral_constant<int, 2>{}, kt + 2);
+        unroll<D>([&](auto c) __attribute__((always_inline)) { step(c, kt + c.value); });
     }
 
     // Accumulator tile to LDS: lane holds, per (ni, mi), outputs
