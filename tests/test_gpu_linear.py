@@ -38,6 +38,18 @@ HIGH_RANK = WorkloadSpec(
     decode_rows=60, base_prob=0.2, prefill_seqs=3, prefill_len=(1, 90))
 
 
+# large enough for the 256 x 128 tile (at least 512 of them): 4104 outputs
+# over three slices (tiles straddle the slice edges; the last tile is 8
+# wide), about 3900 rows of decode and prefill sequences, K = 520 (8 K-tiles
+# and a tail)
+LARGE_RAGGED = WorkloadSpec(
+    name="linear_large_ragged", seed=54,
+    lanes=(LaneSpec("wide_out", 520, (2056, 1024, 1024)),),
+    n_adapters=12, ranks=(8, 16, 32, 64, 128, 3, 17, 40, 100, 8, 16, 64), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=128,
+    decode_rows=3000, base_prob=0.2, prefill_seqs=6, prefill_len=(100, 200))
+
+
 # every decode row its own adapter of rank 256 on two slices: about 60
 # distinct slots in a 64-row tile, 32 delta steps each, past what one tile
 # holds, so the call takes the base product and then lora_delta_apply
@@ -97,9 +109,10 @@ def check_against_oracle(w, lane, W, y, rows=None):
 
 @pytest.mark.parametrize("mode", ["real", "int"])
 @pytest.mark.parametrize("cfg,lane", [("decode_mix", "qkv"), ("ragged", "qkv_like"),
-                                      ("high_rank", "wide")])
+                                      ("high_rank", "wide"), ("large", "wide_out")])
 def test_linear_matches_oracle(lib, cfg, lane, mode):
-    spec = {"ragged": RAGGED, "high_rank": HIGH_RANK}.get(cfg) or config_by_name(cfg)
+    spec = {"ragged": RAGGED, "high_rank": HIGH_RANK,
+            "large": LARGE_RAGGED}.get(cfg) or config_by_name(cfg)
     w = generate(spec, mode=mode, lanes=(lane,))
     li = [l.name for l in spec.lanes].index(lane)
     W = draw_base_weight(spec, li, spec.lanes[li], mode=mode)
