@@ -23,20 +23,34 @@ namespace {
 //
 // vsplit > 0: v is written in the split form of the base projection's
 // epilogue (rows of vsplit bf16) instead of fp32.
-template <bool FP16X, int W>
+//
+// TAB: the task is read from `tasks` (one word per live task: decode
+// segment, slice, rank block), so no workgroup is launched for a rank block
+// past its segment's rank; a slice past the pool's count ends the task.
+template <bool FP16X, int W, bool TAB>
 __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, RoutingDev r,
                                                          int n_tasks, int kb_per_slice,
                                                          const uint16_t *__restrict__ x,
                                                          int64_t ldx, float *__restrict__ v,
-                                                         int vsplit)
+                                                         int vsplit, const int32_t *tasks)
 {
     touch_args(n_tasks, g, p, r, ldx);
-    const int per_seg = g.n_slices * kb_per_slice;
     const int task = xcd_task(blockIdx.x, n_tasks);
-    const int si = task / per_seg;
-    const int rem = task - si * per_seg;
-    const int j = rem / kb_per_slice;
-    const int kb = rem - j * kb_per_slice;
+    int si, j, kb;
+    if constexpr (TAB) {
+        typedef const __attribute__((address_space(4))) int32_t cint;
+        const int w = *(cint *)(tasks + task);
+        si = w & 0xffffff;
+        j = (w >> 24) & 3;
+        kb = (int)((uint32_t)w >> 26);
+        if (j >= g.n_slices) return;
+    } else {
+        const int per_seg = g.n_slices * kb_per_slice;
+        si = task / per_seg;
+        const int rem = task - si * per_seg;
+        j = rem / kb_per_slice;
+        kb = rem - j * kb_per_slice;
+    }
     Seg sd;
     if (!decode_seg(r, si, sd)) return;
     // past the count a device-built descriptor is stale: its slot is read
@@ -300,9 +314,9 @@ __global__ void k_clear_meta(int32_t *rank_tab, float *scale_tab, int n)
 
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx, float *v,
-                              int vsplit, hipStream_t s)
+                              int vsplit, hipStream_t s, const int32_t *tasks, int n_tasks)
 {
-    const int64_t blocks = (int64_t)n_seg * g.n_slices * kb_per_slice;
+    const int64_t blocks = tasks ? n_tasks : (int64_t)n_seg * g.n_slices * kb_per_slice;
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
@@ -317,9 +331,15 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const int w_max = blocks < 512 ? 8 : blocks < 2048 ? 4 : 2;
     const int w = std::min(w_max, n_sub >= 8 ? 8 : n_sub >= 4 ? 4 : n_sub >= 2 ? 2 : 1);
     const dim3 grid((unsigned)blocks), block(64 * w);
-#define LAUNCH_SHRINK(F, W) \
-    hipLaunchKernelGGL((k_shrink_gemv<F, W>), grid, block, 0, s, g, p, r, (int)blocks, \
-                       kb_per_slice, xp, ldx, v, vsplit)
+#define LAUNCH_SHRINK(F, W)                                                                   \
+    do {                                                                                      \
+        if (tasks)                                                                            \
+            hipLaunchKernelGGL((k_shrink_gemv<F, W, true>), grid, block, 0, s, g, p, r,       \
+                               (int)blocks, kb_per_slice, xp, ldx, v, vsplit, tasks);         \
+        else                                                                                  \
+            hipLaunchKernelGGL((k_shrink_gemv<F, W, false>), grid, block, 0, s, g, p, r,      \
+                               (int)blocks, kb_per_slice, xp, ldx, v, vsplit, tasks);         \
+    } while (0)
     if (g.x_fp16) {
         if (w == 8) LAUNCH_SHRINK(true, 8);
         else if (w == 4) LAUNCH_SHRINK(true, 4);

@@ -272,10 +272,13 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
     RoutingDev rd = routing_dev(r);
     PoolDev pd = pool_dev(p);
     if (decode && I.n_decode_segments > 0) {
-        // rank blocks of the GEMV slots only (higher-rank slots are gathered)
+        // rank blocks of the GEMV slots only (higher-rank slots are gathered);
+        // a host-built routing may list the live tasks only
         const int kb = (gemv_max_rank(p, r) + kKBlock - 1) / kKBlock;
+        const bool tab = !r->device_built && r->n_tasks > 0;
         hipError_t e = launch_shrink_gemv(p->geom, pd, rd, I.n_decode_segments, kb, x, ldx, v,
-                                          vsplit, cs.dec);
+                                          vsplit, cs.dec, tab ? r->dev + r->off_tasks : nullptr,
+                                          tab ? r->n_tasks : 0);
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
     const int nt = (kmax + 15) / 16;
@@ -402,6 +405,33 @@ void fill_row_meta(Plan &pl, Ranks ranks)
         }
         pl.tile_steps[b] = most;
     }
+}
+
+// The live GEMV shrink tasks of the plan's decode segments: ceil(rank / 8)
+// rank blocks per slice of each.  Kept only while they fit the routing's
+// words (2 * kSegWords + 2 per token row; at most 16 per row are taken by the
+// segment tables and 4 by the per-row table) and leave at least a quarter of
+// a full grid's tasks out (reading the task is one more dependent load).
+void fill_gemv_tasks(Plan &pl, int32_t max_tokens)
+{
+    pl.tasks.clear();
+    const int64_t n_seg = (int64_t)pl.seg.size() / kSegWords;
+    int32_t most_kb = 0, n_dec = 0;
+    for (int64_t si = 0; si < n_seg; ++si) {
+        const int32_t *d = &pl.seg[(size_t)(si * kSegWords)];
+        if (d[3] != kSegDecode) continue;
+        ++n_dec;
+        for (int j = 0; j < kMetaStride; ++j) {
+            const int32_t nk = (d[4 + j] + kKBlock - 1) / kKBlock;
+            most_kb = std::max(most_kb, nk);
+            for (int32_t kb = 0; kb < nk; ++kb)
+                pl.tasks.push_back(gemv_task_word((int32_t)si, j, kb));
+        }
+    }
+    const int64_t full = (int64_t)n_dec * kMetaStride * most_kb;
+    const int64_t budget = (int64_t)max_tokens * (2 * kSegWords + 2) - pl.off_tasks() - 64;
+    if ((int64_t)pl.tasks.size() * 4 > full * 3 || (int64_t)pl.tasks.size() > budget)
+        pl.tasks.clear();
 }
 
 void append_inactive_rows(Plan &pl)
@@ -580,6 +610,7 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     pl.info.n_seqs = n_seq;
     fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
+    fill_gemv_tasks(pl, max_tokens);
     int32_t na = 0;
     for (int i = 0; i < n_seq; ++i) na += adm[i];
     pl.info.n_admitted_seqs = na;
@@ -682,6 +713,7 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     pl.info.n_seqs = pl.info.n_admitted_seqs = n_rows;
     fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
+    fill_gemv_tasks(pl, n_rows);
     pl.adm.clear();
     pl.distinct_slots = order;
     pl.slot_ranks.clear();
@@ -987,6 +1019,7 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
     std::memset(&r->info, 0, sizeof r->info);
     r->off_seg = r->off_row = r->off_tok = r->off_meta = 0;
     r->tile_steps[0] = r->tile_steps[1] = 0;
+    r->off_tasks = r->n_tasks = 0;
     r->pool_max_slots = 0;
     r->device_built = false;
     r->off_counts = 0;
@@ -1089,6 +1122,8 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->off_row = (int32_t)pl.off_row();
     r->off_tok = (int32_t)pl.off_tok();
     r->off_meta = (int32_t)pl.off_meta();
+    r->off_tasks = (int32_t)pl.off_tasks();
+    r->n_tasks = (int32_t)pl.tasks.size();
     r->tile_steps[0] = pl.tile_steps[0];
     r->tile_steps[1] = pl.tile_steps[1];
     r->device_built = false;
@@ -1231,6 +1266,7 @@ int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_
     r->off_tok = (int32_t)off_tok;
     r->off_counts = (int32_t)off_counts;
     r->device_built = true;
+    r->n_tasks = 0;
     r->max_gather_rows = kPrefillSegRows;   // segment sizes are known on the device only
     r->decode_rows = 0;
     // A MoE layer's dispatched rows spread over (adapter, expert) pairs, so

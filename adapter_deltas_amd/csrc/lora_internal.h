@@ -136,9 +136,16 @@ hipError_t launch_linear(const LaneGeom &g, const PoolDev &p, const LinearArgs &
                          hipStream_t s);
 // Rows per tile (64 or 128) launch_linear takes for an M x N product.
 int linear_tile_rows(int64_t M, int64_t N);
+// With `tasks` (n_tasks words, gemv_task_word) only those tasks are launched.
 hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               int n_seg, int kb_per_slice, const void *x, int64_t ldx,
-                              float *v, int vsplit, hipStream_t s);
+                              float *v, int vsplit, hipStream_t s,
+                              const int32_t *tasks = nullptr, int n_tasks = 0);
+// A GEMV shrink task (decode segment si, slice j, rank block kb) in a word.
+inline int32_t gemv_task_word(int32_t si, int j, int kb)
+{
+    return si | (j << 24) | (kb << 26);
+}
 hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                              int n_seg, const void *x, int64_t ldx, float *y, int64_t ldy,
                              hipStream_t s);
@@ -212,6 +219,9 @@ struct Plan {
     // most delta steps of one 64- and one 128-row tile of the active rows
     // (every slice of the slot counted)
     int32_t tile_steps[2] = {0, 0};
+    // the live GEMV shrink tasks, one word each (gemv_task_word), decode
+    // segments in order, slices, then rank blocks of kKBlock
+    std::vector<int32_t> tasks;
     std::vector<int32_t> slot_ranks;   // per distinct slot: kMetaStride ranks
     std::vector<uint8_t> adm;
     std::vector<int32_t> distinct_slots;
@@ -220,7 +230,8 @@ struct Plan {
     int64_t off_row() const { return (int64_t)seg.size(); }  // multiple of 4
     int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
     int64_t off_meta() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
-    int64_t words() const { return off_meta() + (int64_t)meta.size(); }
+    int64_t off_tasks() const { return off_meta() + (int64_t)meta.size(); }
+    int64_t words() const { return off_tasks() + (int64_t)tasks.size(); }
     void pack(int32_t *w) const
     {
         int64_t o = 0;
@@ -230,6 +241,7 @@ struct Plan {
         for (int32_t a : tok) w[o++] = a;
         while (o < off_meta()) w[o++] = 0;
         for (int32_t a : meta) w[o++] = a;
+        for (int32_t a : tasks) w[o++] = a;
     }
 };
 }  // namespace lora
@@ -246,6 +258,7 @@ struct lora_routing {
     int32_t off_seg, off_row, off_tok;
     int32_t off_meta;                 // per active row slot and ranks (host-built only)
     int32_t tile_steps[2];            // Plan::tile_steps of the current batch
+    int32_t off_tasks, n_tasks;       // the live GEMV shrink tasks (host-built only)
     lora_routing_info info;
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
     bool device_built;                // counts on the device, info holds bounds

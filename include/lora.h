@@ -284,7 +284,9 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  *                 (then the rows outside the delta, ascending); one slot per
  *                 token row at offsets_out[2]; and, from the next multiple
  *                 of 4 words on, 4 words per active row {slot, rank0 |
- *                 rank1 << 16, rank2 | rank3 << 16, 0}
+ *                 rank1 << 16, rank2 | rank3 << 16, 0}, then (possibly
+ *                 none) one word per live decode shrink task {segment |
+ *                 slice << 24 | 8-rank block << 26}
  *   offsets_out   host int32 [3]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]
