@@ -7,9 +7,11 @@
 // Both use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Each wave owns
 // 16 rows of the segment.
 //
-// Shrink:  h_in is cut into K-steps of 32; K-step s belongs to part s % 4.
-//          S_w[t][k] = MFMA chain over the K-steps of part w, ascending, with
-//          the pool's A rows as the first operand and x rows as the second;
+// Shrink:  h_in is cut into pairs of K-steps of 32 (64 elements, loaded as
+//          whole 128-byte rows); pair p belongs to part p % 4.
+//          S_w[t][k] = MFMA chain over the K-steps of part w's pairs,
+//          ascending, with the pool's A rows as the first operand and x rows
+//          as the second;
 //          u = (S_0 + S_1) + (S_2 + S_3) and v = fp32(scale * u).  An fp16 x
 //          is split exactly into bf16 hi + lo and each K-step does the hi
 //          product, then the lo product.  The order depends on h_in only.
@@ -78,19 +80,20 @@ __device__ __forceinline__ void split_f32x8(const float (&f)[8], uint4 &hi, uint
 }
 
 constexpr int kShrinkParts = 4;     // waves of a shrink task: one K-part each
-constexpr int kShrinkDepth = 3;     // K-steps of loads in flight per wave
 constexpr int kRowTiles = kPrefillSegRows / 16;
 
-// Position of 16-byte chunk c of staged row `row`: an XOR swizzle that keeps
-// both the coalesced writes and the operand reads at two LDS passes per
-// 16 lanes.
-__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ ((row >> 1) & 3); }
+// Position of 16-byte chunk c of a staged 128-byte row: an XOR swizzle, so
+// the 16 rows an operand read takes one chunk index from, and the 8 rows a
+// load instruction writes, fall in different bank groups.
+__device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
 
 // Shrink task: RT 16-row tiles of one prefill segment, one slice, NG 16-rank
-// tiles.  Wave w owns K-part w.  Each K-step loads the segment's x rows and
-// the tiles' A rows coalesced (four consecutive lanes read one row's 64
-// bytes), and reorders them through the wave's own LDS into the MFMA operand
-// layout (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
+// tiles.  Wave w owns K-part w.  Each pair of K-steps loads the segment's x
+// rows and the tiles' A rows as whole 128-byte lines (eight consecutive
+// lanes read one row's 64 elements, eight rows per instruction: a load of
+// 16 rows x 64 bytes ran at half the rate), and reorders them through the
+// wave's own LDS into the MFMA operand layout (lane l: row l % 16, elements
+// 8 (l / 16) .. + 7 of the K-step).
 // vsplit > 0: v is written in the split form of the base projection's
 // epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int NG, int RT, bool GATHER>
@@ -100,7 +103,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
                                                  const uint16_t *__restrict__ x, int64_t ldx,
                                                  float *__restrict__ v, int vsplit)
 {
-    constexpr int D = kShrinkDepth, ROWS = 16 * RT;
+    constexpr int ROWS = 16 * RT;
     static_assert(kRowTiles % RT == 0, "row chunks tile the segment");
     // task order within a segment: row chunk, slice, rank group
     const int per_chunk = g.n_slices * groups_per_slice;
@@ -123,24 +126,24 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
     const int nt_here = min(NG, ntiles - t0);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int q = lane & 3, a = lane >> 2;          // load layout: row a, chunk q
+    const int lb = lane >> 3, lc = lane & 7;        // load layout: row lb, chunk lc
     const int li = lane & 15, lg = lane >> 4;       // operand layout: row li, chunk lg
 
-    // Row pointers of the load layout.  Rows past the segment read its last
-    // row and A rows past rank_pad the last padded row: their products only
-    // reach outputs that are not stored.
-    const uint16_t *xr[RT];
+    // Row pointers of the load layout (8 rows of 128 bytes per instruction).
+    // Rows past the segment read its last row and A rows past rank_pad the
+    // last padded row: their products only reach outputs that are not stored.
+    const uint16_t *xr[2 * RT];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-        const int sr = rb + min(16 * i + a, n_rows - 1);       // segment row
+    for (int i = 0; i < 2 * RT; ++i) {
+        const int sr = rb + min(8 * i + lb, n_rows - 1);       // segment row
         const int tok = GATHER ? r.rows[sd.v_row() + sr] : sd.first_row() + sr;
         xr[i] = x + (int64_t)tok * ldx;
     }
     const uint16_t *a_slice =
         p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
 
-    __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][4];   // per wave: x rows, then A rows
-    uint4(*const lw)[4] = lds[wave];
+    __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][8];   // per wave: x rows, then A rows
+    uint4(*const lw)[8] = lds[wave];
 
     f32x4_t acc[RT][NG];
 #pragma unroll
@@ -148,56 +151,70 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
 #pragma unroll
         for (int nt = 0; nt < NG; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // K-steps wave, wave + 4, ...; loads run kShrinkDepth steps ahead.  The
-    // loop is branch-free so the loads stay in flight: every load has a valid
-    // (clamped) address, and K-steps past h_in and the padding steps that
-    // round a wave's count up to a multiple of the depth multiply zeros.
-    // The loop is instantiated for the task's count of live rank tiles NTH
-    // (the rank tiles past the segment's rank are neither loaded nor
-    // multiplied), so no branch sits between its products: a branch per
+    // K-step pairs (64 elements) p = wave, wave + 4, ...; loads run D pairs
+    // ahead.  The loop is branch-free so the loads stay in flight: every load
+    // has a valid (clamped) address, and pairs past h_in and the padding
+    // pairs that round a wave's count up to a multiple of the depth multiply
+    // zeros.  The loop is instantiated for the task's count of live rank
+    // tiles NTH (the rank tiles past the segment's rank are neither loaded
+    // nor multiplied), so no branch sits between its products: a branch per
     // product had every product wait for its own LDS read.
-    const int n_ks = (g.h_in + 31) / 32;
-    const int my_steps = (n_ks - wave + kShrinkParts - 1) / kShrinkParts;
+    constexpr int DP = 2;                           // K-step pairs of loads in flight
+    const int n_pairs = (g.h_in + 63) / 64;
+    const int my_steps = (n_pairs - wave + kShrinkParts - 1) / kShrinkParts;
     auto run = [&](auto nth_c) {
         constexpr int NTH = decltype(nth_c)::value;
-        const uint16_t *ar[NTH];
+        const uint16_t *ar[2 * NTH];
 #pragma unroll
-        for (int i = 0; i < NTH; ++i)
-            ar[i] = a_slice + (int64_t)min(16 * (t0 + i) + a, g.rank_pad - 1) * g.h_in;
-        uint4 xs[D][RT], as[D][NTH];
+        for (int i = 0; i < 2 * NTH; ++i)
+            ar[i] = a_slice + (int64_t)min(16 * t0 + 8 * i + lb, g.rank_pad - 1) * g.h_in;
+        uint4 xs[DP][2 * RT], as[DP][2 * NTH];
         const uint4 zero = make_uint4(0, 0, 0, 0);
-        auto load = [&](uint4 (&xt)[RT], uint4 (&at)[NTH], int step) {
-            const int e = min((wave + kShrinkParts * step) * 32 + 8 * q, g.h_in - 8);
+        auto load = [&](uint4 (&xt)[2 * RT], uint4 (&at)[2 * NTH], int step) {
+            const int e = min((wave + kShrinkParts * step) * 64 + 8 * lc, g.h_in - 8);
 #pragma unroll
-            for (int i = 0; i < RT; ++i) xt[i] = ld16(xr[i] + e);
+            for (int i = 0; i < 2 * RT; ++i) xt[i] = ld16(xr[i] + e);
 #pragma unroll
-            for (int i = 0; i < NTH; ++i) at[i] = ld16(ar[i] + e);
+            for (int i = 0; i < 2 * NTH; ++i) at[i] = ld16(ar[i] + e);
         };
-        auto mma = [&](const uint4 (&xt)[RT], const uint4 (&at)[NTH], int step) {
+        auto mma = [&](const uint4 (&xt)[2 * RT], const uint4 (&at)[2 * NTH], int step) {
             // chunks past h_in are staged as zeros, in both operands
-            const bool e_ok = (wave + kShrinkParts * step) * 32 + 8 * q < g.h_in;
-            auto keep = [&](uint4 w) {   // by value: a select between lvalues spills
-                return e_ok ? w : make_uint4(0, 0, 0, 0);
-            };
+            const uint32_t m =
+                (wave + kShrinkParts * step) * 64 + 8 * lc < g.h_in ? ~0u : 0u;
+            auto keep = [&](uint4 w) { return make_uint4(w.x & m, w.y & m, w.z & m, w.w & m); };
 #pragma unroll
-            for (int i = 0; i < RT; ++i) lw[16 * i + a][chunk_pos(a, q)] = keep(xt[i]);
+            for (int i = 0; i < 2 * RT; ++i) {
+                const int row = 8 * i + lb;
+                lw[row][chunk_pos(row, lc)] = keep(xt[i]);
+            }
 #pragma unroll
-            for (int i = 0; i < NTH; ++i) lw[16 * (RT + i) + a][chunk_pos(a, q)] = keep(at[i]);
+            for (int i = 0; i < 2 * NTH; ++i) {
+                const int row = 16 * RT + 8 * i + lb;
+                lw[row][chunk_pos(row, lc)] = keep(at[i]);
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            uint4 af[NTH];
 #pragma unroll
-            for (int nt = 0; nt < NTH; ++nt) af[nt] = lw[16 * (RT + nt) + li][chunk_pos(li, lg)];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const uint4 xv = lw[16 * rt + li][chunk_pos(li, lg)];
-                uint4 xhi = xv, xlo = zero;
-                if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
+            for (int h = 0; h < 2; ++h) {             // the pair's two K-steps
+                const int cq = 4 * h + lg;
+                uint4 af[NTH];
 #pragma unroll
                 for (int nt = 0; nt < NTH; ++nt) {
-                    acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
-                    if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
+                    const int row = 16 * (RT + nt) + li;
+                    af[nt] = lw[row][chunk_pos(row, cq)];
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int row = 16 * rt + li;
+                    const uint4 xv = lw[row][chunk_pos(row, cq)];
+                    uint4 xhi = xv, xlo = zero;
+                    if constexpr (FP16X) split_f16x8(xv, xhi, xlo);
+#pragma unroll
+                    for (int nt = 0; nt < NTH; ++nt) {
+                        acc[rt][nt] = mfma16x16x32(af[nt], xhi, acc[rt][nt]);
+                        if constexpr (FP16X) acc[rt][nt] = mfma16x16x32(af[nt], xlo, acc[rt][nt]);
+                    }
                 }
             }
             // the next step's writes stay behind these reads
@@ -210,16 +227,16 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
         // the registers it overwrites.  The loads of a pass are then consumed
         // in the next pass and stay in flight across the loop's back edge.
 #pragma unroll
-        for (int st = 0; st < D; ++st) {
+        for (int st = 0; st < DP; ++st) {
             load(xs[st], as[st], st);
             __builtin_amdgcn_sched_barrier(0);
         }
-        for (int base = 0; base < my_steps; base += D) {
+        for (int base = 0; base < my_steps; base += DP) {
 #pragma unroll
-            for (int st = 0; st < D; ++st) {
+            for (int st = 0; st < DP; ++st) {
                 mma(xs[st], as[st], base + st);
                 __builtin_amdgcn_sched_barrier(0);
-                load(xs[st], as[st], base + st + D);
+                load(xs[st], as[st], base + st + DP);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -279,7 +296,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
 }
 
 template <bool FP16X, int NG, int RT, bool GATHER>
-__global__ __launch_bounds__(64 * kShrinkParts) void k_shrink_mfma(
+__global__ __launch_bounds__(64 * kShrinkParts, 2) void k_shrink_mfma(
     LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
     const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v, int vsplit)
 {
