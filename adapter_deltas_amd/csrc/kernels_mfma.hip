@@ -87,43 +87,89 @@ constexpr int kRowTiles = kPrefillSegRows / 16;
 // load instruction writes, fall in different bank groups.
 __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7); }
 
-// Shrink task: RT 16-row tiles of one prefill segment, one slice, NG 16-rank
-// tiles.  Wave w owns K-part w.  Each pair of K-steps loads the segment's x
-// rows and the tiles' A rows as whole 128-byte lines (eight consecutive
-// lanes read one row's 64 elements, eight rows per instruction: a load of
-// 16 rows x 64 bytes ran at half the rate), and reorders them through the
-// wave's own LDS into the MFMA operand layout (lane l: row l % 16, elements
-// 8 (l / 16) .. + 7 of the K-step).
+// Shrink task: RT 16-row tiles of one prefill segment and up to NG 16-rank
+// tiles.  A segment's rank tiles are numbered across its slices (slice 0's
+// tiles, then slice 1's, ...), and a task takes `cnt` consecutive ones from
+// number c0, so one task can cover the tiles of several slices and read the
+// segment's x rows once for all of them.  Wave w owns K-part w.  Each pair of
+// K-steps loads the segment's x rows and the tiles' A rows as whole 128-byte
+// lines (eight consecutive lanes read one row's 64 elements, eight rows per
+// instruction: a load of 16 rows x 64 bytes ran at half the rate), and
+// reorders them through the wave's own LDS into the MFMA operand layout
+// (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
+// Tasks come from a host-built table (word: segment | c0 << 24 |
+// (cnt - 1) << 30, whole segments, heaviest first) when the routing has one
+// for the lane's slice count; otherwise from the block index: row chunk,
+// slice, group of NG tiles.  Either way a (row, rank) sum is the same.
 // vsplit > 0: v is written in the split form of the base projection's
 // epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int NG, int RT, bool GATHER>
 __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDev &p,
                                                  const RoutingDev &r, int task, int seg_begin,
                                                  int groups_per_slice,
+                                                 const uint32_t *__restrict__ tab,
                                                  const uint16_t *__restrict__ x, int64_t ldx,
                                                  float *__restrict__ v, int vsplit)
 {
     constexpr int ROWS = 16 * RT;
     static_assert(kRowTiles % RT == 0, "row chunks tile the segment");
-    // task order within a segment: row chunk, slice, rank group
-    const int per_chunk = g.n_slices * groups_per_slice;
-    const int per_seg = per_chunk * (kRowTiles / RT);
-    const int si = seg_begin + task / per_seg;
-    const int rem = task % per_seg;
-    const int rc = rem / per_chunk;
-    const int rem2 = rem - rc * per_chunk;
-    const int j = rem2 / groups_per_slice;
-    const int grp = rem2 - j * groups_per_slice;
+    int si, rc, c0 = 0, cnt = 0, jb = 0, grp = 0;
+    if (tab) {
+        const uint32_t w = tab[task];
+        si = seg_begin + (int)(w & 0xffffffu);
+        rc = 0;
+        c0 = (int)((w >> 24) & 63u);
+        cnt = (int)(w >> 30) + 1;
+    } else {
+        // task order within a segment: row chunk, slice, rank group
+        const int per_chunk = g.n_slices * groups_per_slice;
+        const int per_seg = per_chunk * (kRowTiles / RT);
+        si = seg_begin + task / per_seg;
+        const int rem = task % per_seg;
+        rc = rem / per_chunk;
+        const int rem2 = rem - rc * per_chunk;
+        jb = rem2 / groups_per_slice;
+        grp = rem2 - jb * groups_per_slice;
+    }
     if (r.counts && si - seg_begin >= r.counts[kCntGather]) return;   // device-built routing
     const Seg sd = load_seg(r.seg, si);
     const int rb = rc * ROWS;                       // first segment row of the task
     const int n_rows = sd.n_rows() - rb;            // rows of the task, if positive
     if (n_rows <= 0) return;
-    const int rank = sd.rank(j);
-    const int ntiles = (rank + 15) / 16;
-    const int t0 = grp * NG;
-    if (t0 >= ntiles) return;
-    const int nt_here = min(NG, ntiles - t0);
+    // rank tiles of each slice (none past the lane's slices)
+    int ntj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ntj[j] = j < g.n_slices ? (sd.rank(j) + 15) / 16 : 0;
+    if (!tab) {
+        const int t0 = grp * NG;
+        if (t0 >= ntj[jb]) return;
+        c0 = (jb > 0 ? ntj[0] : 0) + (jb > 1 ? ntj[1] : 0) + (jb > 2 ? ntj[2] : 0) + t0;
+        cnt = min(NG, ntj[jb] - t0);
+    }
+    // tile i of the task: slice tj[i], rank tile tt[i]; the live ones
+    // (i < nt_here) come first
+    int tj[NG], tt[NG], nt_here = 0;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        int c = c0 + i, j = 0;
+        if (c >= ntj[0]) {
+            c -= ntj[0];
+            j = 1;
+            if (c >= ntj[1]) {
+                c -= ntj[1];
+                j = 2;
+                if (c >= ntj[2]) {
+                    c -= ntj[2];
+                    j = 3;
+                }
+            }
+        }
+        const bool live = i < cnt && c < ntj[j];
+        tj[i] = live ? j : 0;
+        tt[i] = live ? c : 0;
+        nt_here += live ? 1 : 0;
+    }
+    if (nt_here == 0) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int lb = lane >> 3, lc = lane & 7;        // load layout: row lb, chunk lc
@@ -139,8 +185,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
         const int tok = GATHER ? r.rows[sd.v_row() + sr] : sd.first_row() + sr;
         xr[i] = x + (int64_t)tok * ldx;
     }
-    const uint16_t *a_slice =
-        p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride + (int64_t)j * g.rank_pad * g.h_in;
+    const uint16_t *a_slot = p.A + (int64_t)(sd.slot() - 1) * g.a_slot_stride;
 
     __shared__ uint4 lds[kShrinkParts][(RT + NG) * 16][8];   // per wave: x rows, then A rows
     uint4(*const lw)[8] = lds[wave];
@@ -167,7 +212,8 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
         const uint16_t *ar[2 * NTH];
 #pragma unroll
         for (int i = 0; i < 2 * NTH; ++i)
-            ar[i] = a_slice + (int64_t)min(16 * t0 + 8 * i + lb, g.rank_pad - 1) * g.h_in;
+            ar[i] = a_slot + ((int64_t)tj[i / 2] * g.rank_pad +
+                              min(16 * tt[i / 2] + 8 * (i % 2) + lb, g.rank_pad - 1)) * g.h_in;
         uint4 xs[DP][2 * RT], as[DP][2 * NTH];
         const uint4 zero = make_uint4(0, 0, 0, 0);
         auto load = [&](uint4 (&xt)[2 * RT], uint4 (&at)[2 * NTH], int step) {
@@ -256,13 +302,13 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
     static_assert(sizeof(lds) >= kShrinkParts * ROWS * 16 * sizeof(float),
                   "reduction tile fits the staging LDS");
     float(*const red)[ROWS][16] = reinterpret_cast<float(*)[ROWS][16]>(&lds[0][0][0]);
-    const float scale = p.scale[sd.slot() * kMetaStride + j];
     static_assert(kShrinkParts == 4, "the combine below adds four parts");
     const int orow = threadIdx.x >> 2, ok4 = (threadIdx.x & 3) * 4;
-    float *const vrow =
-        v + (int64_t)(sd.v_row() + rb + orow) * g.v_stride + j * g.rank_pad + 16 * t0 + ok4;
+    float *const vrow = v + (int64_t)(sd.v_row() + rb + orow) * g.v_stride + ok4;
 #pragma unroll
     for (int nt = 0; nt < NG; ++nt) {
+        if (nt >= nt_here) break;                   // the same for the whole workgroup
+        const float scale = p.scale[sd.slot() * kMetaStride + tj[nt]];
         __syncthreads();
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -274,7 +320,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
             *reinterpret_cast<float4 *>(&red[wave][16 * rt + li][4 * lg]) = d;
         }
         __syncthreads();
-        if (orow < n_rows && orow < ROWS && nt < nt_here) {
+        if (orow < n_rows && orow < ROWS) {
             float4 u;
             float *uf = &u.x;
 #pragma unroll
@@ -287,9 +333,9 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
             if (vsplit) {
                 const float four[4] = {u.x, u.y, u.z, u.w};
                 store_vsplit<4>(reinterpret_cast<uint16_t *>(v), vsplit, vsplit_groups(g.rank_pad),
-                                sd.v_row() + rb + orow, j, 16 * (t0 + nt) + ok4, four);
+                                sd.v_row() + rb + orow, tj[nt], 16 * tt[nt] + ok4, four);
             } else {
-                *reinterpret_cast<float4 *>(vrow + 16 * nt) = u;
+                *reinterpret_cast<float4 *>(vrow + tj[nt] * g.rank_pad + 16 * tt[nt]) = u;
             }
         }
     }
@@ -298,11 +344,15 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
 template <bool FP16X, int NG, int RT, bool GATHER>
 __global__ __launch_bounds__(64 * kShrinkParts, 2) void k_shrink_mfma(
     LaneGeom g, PoolDev p, RoutingDev r, int n_tasks, int seg_begin, int groups_per_slice,
-    const uint16_t *__restrict__ x, int64_t ldx, float *__restrict__ v, int vsplit)
+    const uint32_t *__restrict__ tab, const uint16_t *__restrict__ x, int64_t ldx,
+    float *__restrict__ v, int vsplit)
 {
     touch_args(n_tasks, g, p, r, ldx);
-    shrink_mfma_task<FP16X, NG, RT, GATHER>(g, p, r, xcd_task(blockIdx.x, n_tasks), seg_begin,
-                                            groups_per_slice, x, ldx, v, vsplit);
+    // a table is ordered for the dispatch (heaviest first, spread over the
+    // XCDs by the block index); the block-index tasks are grouped per XCD
+    const int task = tab ? (int)blockIdx.x : xcd_task(blockIdx.x, n_tasks);
+    shrink_mfma_task<FP16X, NG, RT, GATHER>(g, p, r, task, seg_begin, groups_per_slice, tab, x,
+                                            ldx, v, vsplit);
 }
 
 // A task is one 128-column tile of one slice over a group of consecutive
@@ -552,21 +602,22 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
 template <int NG, int RT>
 static void launch_shrink_t(bool fp16, bool gather, dim3 grid, hipStream_t s, const LaneGeom &g,
                             const PoolDev &p, const RoutingDev &r, int seg_begin, int groups,
-                            const uint16_t *x, int64_t ldx, float *v, int vsplit)
+                            const uint32_t *tab, const uint16_t *x, int64_t ldx, float *v,
+                            int vsplit)
 {
     const dim3 block(64 * kShrinkParts);
     if (fp16 && gather)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
+                           (int)grid.x, seg_begin, groups, tab, x, ldx, v, vsplit);
     else if (fp16)
         hipLaunchKernelGGL((k_shrink_mfma<true, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
+                           (int)grid.x, seg_begin, groups, tab, x, ldx, v, vsplit);
     else if (gather)
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, true>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
+                           (int)grid.x, seg_begin, groups, tab, x, ldx, v, vsplit);
     else
         hipLaunchKernelGGL((k_shrink_mfma<false, NG, RT, false>), grid, block, 0, s, g, p, r,
-                           (int)grid.x, seg_begin, groups, x, ldx, v, vsplit);
+                           (int)grid.x, seg_begin, groups, tab, x, ldx, v, vsplit);
 }
 
 template <int NG>
@@ -576,21 +627,49 @@ static void launch_shrink_ng(int rt, bool fp16, bool gather, dim3 grid, hipStrea
                              int vsplit)
 {
     if (rt == 1)
-        launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
-                               vsplit);
+        launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, groups, nullptr, x,
+                               ldx, v, vsplit);
     else if (rt == 2)
-        launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
-                               vsplit);
+        launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, groups, nullptr, x,
+                               ldx, v, vsplit);
     else
-        launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, groups, x, ldx, v,
-                               vsplit);
+        launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, groups, nullptr, x,
+                               ldx, v, vsplit);
 }
 
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
-                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s)
+                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s,
+                              const uint32_t *tab, int n_tab, int tab_tiles, int tab_rows)
 {
     if (n_seg <= 0) return hipSuccess;
+    const uint16_t *xp = static_cast<const uint16_t *>(x);
+    const bool fp16 = g.x_fp16 != 0;
+    if (tab && n_tab > 0) {
+        // host-built tasks of whole segments: the smallest tile and row
+        // counts that cover the table (fewer registers, more workgroups per
+        // compute unit)
+        static_assert(kShrinkMaxTiles == 4 && kRowTiles == 4, "template sizes 1, 2, 4");
+        const int ng = tab_tiles <= 1 ? 1 : tab_tiles <= 2 ? 2 : 4;
+        const int rt = tab_rows <= 16 ? 1 : tab_rows <= 32 ? 2 : 4;
+        const dim3 grid((unsigned)n_tab);
+        auto go = [&](auto ng_c) {
+            constexpr int NG = decltype(ng_c)::value;
+            if (rt == 1)
+                launch_shrink_t<NG, 1>(fp16, gather, grid, s, g, p, r, seg_begin, 0, tab, xp, ldx,
+                                       v, vsplit);
+            else if (rt == 2)
+                launch_shrink_t<NG, 2>(fp16, gather, grid, s, g, p, r, seg_begin, 0, tab, xp, ldx,
+                                       v, vsplit);
+            else
+                launch_shrink_t<NG, 4>(fp16, gather, grid, s, g, p, r, seg_begin, 0, tab, xp, ldx,
+                                       v, vsplit);
+        };
+        if (ng == 1) go(std::integral_constant<int, 1>{});
+        else if (ng == 2) go(std::integral_constant<int, 2>{});
+        else go(std::integral_constant<int, 4>{});
+        return hipGetLastError();
+    }
     // Task shape: whole segments and up to 4 rank tiles (x and A read the
     // fewest times), made finer -- rows first, then ranks -- while the grid
     // is under kShrinkMinBlocks workgroups.
@@ -605,9 +684,7 @@ hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const Routing
     const int groups = (nt_per_slice + ng - 1) / ng;
     const int64_t blocks = blocks_of(ng, rt);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const uint16_t *xp = static_cast<const uint16_t *>(x);
     const dim3 grid((unsigned)blocks);
-    const bool fp16 = g.x_fp16 != 0;
     if (ng == 1)
         launch_shrink_ng<1>(rt, fp16, gather, grid, s, g, p, r, seg_begin, groups, xp, ldx, v,
                                 vsplit);

@@ -282,6 +282,13 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
         if (e != hipSuccess) return hip_fail(e, "shrink (decode) launch");
     }
     const int nt = (kmax + 15) / 16;
+    // a host-built table of the matrix-core tasks for this lane's slice count
+    const int sc = p->geom.n_slices;
+    const bool mtab = !r->device_built && sc >= 1 && sc <= kMetaStride && r->n_mtasks[sc] > 0;
+    const uint32_t *tab =
+        mtab ? reinterpret_cast<const uint32_t *>(r->dev + r->off_mtasks[sc]) : nullptr;
+    const int n_tab = mtab ? r->n_mtasks[sc] : 0;
+    const int tab_tiles = mtab ? r->mtask_tiles[sc] : 0, tab_rows = mtab ? r->mtask_rows[sc] : 0;
     if (I.n_prefill_segments > 0 && I.n_gather_segments > 0) {
         // Prefill and gather segments follow each other in the table, and the
         // host plan's row table holds the token row of every one of their
@@ -289,15 +296,18 @@ int32_t enqueue_shrink(const lora_pool *p, const lora_routing *r, const void *x,
         // from the table; the sums are the same).
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
                                           I.n_prefill_segments + I.n_gather_segments, nt, x,
-                                          ldx, v, vsplit, s);
+                                          ldx, v, vsplit, s, tab, n_tab,
+                                          tab_tiles, tab_rows);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill + gather) launch");
     } else if (I.n_prefill_segments > 0) {
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, false, I.n_decode_segments,
-                                          I.n_prefill_segments, nt, x, ldx, v, vsplit, s);
+                                          I.n_prefill_segments, nt, x, ldx, v, vsplit, s, tab,
+                                          n_tab, tab_tiles, tab_rows);
         if (e != hipSuccess) return hip_fail(e, "shrink (prefill) launch");
     } else if (I.n_gather_segments > 0) {
         hipError_t e = launch_shrink_mfma(p->geom, pd, rd, true, I.n_decode_segments,
-                                          I.n_gather_segments, nt, x, ldx, v, vsplit, s);
+                                          I.n_gather_segments, nt, x, ldx, v, vsplit, s, tab,
+                                          n_tab, tab_tiles, tab_rows);
         if (e != hipSuccess) return hip_fail(e, "shrink (gather) launch");
     }
     return LORA_OK;
@@ -434,6 +444,108 @@ void fill_gemv_tasks(Plan &pl, int32_t max_tokens)
         pl.tasks.clear();
 }
 
+// The matrix-core shrink tasks of the plan's prefill and gather segments, one
+// table per lane slice count s (1 .. the slices with a rank).  A task is
+// bound by the bytes its compute unit reads, about (rows + 16 * tiles) * h_in
+// * 2: a segment's tiles of all s slices are cut into as few tasks of at most
+// kShrinkMaxTiles tiles as fit, and, while the tasks are fewer than the
+// device's compute units, the heaviest segments are cut finer (the smallest
+// largest task whose count still fits one task per unit).  Tasks are stored
+// heaviest first, so a grid larger than the device starts the long ones
+// first.  A table of fewer than kShrinkMinBlocks tasks is not kept (the
+// block-index tasks split rows for small batches), nor tables that do not
+// fit the routing's words.
+void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
+{
+    pl.mtasks.clear();
+    for (int s = 0; s <= kMetaStride; ++s)
+        pl.mtask_off[s] = pl.mtask_n[s] = pl.mtask_tiles[s] = pl.mtask_rows[s] = 0;
+    const int64_t n_seg = (int64_t)pl.seg.size() / kSegWords;
+    int64_t first = 0;
+    while (first < n_seg && pl.seg[(size_t)(first * kSegWords) + 3] == kSegDecode) ++first;
+    if (first == n_seg || n_seg - first >= (int64_t)1 << 24) return;
+    int max_s = 0;
+    for (int64_t si = first; si < n_seg; ++si) {
+        const int32_t *d = &pl.seg[(size_t)(si * kSegWords)];
+        if (d[3] == kSegDecode) return;       // not the expected order: no tables
+        for (int j = 0; j < kMetaStride; ++j)
+            if (d[4 + j] > 0) max_s = std::max(max_s, j + 1);
+    }
+    struct Item { int32_t si, c0, cnt, cost; };
+    std::vector<int32_t> rows, tiles, m;
+    std::vector<Item> items;
+    for (int sc = 1; sc <= max_s; ++sc) {
+        rows.clear();
+        tiles.clear();
+        int64_t m0 = 0;
+        for (int64_t si = first; si < n_seg; ++si) {
+            const int32_t *d = &pl.seg[(size_t)(si * kSegWords)];
+            int32_t t = 0;
+            for (int j = 0; j < sc; ++j) t += (d[4 + j] + 15) / 16;
+            rows.push_back(std::min(d[2], (int32_t)kPrefillSegRows));
+            tiles.push_back(t);
+            m0 += (t + kShrinkMaxTiles - 1) / kShrinkMaxTiles;
+        }
+        const size_t ns = rows.size();
+        m.assign(ns, 0);
+        auto chunks_at = [&](int32_t c, bool store) {   // tasks if no task costs more than c
+            int64_t total = 0;
+            for (size_t i = 0; i < ns; ++i) {
+                if (tiles[i] == 0) continue;
+                const int32_t kmax = std::min((c - rows[i]) / 16, kShrinkMaxTiles);
+                if (kmax < 1) return INT64_MAX;
+                const int32_t mi = (tiles[i] + kmax - 1) / kmax;
+                if (store) m[i] = mi;
+                total += mi;
+            }
+            return total;
+        };
+        int32_t hi = 0, lo = 0;
+        for (size_t i = 0; i < ns; ++i) {
+            if (tiles[i] == 0) continue;
+            hi = std::max(hi, rows[i] + 16 * std::min(tiles[i], (int32_t)kShrinkMaxTiles));
+            lo = std::max(lo, rows[i] + 16);
+        }
+        if (hi == 0) continue;
+        int32_t c = hi;
+        if (m0 < n_cu) {
+            while (lo < hi) {                       // smallest cost whose tasks fit the units
+                const int32_t mid = lo + (hi - lo) / 2;
+                if (chunks_at(mid, false) <= n_cu) hi = mid;
+                else lo = mid + 1;
+            }
+            c = hi;
+        }
+        chunks_at(c, true);
+        items.clear();
+        for (size_t i = 0; i < ns; ++i) {
+            if (tiles[i] == 0) continue;
+            const int32_t base = tiles[i] / m[i], extra = tiles[i] % m[i];
+            int32_t c0 = 0;
+            for (int32_t k = 0; k < m[i]; ++k) {
+                const int32_t cnt = base + (k < extra ? 1 : 0);
+                items.push_back({(int32_t)i, c0, cnt, rows[i] + 16 * cnt});
+                c0 += cnt;
+            }
+        }
+        if ((int64_t)items.size() < kShrinkMinBlocks) continue;
+        std::stable_sort(items.begin(), items.end(),
+                         [](const Item &a, const Item &b) { return a.cost > b.cost; });
+        pl.mtask_off[sc] = (int32_t)pl.mtasks.size();
+        pl.mtask_n[sc] = (int32_t)items.size();
+        for (const Item &it : items) {
+            pl.mtasks.push_back(mfma_task_word(it.si, it.c0, it.cnt));
+            pl.mtask_tiles[sc] = std::max(pl.mtask_tiles[sc], it.cnt);
+            pl.mtask_rows[sc] = std::max(pl.mtask_rows[sc], rows[(size_t)it.si]);
+        }
+    }
+    const int64_t budget = (int64_t)max_tokens * (2 * kSegWords + 2) - pl.off_mtasks() - 64;
+    if ((int64_t)pl.mtasks.size() > budget) {
+        pl.mtasks.clear();
+        for (int s = 0; s <= kMetaStride; ++s) pl.mtask_off[s] = pl.mtask_n[s] = 0;
+    }
+}
+
 void append_inactive_rows(Plan &pl)
 {
     for (size_t t = 0; t < pl.tok.size(); ++t)
@@ -457,7 +569,7 @@ void push_seg(std::vector<int32_t> &seg, int32_t slot, int32_t v_row, int32_t n,
 template <class Resolve, class Ranks>
 int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t *seq_len,
                      int32_t max_loras, int32_t prefill_min_len, int32_t max_tokens,
-                     int32_t max_slots, Resolve resolve, Ranks ranks, Plan &pl)
+                     int32_t max_slots, Resolve resolve, Ranks ranks, Plan &pl, int32_t n_cu)
 {
     if (n_seq < 0) return fail(LORA_ERR_SHAPE, "n_seq < 0");
     if (n_seq > 0 && (!seq_adapter_id || !seq_len))
@@ -611,6 +723,7 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
     fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
     fill_gemv_tasks(pl, max_tokens);
+    fill_mfma_tasks(pl, max_tokens, n_cu);
     int32_t na = 0;
     for (int i = 0; i < n_seq; ++i) na += adm[i];
     pl.info.n_admitted_seqs = na;
@@ -635,7 +748,7 @@ int32_t plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const int32_t
 // slot are in row order; v holds the GEMV rows, then the gathered rows.
 template <class Ranks>
 void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefill,
-               int32_t max_slots, Ranks ranks, Plan &pl)
+               int32_t max_slots, Ranks ranks, Plan &pl, int32_t n_cu)
 {
     auto high_rank = [&](int32_t s) {
         int32_t m = 0;
@@ -714,6 +827,7 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     fill_row_meta(pl, ranks);
     append_inactive_rows(pl);
     fill_gemv_tasks(pl, n_rows);
+    fill_mfma_tasks(pl, n_rows, n_cu);
     pl.adm.clear();
     pl.distinct_slots = order;
     pl.slot_ranks.clear();
@@ -1020,6 +1134,18 @@ int32_t lora_routing_create(int32_t max_tokens, int32_t max_seqs, void *dev_mem,
     r->off_seg = r->off_row = r->off_tok = r->off_meta = 0;
     r->tile_steps[0] = r->tile_steps[1] = 0;
     r->off_tasks = r->n_tasks = 0;
+    for (int sc = 0; sc <= kMetaStride; ++sc)
+        r->off_mtasks[sc] = r->n_mtasks[sc] = r->mtask_tiles[sc] = r->mtask_rows[sc] = 0;
+    {
+        // compute units of the current device (the shrink task tables are cut for them)
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            r->n_cu = n;
+        else
+            r->n_cu = kPlanComputeUnits;
+    }
     r->pool_max_slots = 0;
     r->device_built = false;
     r->off_counts = 0;
@@ -1065,7 +1191,7 @@ int32_t lora_build_routing(const lora_pool *p, int32_t n_seq, const int32_t *seq
         return p->h_rank[(size_t)slot * kMetaStride + j];
     };
     if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
-                                  r->max_tokens, p->desc.max_slots, resolve, ranks, pl))
+                                  r->max_tokens, p->desc.max_slots, resolve, ranks, pl, r->n_cu))
         return rc;
     if (int32_t rc = upload_plan(p, r, stream)) return rc;
     if (admitted_out)
@@ -1090,7 +1216,7 @@ int32_t lora_build_routing_rows(const lora_pool *p, int32_t n_rows, const int32_
         if (s != 0 && (s < 1 || s > p->desc.max_slots || p->slot_to_id[s] == 0))
             return fail(LORA_ERR_SLOT, "row %d names slot %d, which holds no adapter", i, s);
     }
-    plan_rows(n_rows, row_slot, row_prefill, p->desc.max_slots, ranks, r->plan);
+    plan_rows(n_rows, row_slot, row_prefill, p->desc.max_slots, ranks, r->plan, r->n_cu);
     return upload_plan(p, r, stream);
 }
 
@@ -1124,6 +1250,12 @@ int32_t upload_plan(const lora_pool *p, lora_routing *r, void *stream)
     r->off_meta = (int32_t)pl.off_meta();
     r->off_tasks = (int32_t)pl.off_tasks();
     r->n_tasks = (int32_t)pl.tasks.size();
+    for (int sc = 0; sc <= kMetaStride; ++sc) {
+        r->off_mtasks[sc] = (int32_t)(pl.off_mtasks() + pl.mtask_off[sc]);
+        r->n_mtasks[sc] = pl.mtask_n[sc];
+        r->mtask_tiles[sc] = pl.mtask_tiles[sc];
+        r->mtask_rows[sc] = pl.mtask_rows[sc];
+    }
     r->tile_steps[0] = pl.tile_steps[0];
     r->tile_steps[1] = pl.tile_steps[1];
     r->device_built = false;
@@ -1178,7 +1310,7 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
     };
     Plan pl;
     if (int32_t rc = plan_routing(n_seq, seq_adapter_id, seq_len, max_loras, prefill_min_len,
-                                  max_tokens, max_slots, resolve, ranks, pl))
+                                  max_tokens, max_slots, resolve, ranks, pl, kPlanComputeUnits))
         return rc;
     if (!words_out || !offsets_out || !info_out)
         return fail(LORA_ERR_ARG, "null output");
@@ -1189,6 +1321,8 @@ int32_t lora_plan_routing(int32_t n_seq, const int32_t *seq_adapter_id, const in
     offsets_out[0] = 0;
     offsets_out[1] = (int32_t)pl.off_row();
     offsets_out[2] = (int32_t)pl.off_tok();
+    offsets_out[3] = (int32_t)pl.off_tasks();
+    offsets_out[4] = (int32_t)pl.off_mtask_header();
     *info_out = pl.info;
     if (admitted_out)
         for (int i = 0; i < n_seq; ++i) admitted_out[i] = pl.adm[i];
@@ -1214,7 +1348,7 @@ int32_t lora_plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *r
             return fail(LORA_ERR_SLOT, "row %d names slot %d, which holds no adapter", i, s);
     }
     Plan pl;
-    plan_rows(n_rows, row_slot, row_prefill, max_slots, ranks, pl);
+    plan_rows(n_rows, row_slot, row_prefill, max_slots, ranks, pl, kPlanComputeUnits);
     if (pl.words() > words_capacity)
         return fail(LORA_ERR_CAPACITY, "plan needs %lld words > %lld", (long long)pl.words(),
                     (long long)words_capacity);
@@ -1222,6 +1356,8 @@ int32_t lora_plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *r
     offsets_out[0] = 0;
     offsets_out[1] = (int32_t)pl.off_row();
     offsets_out[2] = (int32_t)pl.off_tok();
+    offsets_out[3] = (int32_t)pl.off_tasks();
+    offsets_out[4] = (int32_t)pl.off_mtask_header();
     *info_out = pl.info;
     return LORA_OK;
 }
@@ -1267,6 +1403,7 @@ int32_t build_routing_device(const lora_pool *p, const int32_t *tok_slot, int32_
     r->off_counts = (int32_t)off_counts;
     r->device_built = true;
     r->n_tasks = 0;
+    for (int sc = 0; sc <= kMetaStride; ++sc) r->n_mtasks[sc] = 0;
     r->max_gather_rows = kPrefillSegRows;   // segment sizes are known on the device only
     r->decode_rows = 0;
     // A MoE layer's dispatched rows spread over (adapter, expert) pairs, so

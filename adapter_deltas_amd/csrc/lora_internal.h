@@ -32,6 +32,8 @@ constexpr int kMfmaExpandCols = 128;                    // columns per prefill e
 constexpr int kExpandTargetBlocks = LORA_EXPAND_BLOCKS; // prefill expand grid to aim for
 constexpr int kExpandMaxGroup = 32;                     // prefill segments per expand task
 constexpr int kShrinkMinBlocks = 128;                   // prefill shrink grid below which tasks shrink
+constexpr int kShrinkMaxTiles = 4;                      // rank tiles of one host-built shrink task
+constexpr int kPlanComputeUnits = 256;                  // device size a host-only plan assumes
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
 enum SegKind : int32_t { kSegDecode = 0, kSegPrefill = 1, kSegGather = 2 };
@@ -146,6 +148,14 @@ inline int32_t gemv_task_word(int32_t si, int j, int kb)
 {
     return si | (j << 24) | (kb << 26);
 }
+// A matrix-core shrink task of a host-built table: segment si (counted from
+// the first prefill or gather segment, < 2^24) and cnt (1..kShrinkMaxTiles)
+// consecutive rank tiles from number c0 (< 64) of the segment's tiles
+// numbered across its slices.
+inline int32_t mfma_task_word(int32_t si, int c0, int cnt)
+{
+    return (int32_t)((uint32_t)si | ((uint32_t)c0 << 24) | ((uint32_t)(cnt - 1) << 30));
+}
 hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                              int n_seg, const void *x, int64_t ldx, float *y, int64_t ldy,
                              hipStream_t s);
@@ -154,7 +164,9 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
                               float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_shrink_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int nt_per_slice,
-                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s);
+                              const void *x, int64_t ldx, float *v, int vsplit, hipStream_t s,
+                              const uint32_t *tab = nullptr, int n_tab = 0, int tab_tiles = 0,
+                              int tab_rows = 0);
 hipError_t launch_expand_mfma(const LaneGeom &g, const PoolDev &p, const RoutingDev &r,
                               bool gather, int seg_begin, int n_seg, int group, int max_rank,
                               int max_seg_rows, const float *v, float *y, int64_t ldy,
@@ -222,6 +234,16 @@ struct Plan {
     // the live GEMV shrink tasks, one word each (gemv_task_word), decode
     // segments in order, slices, then rank blocks of kKBlock
     std::vector<int32_t> tasks;
+    // the matrix-core shrink tasks of the prefill and gather segments, one
+    // table per lane slice count s = 1 .. kMetaStride (mtask_n[s] words from
+    // mtask_off[s] of mtasks; none: 0), see mfma_task_word.  Packed after an
+    // 8-word header {offset from the header, count} per s.
+    std::vector<int32_t> mtasks;
+    int32_t mtask_off[kMetaStride + 1] = {}, mtask_n[kMetaStride + 1] = {};
+    // per table: most tiles of a task and most rows of a segment (the
+    // kernel's tile and row template sizes cover them)
+    int32_t mtask_tiles[kMetaStride + 1] = {}, mtask_rows[kMetaStride + 1] = {};
+    static constexpr int kMtaskHeader = 2 * kMetaStride;
     std::vector<int32_t> slot_ranks;   // per distinct slot: kMetaStride ranks
     std::vector<uint8_t> adm;
     std::vector<int32_t> distinct_slots;
@@ -231,7 +253,9 @@ struct Plan {
     int64_t off_tok() const { return (off_row() + (int64_t)rows.size() + 3) / 4 * 4; }
     int64_t off_meta() const { return (off_tok() + (int64_t)tok.size() + 3) / 4 * 4; }
     int64_t off_tasks() const { return off_meta() + (int64_t)meta.size(); }
-    int64_t words() const { return off_tasks() + (int64_t)tasks.size(); }
+    int64_t off_mtask_header() const { return off_tasks() + (int64_t)tasks.size(); }
+    int64_t off_mtasks() const { return off_mtask_header() + kMtaskHeader; }
+    int64_t words() const { return off_mtasks() + (int64_t)mtasks.size(); }
     void pack(int32_t *w) const
     {
         int64_t o = 0;
@@ -242,6 +266,11 @@ struct Plan {
         while (o < off_meta()) w[o++] = 0;
         for (int32_t a : meta) w[o++] = a;
         for (int32_t a : tasks) w[o++] = a;
+        for (int sc = 1; sc <= kMetaStride; ++sc) {
+            w[o++] = mtask_n[sc] ? kMtaskHeader + mtask_off[sc] : 0;
+            w[o++] = mtask_n[sc];
+        }
+        for (int32_t a : mtasks) w[o++] = a;
     }
 };
 }  // namespace lora
@@ -259,6 +288,11 @@ struct lora_routing {
     int32_t off_meta;                 // per active row slot and ranks (host-built only)
     int32_t tile_steps[2];            // Plan::tile_steps of the current batch
     int32_t off_tasks, n_tasks;       // the live GEMV shrink tasks (host-built only)
+    int32_t off_mtasks[lora::kMetaStride + 1];   // matrix-core shrink task table per lane
+    int32_t n_mtasks[lora::kMetaStride + 1];     // slice count (host-built only; 0: none)
+    int32_t mtask_tiles[lora::kMetaStride + 1];  // most tiles of a task of each table
+    int32_t mtask_rows[lora::kMetaStride + 1];   // most rows of a segment of each table
+    int32_t n_cu;                     // compute units of the device the routing is on
     lora_routing_info info;
     int32_t pool_max_slots;           // slots of the pool the ids were resolved in
     bool device_built;                // counts on the device, info holds bounds

@@ -184,13 +184,26 @@ def lora_routing_get_info(routing) -> dict:
     return info.as_dict()
 
 
+def _task_tables(words, offs):
+    """The shrink task words of a packed plan: the decode (GEMV) tasks, and
+    the matrix-core task table per lane slice count (absent: no table)."""
+    h = offs[4]
+    mfma = {}
+    for s in range(1, 5):
+        o, n = int(words[h + 2 * (s - 1)]), int(words[h + 2 * (s - 1) + 1])
+        if n:
+            mfma[s] = words[h + o:h + o + n].view(np.uint32).copy()
+    return dict(gemv_tasks=words[offs[3]:h].view(np.uint32).copy(), mfma_tasks=mfma)
+
+
 def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resident,
                       max_slots, max_tokens, resident_rank=None):
     """Host-only routing plan.  `resident` maps registry id -> slot and
     `resident_rank` (optional) registry id -> per-slice ranks.
 
-    Returns a dict with info counts, admitted (bool array), and the tables
-    seg (int32 [n_seg, 16]), rows (int32 [n_active]) and tok_slot (int32 [T]).
+    Returns a dict with info counts, admitted (bool array), the tables seg
+    (int32 [n_seg, 16]), rows (int32 [n_active]) and tok_slot (int32 [T]),
+    and the shrink task words gemv_tasks and mfma_tasks ({slice count: words}).
     """
     i32p = ctypes.POINTER(ctypes.c_int32)
     ids = _seq_ids(seq_adapter_id)
@@ -203,7 +216,7 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
         rrk[i, :len(rk)] = rk
     cap = lora_routing_bytes(max_tokens) // 4
     words = np.zeros(cap, dtype=np.int32)
-    offs = np.zeros(3, dtype=np.int32)
+    offs = np.zeros(5, dtype=np.int32)
     info = L.RoutingInfo()
     adm = np.zeros(max(len(ids), 1), dtype=np.uint8)
     _check(_lib().lora_plan_routing(
@@ -217,7 +230,8 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
         info=d, admitted=adm[:len(ids)].astype(bool),
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
-        tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy())
+        tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
+        **_task_tables(words, offs))
 
 
 def lora_routing_token_slots(routing) -> int:
@@ -256,8 +270,9 @@ def lora_build_routing_rows(pool, row_slot, row_prefill, routing, stream=None) -
 def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
     """Host-only plan from per-row slots.  slot_rank: int32 [max_slots + 1, 4].
 
-    Returns a dict with info counts and the tables seg (int32 [n_seg, 16]),
-    rows (int32 [n_active]) and tok_slot (int32 [n_rows])."""
+    Returns a dict with info counts, the tables seg (int32 [n_seg, 16]),
+    rows (int32 [n_active]) and tok_slot (int32 [n_rows]), and the shrink task
+    words gemv_tasks and mfma_tasks ({slice count: words})."""
     i32p = ctypes.POINTER(ctypes.c_int32)
     slots = np.ascontiguousarray(row_slot, dtype=np.int32)
     pre = None if row_prefill is None else np.ascontiguousarray(row_prefill, dtype=np.uint8)
@@ -266,7 +281,7 @@ def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
         raise ValueError("slot_rank must be [max_slots + 1, 4]")
     cap = lora_routing_bytes(max_tokens) // 4
     words = np.zeros(cap, dtype=np.int32)
-    offs = np.zeros(3, dtype=np.int32)
+    offs = np.zeros(5, dtype=np.int32)
     info = L.RoutingInfo()
     _check(_lib().lora_plan_rows(
         len(slots), slots.ctypes.data_as(i32p),
@@ -278,7 +293,8 @@ def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
         info=d,
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
-        tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy())
+        tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
+        **_task_tables(words, offs))
 
 
 def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:

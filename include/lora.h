@@ -286,8 +286,16 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  *                 of 4 words on, 4 words per active row {slot, rank0 |
  *                 rank1 << 16, rank2 | rank3 << 16, 0}, then (possibly
  *                 none) one word per live decode shrink task {segment |
- *                 slice << 24 | 8-rank block << 26}
- *   offsets_out   host int32 [3]
+ *                 slice << 24 | 8-rank block << 26} at offsets_out[3]; at
+ *                 offsets_out[4] an 8-word header {offset from the header,
+ *                 count} per lane slice count 1..4 of the matrix-core shrink
+ *                 task tables that follow (count 0: no table; the kernels
+ *                 then number tasks by block index), one word per task
+ *                 {segment counted from the first prefill or gather segment
+ *                 | first rank tile << 24 | (tiles - 1) << 30}, a segment's
+ *                 16-rank tiles numbered across its slices (slice 0's, then
+ *                 slice 1's, ...), heaviest task first
+ *   offsets_out   host int32 [5]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]
  *

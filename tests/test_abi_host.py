@@ -227,9 +227,88 @@ def test_plan_random_batches(m, seed):
     ranks = {i: [int(x) for x in rng.integers(1, 100, size=4)] for i in ids_pool}
     p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T, resident_rank=ranks)
     _check_plan(p, ids, lens, resident, cap, pmin, ranks)
+    _check_mfma_tables(p)
     inv = {s: i for i, s in resident.items()}
     for d in p["seg"]:
         assert list(d[4:8]) == ranks[inv[d[0]]]
+
+
+N_CU = 256          # the device size the host-only plans assume
+
+
+def _check_mfma_tables(p):
+    """Every table covers each prefill/gather segment's 16-rank tiles of its
+    first s slices exactly once, in tasks of 1..4 consecutive tiles, heaviest
+    (rows + 16 * tiles) first, and has at least 128 tasks."""
+    seg = p["seg"]
+    first = p["info"]["n_decode_segments"]
+    rest = seg[first:]
+    for s, words in p["mfma_tasks"].items():
+        assert 1 <= s <= 4 and len(words) >= 128
+        si = (words & 0xFFFFFF).astype(np.int64)
+        c0 = ((words >> 24) & 63).astype(np.int64)
+        cnt = ((words >> 30) + 1).astype(np.int64)
+        assert np.all(si < len(rest))
+        tiles = ((rest[:, 4:4 + s] + 15) // 16).sum(axis=1)
+        cover = [np.zeros(t, np.int64) for t in tiles]
+        for a, b, k in zip(si, c0, cnt):
+            assert b + k <= tiles[a]
+            cover[a][b:b + k] += 1
+        assert all(np.all(c == 1) for c in cover)
+        cost = np.minimum(rest[si, 2], 64) + 16 * cnt
+        assert np.all(np.diff(cost) <= 0)
+
+
+def test_mfma_task_tables_balance_the_units(m):
+    """Prefill chunks of 6 adapters (ranks 8, 8, 16, 16, 64, 64, two slices):
+    fewer whole-segment tasks than compute units, so the heavy segments are
+    cut until the largest task is as small as 256 tasks allow."""
+    resident = {5 + i: i + 1 for i in range(6)}
+    ranks = {5 + i: [r, r, 0, 0] for i, r in enumerate((8, 8, 16, 16, 64, 64))}
+    lens = [604, 1925, 1047, 409, 1479, 965, 598, 1283]
+    ids = [5 + i for i in (5, 0, 2, 4, 1, 3, 0, 5)]
+    p = m.lora_plan_routing(ids, lens, 0, 64, resident, 8, sum(lens), resident_rank=ranks)
+    _check_mfma_tables(p)
+    assert sorted(p["mfma_tasks"]) == [1, 2]
+    rest = p["seg"][p["info"]["n_decode_segments"]:]
+    for s, words in p["mfma_tasks"].items():
+        cnt = (words >> 30) + 1
+        cost = np.minimum(rest[words & 0xFFFFFF, 2], 64) + 16 * cnt
+        assert len(words) <= N_CU
+        # no cut into smaller pieces would still fit the units
+        tiles = ((rest[:, 4:4 + s] + 15) // 16)
+        tiles = tiles.sum(axis=1)
+        rows = np.minimum(rest[:, 2], 64)
+        c = int(cost.max()) - 1
+        kmax = np.minimum((c - rows) // 16, 4)
+        assert np.any(kmax < 1) or np.sum(-(-tiles // np.maximum(kmax, 1))) > N_CU
+    def cost(words):
+        return np.minimum(rest[words & 0xFFFFFF, 2], 64) + 16 * ((words >> 30) + 1)
+
+    # one slice: 98 light and 38 heavy segments; a full segment and one tile
+    # a task fits (at most 250 tasks)
+    assert cost(p["mfma_tasks"][1]).max() == 64 + 16
+    # two slices: one tile a task would not (500); two do, and a light
+    # segment's task takes its tile of both slices, reading its x rows once
+    w2 = p["mfma_tasks"][2]
+    assert cost(w2).max() == 64 + 32
+    for i in np.nonzero(rest[:, 4] <= 16)[0]:
+        mine = w2[(w2 & 0xFFFFFF) == i]
+        assert len(mine) == 1 and (mine[0] >> 30) + 1 == 2
+
+
+def test_mfma_task_tables_small_and_many(m):
+    """A small batch has no table (its tasks are cut by rows instead); many
+    small gather groups get one task per segment covering both slices."""
+    resident = {5: 1}
+    p = m.lora_plan_routing([5], [300], 0, 64, resident, 4, 300, resident_rank={5: [16, 16, 0, 0]})
+    assert p["mfma_tasks"] == {}
+    slot_rank = np.zeros((301, 4), np.int32)
+    slot_rank[1:, :2] = 16
+    row_slot = np.repeat(np.arange(1, 301), 12).astype(np.int32)
+    p = m.lora_plan_rows(row_slot, np.ones(len(row_slot), np.uint8), 300, slot_rank, len(row_slot))
+    _check_mfma_tables(p)
+    assert len(p["mfma_tasks"][2]) == len(p["mfma_tasks"][1]) == 300
 
 
 def test_plan_errors(m):
@@ -307,6 +386,7 @@ def test_plan_rows_random(m, seed):
     row_prefill = (rng.random(n) < [0.0, 0.5, 1.0][seed % 3]) if seed % 4 else None
     p = m.lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max(n, 1))
     _check_rows_plan(p, row_slot, row_prefill, slot_rank)
+    _check_mfma_tables(p)
 
 
 def test_plan_rows_cuts_small_groups_at_16(m):
