@@ -55,7 +55,6 @@ __device__ __forceinline__ Seg load_seg(const int32_t *seg, int si)
 // range of its share, so tasks that read the same rows or factor tiles (which
 // sit next to each other in task order) share an L2.  Placement only changes
 // speed, never results.
-constexpr int kXcds = 8;
 __device__ __forceinline__ int xcd_task(int b, int n)
 {
     // XCD x < n % 8 has q + 1 tasks, the others q (written without a branch,

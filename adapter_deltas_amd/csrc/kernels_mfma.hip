@@ -98,9 +98,10 @@ __device__ __forceinline__ int chunk_pos(int row, int c) { return c ^ (row & 7);
 // reorders them through the wave's own LDS into the MFMA operand layout
 // (lane l: row l % 16, elements 8 (l / 16) .. + 7 of the K-step).
 // Tasks come from a host-built table (word: segment | c0 << 24 |
-// (cnt - 1) << 30, whole segments, heaviest first) when the routing has one
-// for the lane's slice count; otherwise from the block index: row chunk,
-// slice, group of NG tiles.  Either way a (row, rank) sum is the same.
+// (cnt - 1) << 30, whole segments; block b takes word b, laid out for XCD
+// b % 8) when the routing has one for the lane's slice count; otherwise from
+// the block index: row chunk, slice, group of NG tiles.  Either way a
+// (row, rank) sum is the same.
 // vsplit > 0: v is written in the split form of the base projection's
 // epilogue (rows of vsplit bf16) instead of fp32.
 template <bool FP16X, int NG, int RT, bool GATHER>
@@ -116,6 +117,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
     int si, rc, c0 = 0, cnt = 0, jb = 0, grp = 0;
     if (tab) {
         const uint32_t w = tab[task];
+        if (w == (uint32_t)kMfmaTaskNone) return;   // an empty place of the table
         si = seg_begin + (int)(w & 0xffffffu);
         rc = 0;
         c0 = (int)((w >> 24) & 63u);
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(64 * kShrinkParts, 2) void k_shrink_mfma(
     float *__restrict__ v, int vsplit)
 {
     touch_args(n_tasks, g, p, r, ldx);
-    // a table is ordered for the dispatch (heaviest first, spread over the
-    // XCDs by the block index); the block-index tasks are grouped per XCD
+    // a table is laid out for the dispatch (word b is a task of XCD b % 8,
+    // each XCD's heaviest first); the block-index tasks are grouped per XCD
     const int task = tab ? (int)blockIdx.x : xcd_task(blockIdx.x, n_tasks);
     shrink_mfma_task<FP16X, NG, RT, GATHER>(g, p, r, task, seg_begin, groups_per_slice, tab, x,
                                             ldx, v, vsplit);

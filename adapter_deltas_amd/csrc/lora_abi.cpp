@@ -450,11 +450,11 @@ void fill_gemv_tasks(Plan &pl, int32_t max_tokens)
 // * 2: a segment's tiles of all s slices are cut into as few tasks of at most
 // kShrinkMaxTiles tiles as fit, and, while the tasks are fewer than the
 // device's compute units, the heaviest segments are cut finer (the smallest
-// largest task whose count still fits one task per unit).  Tasks are stored
-// heaviest first, so a grid larger than the device starts the long ones
-// first.  A table of fewer than kShrinkMinBlocks tasks is not kept (the
-// block-index tasks split rows for small batches), nor tables that do not
-// fit the routing's words.
+// largest task whose count still fits one task per unit).  A segment's
+// tasks go to one XCD, and each XCD's tasks are stored heaviest first, so a
+// grid larger than the device starts the long ones first.  A table of fewer
+// than kShrinkMinBlocks tasks is not kept (the block-index tasks split rows
+// for small batches), nor tables that do not fit the routing's words.
 void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
 {
     pl.mtasks.clear();
@@ -472,7 +472,8 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
             if (d[4 + j] > 0) max_s = std::max(max_s, j + 1);
     }
     struct Item { int32_t si, c0, cnt, cost; };
-    std::vector<int32_t> rows, tiles, m;
+    std::vector<int32_t> rows, tiles, m, seg_tasks, order, xcd_of;
+    std::vector<int64_t> seg_cost;
     std::vector<Item> items;
     for (int sc = 1; sc <= max_s; ++sc) {
         rows.clear();
@@ -529,12 +530,51 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
             }
         }
         if ((int64_t)items.size() < kShrinkMinBlocks) continue;
+        // Block b runs on XCD b % kXcds.  The tasks of one segment share its
+        // x rows, so a segment goes to one XCD (its L2 then reads them once):
+        // segments by decreasing cost to the XCD with the least cost among
+        // those with room for its tasks (an equal share of the units).
+        seg_cost.assign(ns, 0);
+        seg_tasks.assign(ns, 0);
+        for (const Item &it : items) {
+            seg_cost[(size_t)it.si] += it.cost;
+            ++seg_tasks[(size_t)it.si];
+        }
+        order.clear();
+        for (size_t i = 0; i < ns; ++i)
+            if (seg_tasks[i]) order.push_back((int32_t)i);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t b) { return seg_cost[a] > seg_cost[b]; });
+        const int64_t room = std::max<int64_t>((int64_t)(items.size() + kXcds - 1) / kXcds,
+                                               n_cu / kXcds);
+        int64_t xcost[kXcds] = {}, xcount[kXcds] = {};
+        xcd_of.assign(ns, 0);
+        for (int32_t i : order) {
+            int best = -1;
+            for (int x = 0; x < kXcds; ++x)
+                if (xcount[x] + seg_tasks[i] <= room && (best < 0 || xcost[x] < xcost[best]))
+                    best = x;
+            if (best < 0)
+                for (int x = 0; x < kXcds; ++x)
+                    if (best < 0 || xcount[x] < xcount[best]) best = x;
+            xcd_of[i] = best;
+            xcost[best] += seg_cost[i];
+            xcount[best] += seg_tasks[i];
+        }
+        // per XCD heaviest first, interleaved so that block b is its XCD's
+        // (b / kXcds)-th task; empty places hold kMfmaTaskNone
         std::stable_sort(items.begin(), items.end(),
                          [](const Item &a, const Item &b) { return a.cost > b.cost; });
+        int64_t longest = 0;
+        for (int x = 0; x < kXcds; ++x) longest = std::max(longest, xcount[x]);
         pl.mtask_off[sc] = (int32_t)pl.mtasks.size();
-        pl.mtask_n[sc] = (int32_t)items.size();
+        pl.mtask_n[sc] = (int32_t)(longest * kXcds);
+        pl.mtasks.resize(pl.mtasks.size() + (size_t)(longest * kXcds), kMfmaTaskNone);
+        int64_t next[kXcds] = {};
         for (const Item &it : items) {
-            pl.mtasks.push_back(mfma_task_word(it.si, it.c0, it.cnt));
+            const int x = xcd_of[(size_t)it.si];
+            pl.mtasks[(size_t)(pl.mtask_off[sc] + next[x]++ * kXcds + x)] =
+                mfma_task_word(it.si, it.c0, it.cnt);
             pl.mtask_tiles[sc] = std::max(pl.mtask_tiles[sc], it.cnt);
             pl.mtask_rows[sc] = std::max(pl.mtask_rows[sc], rows[(size_t)it.si]);
         }

@@ -294,7 +294,10 @@ int32_t lora_routing_get_info(const lora_routing *routing, lora_routing_info *in
  *                 {segment counted from the first prefill or gather segment
  *                 | first rank tile << 24 | (tiles - 1) << 30}, a segment's
  *                 16-rank tiles numbered across its slices (slice 0's, then
- *                 slice 1's, ...), heaviest task first
+ *                 slice 1's, ...); word b is run by block b, which the
+ *                 device places on XCD b % 8: a segment's tasks sit in one
+ *                 such residue class, heaviest first, and places left
+ *                 empty hold -1
  *   offsets_out   host int32 [5]
  *   info_out      counts, as lora_routing_get_info
  *   admitted_out  optional host uint8 [n_seq]

@@ -236,15 +236,27 @@ def test_plan_random_batches(m, seed):
 N_CU = 256          # the device size the host-only plans assume
 
 
+XCDS = 8
+NONE = 0xFFFFFFFF     # an empty place of a task table
+
+
+def _live(words):
+    return words[words != NONE]
+
+
 def _check_mfma_tables(p):
     """Every table covers each prefill/gather segment's 16-rank tiles of its
-    first s slices exactly once, in tasks of 1..4 consecutive tiles, heaviest
-    (rows + 16 * tiles) first, and has at least 128 tasks."""
+    first s slices exactly once, in tasks of 1..4 consecutive tiles, has at
+    least 128 tasks, keeps a segment's tasks in one XCD residue class (word
+    b runs on XCD b % 8), heaviest (rows + 16 * tiles) first in each class,
+    and gives no class more than an equal share of the units (or of the
+    tasks) by more than one segment's tasks."""
     seg = p["seg"]
     first = p["info"]["n_decode_segments"]
     rest = seg[first:]
-    for s, words in p["mfma_tasks"].items():
-        assert 1 <= s <= 4 and len(words) >= 128
+    for s, table in p["mfma_tasks"].items():
+        words = _live(table)
+        assert 1 <= s <= 4 and len(words) >= 128 and len(table) % XCDS == 0
         si = (words & 0xFFFFFF).astype(np.int64)
         c0 = ((words >> 24) & 63).astype(np.int64)
         cnt = ((words >> 30) + 1).astype(np.int64)
@@ -255,8 +267,19 @@ def _check_mfma_tables(p):
             assert b + k <= tiles[a]
             cover[a][b:b + k] += 1
         assert all(np.all(c == 1) for c in cover)
-        cost = np.minimum(rest[si, 2], 64) + 16 * cnt
-        assert np.all(np.diff(cost) <= 0)
+        home = {}
+        room = max(-(-len(words) // XCDS), N_CU // XCDS)
+        most = np.bincount(si).max()        # tasks of one segment: the packing grain
+        for x in range(XCDS):
+            col = table[x::XCDS]
+            live = col != NONE
+            assert np.all(live[:live.sum()])            # empty places only at the end
+            w = col[live]
+            cost = np.minimum(rest[w & 0xFFFFFF, 2], 64) + 16 * ((w >> 30) + 1)
+            assert np.all(np.diff(cost) <= 0)
+            for a in (w & 0xFFFFFF):
+                assert home.setdefault(int(a), x) == x
+            assert len(w) <= room + most - 1
 
 
 def test_mfma_task_tables_balance_the_units(m):
@@ -271,7 +294,8 @@ def test_mfma_task_tables_balance_the_units(m):
     _check_mfma_tables(p)
     assert sorted(p["mfma_tasks"]) == [1, 2]
     rest = p["seg"][p["info"]["n_decode_segments"]:]
-    for s, words in p["mfma_tasks"].items():
+    for s, table in p["mfma_tasks"].items():
+        words = _live(table)
         cnt = (words >> 30) + 1
         cost = np.minimum(rest[words & 0xFFFFFF, 2], 64) + 16 * cnt
         assert len(words) <= N_CU
@@ -282,7 +306,8 @@ def test_mfma_task_tables_balance_the_units(m):
         c = int(cost.max()) - 1
         kmax = np.minimum((c - rows) // 16, 4)
         assert np.any(kmax < 1) or np.sum(-(-tiles // np.maximum(kmax, 1))) > N_CU
-    def cost(words):
+    def cost(table):
+        words = _live(table)
         return np.minimum(rest[words & 0xFFFFFF, 2], 64) + 16 * ((words >> 30) + 1)
 
     # one slice: 98 light and 38 heavy segments; a full segment and one tile
@@ -290,7 +315,7 @@ def test_mfma_task_tables_balance_the_units(m):
     assert cost(p["mfma_tasks"][1]).max() == 64 + 16
     # two slices: one tile a task would not (500); two do, and a light
     # segment's task takes its tile of both slices, reading its x rows once
-    w2 = p["mfma_tasks"][2]
+    w2 = _live(p["mfma_tasks"][2])
     assert cost(w2).max() == 64 + 32
     for i in np.nonzero(rest[:, 4] <= 16)[0]:
         mine = w2[(w2 & 0xFFFFFF) == i]
@@ -308,7 +333,7 @@ def test_mfma_task_tables_small_and_many(m):
     row_slot = np.repeat(np.arange(1, 301), 12).astype(np.int32)
     p = m.lora_plan_rows(row_slot, np.ones(len(row_slot), np.uint8), 300, slot_rank, len(row_slot))
     _check_mfma_tables(p)
-    assert len(p["mfma_tasks"][2]) == len(p["mfma_tasks"][1]) == 300
+    assert len(_live(p["mfma_tasks"][2])) == len(_live(p["mfma_tasks"][1])) == 300
 
 
 def test_plan_errors(m):
