@@ -450,20 +450,39 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
     };
 
     int staged = 0;                               // slot whose B tile is in bs
+    // B tile of a slot into bs: PER 16-byte chunks per thread, loaded in
+    // batches (of up to 8, or 4) whose loads are all issued before the first LDS
+    // write (a loop of load-then-write waited out one load latency per chunk:
+    // eight for a rank-128 tile).  Every load reads a clamped address in the
+    // slot's rows; chunks past the slice or the rank are written as zeros.
+    constexpr int PER = COLS * CPR / (64 * WAVES);
+    constexpr int BMAX = WAVES == 1 ? 4 : 8;    // the one-wave forms hold more registers
+    constexpr int BATCH = PER < BMAX ? PER : BMAX;
+    static_assert(PER % BATCH == 0, "whole batches");
     auto stage_b = [&](Seg sd) {           // uniform over the workgroup
         const int slot = sd.slot();
         if (slot == staged) return;
-        __syncthreads();
         const int rank = sd.rank(j);
         const uint16_t *Bn = p.Bn + (int64_t)(slot - 1) * g.bt_slot_stride + bt_off;
-        for (int c = threadIdx.x; c < COLS * CPR; c += 64 * WAVES) {
-            const int ol = c / CPR, kc = (c - ol * CPR) * 8;
-            const int o = o_base + ol;
-            // kc < rank <= rank_pad (a multiple of 16): the chunk lies in the
-            // row, and past the rank it holds the pool's zero padding
-            const uint4 w = (o < hj && kc < rank) ? ld16(Bn + (int64_t)o * g.rank_pad + kc)
-                                                   : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4 *>(&bs[ol][kc]) = w;
+        __syncthreads();
+#pragma unroll 1
+        for (int b0 = 0; b0 < PER; b0 += BATCH) {
+            uint4 w[BATCH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int c = (int)threadIdx.x + (b0 + i) * 64 * WAVES;
+                const int ol = c / CPR, kc = (c - ol * CPR) * 8;
+                const int o = min(o_base + ol, hj - 1);
+                w[i] = ld16(Bn + (int64_t)o * g.rank_pad + min(kc, g.rank_pad - 8));
+            }
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int c = (int)threadIdx.x + (b0 + i) * 64 * WAVES;
+                const int ol = c / CPR, kc = (c - ol * CPR) * 8;
+                const uint32_t m = (o_base + ol < hj && kc < rank) ? ~0u : 0u;
+                *reinterpret_cast<uint4 *>(&bs[ol][kc]) =
+                    make_uint4(w[i].x & m, w[i].y & m, w[i].z & m, w[i].w & m);
+            }
         }
         __syncthreads();
         staged = slot;
