@@ -528,8 +528,8 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
     auto step = [&](int si, Seg sd, float4 (&yv)[8], float4 (&vr)[2 * NK],
                     float4 (&yn)[8], float4 (&vn)[2 * NK]) {
         const bool act = r0 < sd.n_rows();
-        if constexpr (!kPrefetchV)
-            if (act) load_v(sd, vr);
+        if constexpr (!kPrefetchV)      // the group's first v loads with its first y
+            if (act && si != s_first) load_v(sd, vr);
         if constexpr (kPrefetchB) {
             if (sd.slot() != staged) store_b(sd, bq);
         } else {
@@ -608,7 +608,10 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
     float4 va[2 * NK], vb[2 * NK];
     {
         const Seg sd = load_seg(r.seg, s_first);
-        if (r0 < sd.n_rows()) load_rows(sd, ya, va);
+        if (r0 < sd.n_rows()) {
+            if constexpr (!kPrefetchV) load_v(sd, va);
+            load_rows(sd, ya, va);
+        }
         if constexpr (kPrefetchB) load_b_regs(sd, bq);
     }
     for (int si = s_first; si < s_last; si += 2) {
