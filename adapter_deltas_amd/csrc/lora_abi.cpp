@@ -397,17 +397,19 @@ void fill_row_meta(Plan &pl, Ranks ranks)
         return n;
     };
     const int64_t n = (int64_t)pl.rows.size();
+    int32_t top = 0;
+    for (int64_t m = 0; m < n; ++m) top = std::max(top, pl.tok[(size_t)pl.rows[(size_t)m]]);
+    std::vector<int64_t> seen((size_t)top + 1, -1);   // last tile that counted each slot
     for (int b = 0; b < 2; ++b) {
         const int64_t bm = b == 0 ? 64 : 128;
         int32_t most = 0;
-        std::vector<int32_t> seen;
+        std::fill(seen.begin(), seen.end(), -1);
         for (int64_t m0 = 0; m0 < n; m0 += bm) {
-            seen.clear();
             int32_t tot = 0;
             for (int64_t m = m0; m < std::min(n, m0 + bm); ++m) {
                 const int32_t s = pl.tok[(size_t)pl.rows[(size_t)m]];
-                if (std::find(seen.begin(), seen.end(), s) == seen.end()) {
-                    seen.push_back(s);
+                if (seen[(size_t)s] != m0) {
+                    seen[(size_t)s] = m0;
                     tot += steps(s);
                 }
             }
@@ -473,8 +475,8 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
     }
     struct Item { int32_t si, c0, cnt, cost; };
     std::vector<int32_t> rows, tiles, m, seg_tasks, order, xcd_of;
-    std::vector<int64_t> seg_cost;
-    std::vector<Item> items;
+    std::vector<int64_t> seg_cost, bucket;
+    std::vector<Item> items, sorted;
     for (int sc = 1; sc <= max_s; ++sc) {
         rows.clear();
         tiles.clear();
@@ -540,11 +542,17 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
             seg_cost[(size_t)it.si] += it.cost;
             ++seg_tasks[(size_t)it.si];
         }
-        order.clear();
+        // segments by decreasing cost, equal costs in segment order (a
+        // counting sort: costs are small integers)
+        int64_t top = 0;
+        for (size_t i = 0; i < ns; ++i) top = std::max(top, seg_cost[i]);
+        bucket.assign((size_t)top + 2, 0);
         for (size_t i = 0; i < ns; ++i)
-            if (seg_tasks[i]) order.push_back((int32_t)i);
-        std::stable_sort(order.begin(), order.end(),
-                         [&](int32_t a, int32_t b) { return seg_cost[a] > seg_cost[b]; });
+            if (seg_tasks[i]) ++bucket[(size_t)(top - seg_cost[i]) + 1];
+        for (size_t k = 1; k < bucket.size(); ++k) bucket[k] += bucket[k - 1];
+        order.assign((size_t)bucket.back(), 0);
+        for (size_t i = 0; i < ns; ++i)
+            if (seg_tasks[i]) order[(size_t)bucket[(size_t)(top - seg_cost[i])]++] = (int32_t)i;
         const int64_t room = std::max<int64_t>((int64_t)(items.size() + kXcds - 1) / kXcds,
                                                n_cu / kXcds);
         int64_t xcost[kXcds] = {}, xcount[kXcds] = {};
@@ -561,10 +569,19 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
             xcost[best] += seg_cost[i];
             xcount[best] += seg_tasks[i];
         }
-        // per XCD heaviest first, interleaved so that block b is its XCD's
+        // per XCD heaviest first (tasks by decreasing cost, equal costs in
+        // segment order), interleaved so that block b is its XCD's
         // (b / kXcds)-th task; empty places hold kMfmaTaskNone
-        std::stable_sort(items.begin(), items.end(),
-                         [](const Item &a, const Item &b) { return a.cost > b.cost; });
+        {
+            int32_t most = 0;
+            for (const Item &it : items) most = std::max(most, it.cost);
+            bucket.assign((size_t)most + 2, 0);
+            for (const Item &it : items) ++bucket[(size_t)(most - it.cost) + 1];
+            for (size_t k = 1; k < bucket.size(); ++k) bucket[k] += bucket[k - 1];
+            sorted.resize(items.size());
+            for (const Item &it : items) sorted[(size_t)bucket[(size_t)(most - it.cost)]++] = it;
+            items.swap(sorted);
+        }
         int64_t longest = 0;
         for (int x = 0; x < kXcds; ++x) longest = std::max(longest, xcount[x]);
         pl.mtask_off[sc] = (int32_t)pl.mtasks.size();
