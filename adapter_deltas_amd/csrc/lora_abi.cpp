@@ -380,14 +380,23 @@ int32_t enqueue_expand(const lora_pool *p, const lora_routing *r, const float *v
 template <class Ranks>
 void fill_row_meta(Plan &pl, Ranks ranks)
 {
-    pl.meta.clear();
-    pl.meta.reserve(pl.rows.size() * 4);
-    for (int32_t t : pl.rows) {
-        const int32_t s = pl.tok[(size_t)t];
-        pl.meta.push_back(s);
-        pl.meta.push_back((ranks(s, 0) & 0xffff) | (ranks(s, 1) << 16));
-        pl.meta.push_back((ranks(s, 2) & 0xffff) | (ranks(s, 3) << 16));
-        pl.meta.push_back(0);
+    pl.meta.resize(pl.rows.size() * 4);
+    {
+        int32_t *w = pl.meta.data();
+        int32_t last = -1, r01 = 0, r23 = 0;   // rows of one slot come together
+        for (int32_t t : pl.rows) {
+            const int32_t s = pl.tok[(size_t)t];
+            if (s != last) {
+                last = s;
+                r01 = (ranks(s, 0) & 0xffff) | (ranks(s, 1) << 16);
+                r23 = (ranks(s, 2) & 0xffff) | (ranks(s, 3) << 16);
+            }
+            w[0] = s;
+            w[1] = r01;
+            w[2] = r23;
+            w[3] = 0;
+            w += 4;
+        }
     }
     // delta steps of each 64- and 128-row tile: per distinct slot, one per 16
     // ranks of every slice (a bound on what the tile's columns need)
@@ -605,8 +614,12 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
 
 void append_inactive_rows(Plan &pl)
 {
+    const size_t n_active = pl.rows.size();
+    pl.rows.resize(pl.tok.size());
+    size_t k = n_active;
     for (size_t t = 0; t < pl.tok.size(); ++t)
-        if (pl.tok[t] == 0) pl.rows.push_back((int32_t)t);
+        if (pl.tok[t] == 0) pl.rows[k++] = (int32_t)t;
+    pl.rows.resize(k);
 }
 
 template <class Ranks>
@@ -816,14 +829,18 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     // of the slots in first-appearance order, then gathered rows likewise
     std::vector<int32_t> n_gemv((size_t)max_slots + 1, 0), n_gath((size_t)max_slots + 1, 0);
     std::vector<uint8_t> is_gath((size_t)n_rows, 0);
+    std::vector<uint8_t> high((size_t)max_slots + 1, 0);   // high_rank of each slot seen
     std::vector<int32_t> order;
     pl.tok.assign((size_t)n_rows, 0);
     for (int32_t i = 0; i < n_rows; ++i) {
         const int32_t s = row_slot[i];
         if (s == 0) continue;
         pl.tok[(size_t)i] = s;
-        if (n_gemv[s] == 0 && n_gath[s] == 0) order.push_back(s);
-        const bool g = (row_prefill && row_prefill[i]) || high_rank(s);
+        if (n_gemv[s] == 0 && n_gath[s] == 0) {
+            order.push_back(s);
+            high[(size_t)s] = high_rank(s);
+        }
+        const bool g = (row_prefill && row_prefill[i]) || high[(size_t)s];
         is_gath[(size_t)i] = g;
         ++(g ? n_gath : n_gemv)[s];
     }
