@@ -198,7 +198,7 @@ __device__ __forceinline__ void shrink_mfma_task(const LaneGeom &g, const PoolDe
 #pragma unroll
         for (int nt = 0; nt < NG; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // K-step pairs (64 elements) p = wave, wave + 4, ...; loads run D pairs
+    // K-step pairs (64 elements) p = wave, wave + 4, ...; loads run DP pairs
     // ahead.  The loop is branch-free so the loads stay in flight: every load
     // has a valid (clamped) address, and pairs past h_in and the padding
     // pairs that round a wave's count up to a multiple of the depth multiply
@@ -451,9 +451,9 @@ void k_expand_mfma(LaneGeom g, PoolDev p, RoutingDev r, int n_tasks,
 
     int staged = 0;                               // slot whose B tile is in bs
     // B tile of a slot into bs: PER 16-byte chunks per thread, loaded in
-    // batches (of up to 8, or 4) whose loads are all issued before the first LDS
-    // write (a loop of load-then-write waited out one load latency per chunk:
-    // eight for a rank-128 tile).  Every load reads a clamped address in the
+    // batches (of up to 8, or 4) whose loads are all issued before the first
+    // LDS write (a loop of load-then-write waited out one load latency per
+    // chunk: eight for a rank-128 tile).  Every load reads a clamped address in the
     // slot's rows; chunks past the slice or the rank are written as zeros.
     constexpr int PER = COLS * CPR / (64 * WAVES);
     constexpr int BMAX = WAVES == 1 ? 4 : 8;    // the one-wave forms hold more registers

@@ -34,7 +34,7 @@ constexpr int kExpandMaxGroup = 32;                     // prefill segments per 
 constexpr int kShrinkMinBlocks = 128;                   // prefill shrink grid below which tasks shrink
 constexpr int kShrinkMaxTiles = 4;                      // rank tiles of one host-built shrink task
 constexpr int kPlanComputeUnits = 256;                  // device size a host-only plan assumes
-constexpr int kXcds = 8;                                 // XCDs; block b of a grid runs on XCD b % kXcds
+constexpr int kXcds = 8;                                // XCDs: block b of a grid runs on XCD b % 8
 constexpr int32_t kMfmaTaskNone = -1;                   // an empty place of a shrink task table
 constexpr int kMetaStride = 4;                          // slices per slot in metadata
 
