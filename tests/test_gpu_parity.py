@@ -241,6 +241,60 @@ def test_matrix_core_ranks_to_256(lib, lane, path, mode, prefill_min_len):
     check_full(w, lane, y, adm, prefill_min_len=prefill_min_len)
 
 
+# Many short prompts: 200 prefill segments of 24 rows, so a host plan carries
+# matrix-core shrink task tables (at least 128 tasks; the 32-row template
+# covers them) and, on the two-slice lane, tasks that take a short segment's
+# tile of both slices; ranks 8..100 (a rank-100 segment is cut into several
+# tasks), h_in with a ragged last K-step pair, decode rows beside them.
+SHORT_PROMPTS = WorkloadSpec(
+    name="short_prompts", seed=27,
+    lanes=(LaneSpec("one", 520, (264,)), LaneSpec("two", 520, (264, 136))),
+    n_adapters=4, ranks=(8, 16, 64, 100), rank_mode="list",
+    scale_mode="uniform", scale_range=(0.25, 3.0), max_rank=100,
+    decode_rows=40, base_prob=0.2, prefill_seqs=200, prefill_len=(24, 24))
+
+
+def short_prompt_tables(lib, w):
+    """The matrix-core task tables a host plan of SHORT_PROMPTS carries (the
+    pool loads its adapters into slots 1.. in order)."""
+    resident = {aid: i + 1 for i, aid in enumerate(w.adapters)}
+    ranks = {aid: [ad.lanes["two"][0].rank] * 2 for aid, ad in w.adapters.items()}
+    p = lib.lora_plan_routing(w.seq_adapter, w.seq_len, w.spec.max_loras, 16, resident,
+                              w.spec.n_adapters, int(np.sum(w.seq_len)), resident_rank=ranks)
+    return p["mfma_tasks"]
+
+
+@pytest.mark.parametrize("mode", ["real", "int"])
+@pytest.mark.parametrize("path", ["apply", "split"])
+@pytest.mark.parametrize("lane", ["one", "two"])
+def test_short_prompts_task_tables_parity(lib, lane, path, mode):
+    w = generate(SHORT_PROMPTS, mode=mode)
+    assert sorted(short_prompt_tables(lib, w)) == [1, 2]
+    y, adm, info = run_lane(lib, w, lane, path=path, prefill_min_len=16)
+    assert info["n_prefill_segments"] >= 128 and info["n_decode_segments"] > 0
+    check_full(w, lane, y, adm, prefill_min_len=16)
+
+
+def test_routing_serves_a_lane_with_fewer_slices(lib):
+    """A routing built against the two-slice lane's pool serves the one-slice
+    lane (their slice-0 ranks agree) from its one-slice task table: every
+    row's bits equal those of the lane's own routing."""
+    import torch
+    w = generate(SHORT_PROMPTS)
+    T = int(np.sum(w.seq_len))
+    p1 = load_lane_pool(lib.Pool, w, "one")
+    p2 = load_lane_pool(lib.Pool, w, "two")
+    shared = lib.Routing(T, len(w.seq_len))
+    shared.build(p2, w.seq_adapter, w.seq_len, w.spec.max_loras, 16)
+    L = w.lanes["one"]
+    xd, yd = to_device_x(L.x), to_device_y(L.y0)
+    lib.delta_apply(p1, shared, xd, yd)
+    torch.cuda.synchronize()
+    y_own, adm, _ = run_lane(lib, w, "one", prefill_min_len=16)
+    assert np.array_equal(yd.cpu().numpy().view(np.uint32), y_own.view(np.uint32))
+    check_full(w, "one", y_own, adm, prefill_min_len=16)
+
+
 # ------------------------------------------------- full-size configs, every row
 
 @pytest.mark.slow
