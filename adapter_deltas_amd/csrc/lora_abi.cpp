@@ -405,9 +405,11 @@ void fill_row_meta(Plan &pl, Ranks ranks)
         for (int j = 0; j < kMetaStride; ++j) n += (ranks(s, j) + 15) / 16;
         return n;
     };
+    // (the slot of active row m is meta[4 m], read in order)
     const int64_t n = (int64_t)pl.rows.size();
+    const int32_t *slot_of = pl.meta.data();
     int32_t top = 0;
-    for (int64_t m = 0; m < n; ++m) top = std::max(top, pl.tok[(size_t)pl.rows[(size_t)m]]);
+    for (int64_t m = 0; m < n; ++m) top = std::max(top, slot_of[4 * m]);
     std::vector<int64_t> seen((size_t)top + 1, -1);   // last tile that counted each slot
     for (int b = 0; b < 2; ++b) {
         const int64_t bm = b == 0 ? 64 : 128;
@@ -416,7 +418,7 @@ void fill_row_meta(Plan &pl, Ranks ranks)
         for (int64_t m0 = 0; m0 < n; m0 += bm) {
             int32_t tot = 0;
             for (int64_t m = m0; m < std::min(n, m0 + bm); ++m) {
-                const int32_t s = pl.tok[(size_t)pl.rows[(size_t)m]];
+                const int32_t s = slot_of[4 * m];
                 if (seen[(size_t)s] != m0) {
                     seen[(size_t)s] = m0;
                     tot += steps(s);
