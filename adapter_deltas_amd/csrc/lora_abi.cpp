@@ -616,11 +616,14 @@ void fill_mfma_tasks(Plan &pl, int32_t max_tokens, int32_t n_cu)
 
 void append_inactive_rows(Plan &pl)
 {
-    const size_t n_active = pl.rows.size();
-    pl.rows.resize(pl.tok.size());
+    const size_t n_active = pl.rows.size(), n = pl.tok.size();
+    pl.rows.resize(n_active + n + 1);
+    int32_t *w = pl.rows.data();
     size_t k = n_active;
-    for (size_t t = 0; t < pl.tok.size(); ++t)
-        if (pl.tok[t] == 0) pl.rows[k++] = (int32_t)t;
+    for (size_t t = 0; t < n; ++t) {   // branch-free: every row is written, kept if inactive
+        w[k] = (int32_t)t;
+        k += pl.tok[t] == 0;
+    }
     pl.rows.resize(k);
 }
 
@@ -834,11 +837,11 @@ void plan_rows(int32_t n_rows, const int32_t *row_slot, const uint8_t *row_prefi
     std::vector<uint8_t> high((size_t)max_slots + 1, 0);   // high_rank of each slot seen
     std::vector<int32_t> order;
     pl.tok.assign((size_t)n_rows, 0);
+    // (slot 0's counts are kept too, and never read: no branch on base rows)
     for (int32_t i = 0; i < n_rows; ++i) {
         const int32_t s = row_slot[i];
-        if (s == 0) continue;
         pl.tok[(size_t)i] = s;
-        if (n_gemv[s] == 0 && n_gath[s] == 0) {
+        if (s != 0 && n_gemv[s] == 0 && n_gath[s] == 0) {
             order.push_back(s);
             high[(size_t)s] = high_rank(s);
         }
