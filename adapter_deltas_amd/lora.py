@@ -184,16 +184,20 @@ def lora_routing_get_info(routing) -> dict:
     return info.as_dict()
 
 
-def _task_tables(words, offs):
-    """The shrink task words of a packed plan: the decode (GEMV) tasks, and
-    the matrix-core task table per lane slice count (absent: no table)."""
+def _task_tables(words, offs, n_active):
+    """The per-row metadata and shrink task words of a packed plan: 4 words
+    per active row {slot, rank0 | rank1 << 16, rank2 | rank3 << 16, 0}, the
+    decode (GEMV) tasks, and the matrix-core task table per lane slice count
+    (absent: no table)."""
     h = offs[4]
+    meta = words[offs[3] - 4 * n_active:offs[3]].reshape(-1, 4).copy()
     mfma = {}
     for s in range(1, 5):
         o, n = int(words[h + 2 * (s - 1)]), int(words[h + 2 * (s - 1) + 1])
         if n:
             mfma[s] = words[h + o:h + o + n].view(np.uint32).copy()
-    return dict(gemv_tasks=words[offs[3]:h].view(np.uint32).copy(), mfma_tasks=mfma)
+    return dict(row_meta=meta, gemv_tasks=words[offs[3]:h].view(np.uint32).copy(),
+                mfma_tasks=mfma)
 
 
 def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resident,
@@ -203,7 +207,8 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
 
     Returns a dict with info counts, admitted (bool array), the tables seg
     (int32 [n_seg, 16]), rows (int32 [n_active]) and tok_slot (int32 [T]),
-    and the shrink task words gemv_tasks and mfma_tasks ({slice count: words}).
+    the per-row metadata row_meta (int32 [n_active, 4]) and the shrink task
+    words gemv_tasks and mfma_tasks ({slice count: words}).
     """
     i32p = ctypes.POINTER(ctypes.c_int32)
     ids = _seq_ids(seq_adapter_id)
@@ -231,7 +236,7 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
         tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
-        **_task_tables(words, offs))
+        **_task_tables(words, offs, d["n_active"]))
 
 
 def lora_routing_token_slots(routing) -> int:
@@ -271,8 +276,9 @@ def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
     """Host-only plan from per-row slots.  slot_rank: int32 [max_slots + 1, 4].
 
     Returns a dict with info counts, the tables seg (int32 [n_seg, 16]),
-    rows (int32 [n_active]) and tok_slot (int32 [n_rows]), and the shrink task
-    words gemv_tasks and mfma_tasks ({slice count: words})."""
+    rows (int32 [n_active]) and tok_slot (int32 [n_rows]), the per-row
+    metadata row_meta (int32 [n_active, 4]) and the shrink task words
+    gemv_tasks and mfma_tasks ({slice count: words})."""
     i32p = ctypes.POINTER(ctypes.c_int32)
     slots = np.ascontiguousarray(row_slot, dtype=np.int32)
     pre = None if row_prefill is None else np.ascontiguousarray(row_prefill, dtype=np.uint8)
@@ -294,7 +300,7 @@ def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
         tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
-        **_task_tables(words, offs))
+        **_task_tables(words, offs, d["n_active"]))
 
 
 def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:

@@ -228,6 +228,8 @@ def test_plan_random_batches(m, seed):
     p = m.lora_plan_routing(ids, lens, cap, pmin, resident, 40, T, resident_rank=ranks)
     _check_plan(p, ids, lens, resident, cap, pmin, ranks)
     _check_mfma_tables(p)
+    inv_slot = {s: i for i, s in resident.items()}
+    _check_row_meta(p, lambda s: ranks[inv_slot[s]])
     inv = {s: i for i, s in resident.items()}
     for d in p["seg"]:
         assert list(d[4:8]) == ranks[inv[d[0]]]
@@ -242,6 +244,19 @@ NONE = 0xFFFFFFFF     # an empty place of a task table
 
 def _live(words):
     return words[words != NONE]
+
+
+def _check_row_meta(p, slot_ranks):
+    """Row metadata: active row m holds its slot and the slot's four ranks
+    (slot_ranks(slot) -> 4 ranks)."""
+    meta = p["row_meta"]
+    rows = p["rows"]
+    assert meta.shape == (len(rows), 4)
+    for m, t in enumerate(rows):
+        s = int(p["tok_slot"][t])
+        r = slot_ranks(s)
+        assert list(meta[m]) == [s, (r[0] & 0xffff) | (r[1] << 16),
+                                 (r[2] & 0xffff) | (r[3] << 16), 0], m
 
 
 def _check_mfma_tables(p):
@@ -412,6 +427,7 @@ def test_plan_rows_random(m, seed):
     p = m.lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max(n, 1))
     _check_rows_plan(p, row_slot, row_prefill, slot_rank)
     _check_mfma_tables(p)
+    _check_row_meta(p, lambda s: [int(v) for v in slot_rank[s]])
 
 
 def test_plan_rows_cuts_small_groups_at_16(m):
