@@ -184,13 +184,16 @@ def lora_routing_get_info(routing) -> dict:
     return info.as_dict()
 
 
-def _task_tables(words, offs, n_active):
+def _task_tables(words, offs, n_active, n_tokens):
     """The per-row metadata and shrink task words of a packed plan: 4 words
     per active row {slot, rank0 | rank1 << 16, rank2 | rank3 << 16, 0}, the
     decode (GEMV) tasks, and the matrix-core task table per lane slice count
     (absent: no table)."""
     h = offs[4]
-    meta = words[offs[3] - 4 * n_active:offs[3]].reshape(-1, 4).copy()
+    m0 = (offs[2] + n_tokens + 3) // 4 * 4
+    if m0 + 4 * n_active != offs[3]:
+        raise LoraError(f"plan words: row metadata at {m0} does not end at the tasks ({offs[3]})")
+    meta = words[m0:offs[3]].reshape(-1, 4).copy()
     mfma = {}
     for s in range(1, 5):
         o, n = int(words[h + 2 * (s - 1)]), int(words[h + 2 * (s - 1) + 1])
@@ -236,7 +239,7 @@ def lora_plan_routing(seq_adapter_id, seq_len, max_loras, prefill_min_len, resid
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
         tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
-        **_task_tables(words, offs, d["n_active"]))
+        **_task_tables(words, offs, d["n_active"], d["n_tokens"]))
 
 
 def lora_routing_token_slots(routing) -> int:
@@ -300,7 +303,7 @@ def lora_plan_rows(row_slot, row_prefill, max_slots, slot_rank, max_tokens):
         seg=words[offs[0]:offs[0] + L.SEG_WORDS * d["n_segments"]].reshape(-1, L.SEG_WORDS).copy(),
         rows=words[offs[1]:offs[1] + d["n_active"]].copy(),
         tok_slot=words[offs[2]:offs[2] + d["n_tokens"]].copy(),
-        **_task_tables(words, offs, d["n_active"]))
+        **_task_tables(words, offs, d["n_active"], d["n_tokens"]))
 
 
 def moe_slot(adapter_slot: int, expert: int, n_experts: int) -> int:
