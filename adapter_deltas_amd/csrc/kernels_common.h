@@ -64,6 +64,27 @@ __device__ __forceinline__ int xcd_task(int b, int n)
     return xcd * q + min(xcd, rem) + local;
 }
 
+// A device-built routing knows its segment count only on the device: a
+// launch covers a bound, and the live segments are a prefix of it.  Dealt out
+// by xcd_task, that prefix would sit on the first few XCDs only; here `deal`
+// tasks (whole segments: r.spread of them, `per` tasks each) go to the XCDs
+// in turn, deal d to XCD d % 8, so the prefix spreads over every XCD while a
+// segment's tasks, and those of the next few segments, share an L2.  The
+// grid is seg_grid(): 8 * deal * ceil(n / (8 * spread)) blocks, a bijection
+// onto the tasks below that, of which those from n * per on are empty.
+__device__ __forceinline__ int spread_task(int b, int deal)
+{
+    const int xcd = b % kXcds, l = b / kXcds;
+    const int i = l / deal;
+    return (xcd + kXcds * i) * deal + (l - i * deal);
+}
+
+// Task of block b in a launch of n tasks, `per` to a segment (see seg_grid).
+__device__ __forceinline__ int seg_task(const RoutingDev &r, int b, int n, int per)
+{
+    return r.spread > 0 ? spread_task(b, r.spread * per) : xcd_task(b, n);
+}
+
 // Slice j and tile within the slice of tile number `rem` of a segment, by
 // compares and selects on the widths in the kernel arguments, so every task
 // of a launch is a live tile and none waits for a table load to find that out.

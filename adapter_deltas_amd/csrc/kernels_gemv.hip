@@ -35,7 +35,9 @@ __global__ __launch_bounds__(64 * W) void k_shrink_gemv(LaneGeom g, PoolDev p, R
                                                          int vsplit, const int32_t *tasks)
 {
     touch_args(n_tasks, g, p, r, ldx);
-    const int task = xcd_task(blockIdx.x, n_tasks);
+    const int task = TAB ? xcd_task(blockIdx.x, n_tasks)
+                         : seg_task(r, blockIdx.x, n_tasks, g.n_slices * kb_per_slice);
+    if (task >= n_tasks) return;
     int si, j, kb;
     if constexpr (TAB) {
         typedef const __attribute__((address_space(4))) int32_t cint;
@@ -115,7 +117,8 @@ __global__ __launch_bounds__(64 * (kDecodeSegRows / C)) void k_expand_gemv(LaneG
     constexpr int kExpandWaves = kDecodeSegRows / C;
     constexpr int TILE = 64 * LC;
     touch_args(n_tasks, g, p, r, ldy);
-    const int task = xcd_task(blockIdx.x, n_tasks);
+    const int task = seg_task(r, blockIdx.x, n_tasks, tiles_per_seg);
+    if (task >= n_tasks) return;
     const int si = task / tiles_per_seg;
     int j, tile;
     slice_tile<TILE>(g, task - si * tiles_per_seg, j, tile);
@@ -205,7 +208,8 @@ __global__ __launch_bounds__(64 * kParts) void k_delta_gemv(LaneGeom g, PoolDev 
     constexpr int KB = kFusedMaxRank / kKBlock;   // rank blocks at most
     static_assert(kParts == kDecodeSegRows, "one part and one row per wave");
     touch_args(n_tasks, g, p, r, ldy);
-    const int task = xcd_task(blockIdx.x, n_tasks);
+    const int task = seg_task(r, blockIdx.x, n_tasks, tiles_per_seg);
+    if (task >= n_tasks) return;
     const int si = task / tiles_per_seg;
     int j, tile;
     slice_tile<kExpandTile>(g, task - si * tiles_per_seg, j, tile);
@@ -330,7 +334,10 @@ hipError_t launch_shrink_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const int n_sub = (g.h_in + kSubChunk - 1) / kSubChunk;
     const int w_max = blocks < 512 ? 8 : blocks < 2048 ? 4 : 2;
     const int w = std::min(w_max, n_sub >= 8 ? 8 : n_sub >= 4 ? 4 : n_sub >= 2 ? 2 : 1);
-    const dim3 grid((unsigned)blocks), block(64 * w);
+    const int64_t n_blocks =
+        tasks ? blocks : seg_grid(r, n_seg, (int64_t)g.n_slices * kb_per_slice);
+    if (n_blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n_blocks), block(64 * w);
 #define LAUNCH_SHRINK(F, W)                                                                   \
     do {                                                                                      \
         if (tasks)                                                                            \
@@ -364,7 +371,9 @@ hipError_t launch_delta_gemv(const LaneGeom &g, const PoolDev &p, const RoutingD
     if (blocks <= 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
-    const dim3 grid((unsigned)blocks), block(64 * kParts);
+    const int64_t n_blocks = seg_grid(r, n_seg, tiles_per_seg);
+    if (n_blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n_blocks), block(64 * kParts);
     if (g.x_fp16)
         hipLaunchKernelGGL(k_delta_gemv<true>, grid, block, 0, s, g, p, r, (int)blocks,
                            tiles_per_seg, xp, ldx, y, ldy);
@@ -382,8 +391,9 @@ hipError_t launch_expand_gemv(const LaneGeom &g, const PoolDev &p, const Routing
     const int tiles_per_seg = lane_tiles(g, 64 * lane_cols);
     const int64_t blocks = (int64_t)n_seg * tiles_per_seg;
     if (blocks <= 0) return hipSuccess;
-    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks);
+    const int64_t n_blocks = seg_grid(r, n_seg, tiles_per_seg);
+    if (n_blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n_blocks);
 #define LAUNCH_EXPAND(C, LC)                                                                      \
     hipLaunchKernelGGL((k_expand_gemv<C, LC>), grid, dim3(64 * (kDecodeSegRows / C)), 0, s, g, p, \
                        r, (int)blocks, tiles_per_seg, v, y, ldy)

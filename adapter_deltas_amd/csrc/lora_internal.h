@@ -103,7 +103,19 @@ struct RoutingDev {
     const int32_t *rows;      // token row of each active row (host-built: then the
                               // other rows of the batch)
     const int32_t *counts;    // device-built routing: exact counts (else null)
+    int32_t spread;           // > 0: segments dealt to the XCDs this many at a time
+                              // (the count is a bound; spread_task), else xcd_task
 };
+// Blocks of a launch over n segments of `per` tasks each.  When n is a bound
+// (device-built routing, spread > 0) its segments are dealt to the XCDs
+// `spread` at a time (spread_task) on a grid padded to whole rounds.
+inline int64_t seg_grid(const RoutingDev &r, int64_t n, int64_t per)
+{
+    const int64_t deal = (int64_t)r.spread * per;
+    const int64_t round = (int64_t)kXcds * r.spread;
+    return r.spread > 0 ? kXcds * deal * ((n + round - 1) / round) : n * per;
+}
+
 // Entries of a device-built routing's counts.
 enum DeviceCount : int { kCntActive = 0, kCntDecode = 1, kCntPrefill = 2, kCntGather = 3,
                          kCntInvalid = 4, kCntUnedited = 5, kCntWords = 8 };
@@ -302,6 +314,7 @@ struct lora_routing {
     int32_t max_gather_rows;          // rows of the largest gather segment (bound)
     int32_t decode_rows;              // rows of the decode segments (0: not known on the host)
     int32_t expand_lane_cols;         // columns per lane of the decode expand: 8 or 4 (0: 8)
+    int32_t seg_spread;               // RoutingDev::spread (device-built only)
     hipStream_t side;                 // decode kernels of a mixed batch (default priority)
     hipEvent_t fork_ev, join_ev;      // fork from / join into the caller's stream
     std::vector<int32_t> distinct_slots;
