@@ -44,10 +44,22 @@ def _check(rc: int):
         raise LoraError(rc, lora_last_error())
 
 
+_current_stream = None
+
+
 def _stream(stream) -> Optional[int]:
+    """A stream argument as a raw handle; None is torch's current stream on the
+    current device (looked up without building a Stream object: this runs on
+    every call, and the object costs a few microseconds)."""
+    global _current_stream
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _current_stream is None:
+            import torch
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            dev = torch.cuda.current_device
+            _current_stream = ((lambda: raw(dev())) if raw is not None else
+                               (lambda: torch.cuda.current_stream().cuda_stream))
+        return _current_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream

@@ -402,10 +402,7 @@ def main_moe(args, spec):
                 pool, x, y = per[ln]
                 m.delta_apply(pool, routing, x, y, ws[ln])
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup(args, step)
     if args.only_apply:
         for _ in range(args.steps):
             step()
@@ -550,11 +547,42 @@ def main_moe(args, spec):
     print(json.dumps(out), flush=True)
 
 
+# Default warmup: a step count alone left the first timed steps of a fresh
+# process up to twice as slow as later ones (decode_mix: 1.64 against 0.87 ms
+# per step after 10 warmup steps), so it also runs for a minimum time.
+WARMUP_MIN_STEPS = 10
+WARMUP_MIN_S = 0.5
+
+
+def warmup(args, step):
+    """Untimed warmup steps: args.warmup of them, or when not given at least
+    WARMUP_MIN_STEPS and WARMUP_MIN_S seconds' worth (args.warmup is then set
+    to the count run, which the JSON line reports)."""
+    import torch
+    if args.warmup is not None:
+        log(f"warmup {args.warmup}")
+        for _ in range(args.warmup):
+            step()
+    else:
+        n, t0 = 0, time.perf_counter()
+        while n < WARMUP_MIN_STEPS or time.perf_counter() - t0 < WARMUP_MIN_S:
+            step()
+            n += 1
+            if n % WARMUP_MIN_STEPS == 0:
+                torch.cuda.synchronize()     # time what the device has done
+        args.warmup = n
+        log(f"warmup {n} steps")
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least %d steps and %.1f s of "
+                         "them, so that clocks and first-touch costs have settled)"
+                         % (WARMUP_MIN_STEPS, WARMUP_MIN_S))
     ap.add_argument("--config", default="decode_mix")
     ap.add_argument("--layers", type=int, default=0,
                     help="layer buffer sets (default: enough for 1 GiB, at least 16)")
@@ -660,10 +688,7 @@ def main():
                 pool, x, y = per[ln]
                 m.delta_apply(pool, routing, x, y, ws[ln])
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup(args, step)
     if args.only_apply:
         # a counter pass: the library's only work is delta_apply on every lane
         # of every layer, (warmup + steps) x layers times per lane
